@@ -1,0 +1,180 @@
+"""FLCE forward + backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: flce_forward (logits
+GEMM with the online log-sum-exp epilogue, combine, reduction) then
+flce_backward (per vocabulary slab: logits recompute into dlogits, dW, dx; db)
+with inputs, outputs and workspaces already resident in HBM.  Prints one JSON
+line.  Inputs are seeded synthetic data with the workload's shapes and
+distributions (random weights; no dataset).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/s and % bf16 MFMA peak at N=8192,H=4096,V=128256"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0: automatic)")
+    return p.parse_args()
+
+
+def cpu_baseline(inp, rows):
+    """Time the fp64 oracle (as it stands) on the first ``rows`` tokens."""
+    import numpy as np
+    from lm_head_cross_flce_amd import synth
+    from oracle import flce_oracle as O
+
+    w = inp.w
+    W64 = inp.as_f64("W")
+    b64 = inp.as_f64("b")
+    x = synth.bf16_bits_to_f64(inp.x[:rows]) if w.dtype == "bf16" else inp.x[:rows].astype(np.float64)
+    t = inp.targets[:rows]
+    g = inp.grad[:rows] if w.reduction == "none" else inp.grad
+    t0 = time.perf_counter()
+    O.loss_and_grads(x, W64, b64, t, g, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                     rows_per_chunk=rows)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.N} tokens, full V={w.V} and H={w.H}, fp64 forward+backward "
+                      f"(logits computed twice), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path would shard "
+              "tokens across GPUs with a dW reduce-scatter, which this build does not implement)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lm_head_cross_flce_amd import _lib, functional as F, synth
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from lm_head_cross_flce_amd import build
+        build.build()
+    name = args.workload or synth.BENCH_WORKLOAD
+    w = synth.WORKLOADS[name]
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {name}: inputs drawn in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def t(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x, W = t(inp.x), t(inp.W)
+    b = t(inp.b) if inp.b is not None else None
+    tg = torch.from_numpy(inp.targets).to(dev)
+    g = torch.from_numpy(inp.grad).to(dev)
+    N, H, V = w.N, w.H, w.V
+    fwd_bytes, bwd_bytes = F.flce_workspace_size(N, H, V, tdt, b is not None, w.reduction)
+    ws_f = torch.empty(fwd_bytes, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bwd_bytes, dtype=torch.uint8, device=dev)
+    dx, dW = torch.empty_like(x), torch.empty_like(W)
+    db = torch.empty_like(b) if b is not None else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        loss, lse, nv = F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                       w.reduction, workspace=ws_f)
+        if ev is not None:
+            ev[1].record(stream)
+        F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                        w.reduction, workspace=ws_b, out=(dx, dW, db))
+        if ev is not None:
+            ev[2].record(stream)
+        return loss
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        loss = step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
+    fwd_med, bwd_med = fwd_ms[len(fwd_ms) // 2], bwd_ms[len(bwd_ms) // 2]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = N * args.steps / elapsed
+    flops = 8.0 * N * H * V
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = 2.0 * N * H * V / (fwd_avg * 1e-3) / 1e12
+    extra = fwd_bytes + bwd_bytes + N * 4 + 8
+    print(f"[bench] loss {loss.item():.6f}; fwd {fwd_med:.3f} ms, bwd {bwd_med:.3f} ms (median)",
+          file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64 draws, random-init weights)",
+        "config": {"workload": name, "N": N, "H": H, "V": V, "bias": b is not None,
+                   "label_smoothing": w.label_smoothing, "z_loss_scale": w.z_loss_scale,
+                   "reduction": w.reduction, "ignored_rows": w.n_ignored, "targets": w.targets},
+        "fwd_ms": fwd_med,
+        "bwd_ms": bwd_med,
+        "tflops_8nhv": tflops,
+        "mfma_frac_8nhv": tflops / peak,
+        "extra_hbm_mb": extra / 1e6,
+        "extra_hbm_frac_of_fp32_logits": extra / (N * V * 4.0),
+        "roofline": {"kernel": "fwd_lse_kernel", "bound": "mfma", "achieved": fwd_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": fwd_tflops / peak, "traffic": None,
+                     "note": "2NHV flops per launch / average duration of the forward call "
+                             "(HIP events on the launch stream; the call adds two O(N) kernels)"},
+    }
+    if not args.no_cpu_baseline:
+        del x, W, b, dx, dW, db, ws_f, ws_b
+        torch.cuda.empty_cache()
+        rows = args.cpu_rows or max(8, min(N, int(2.5e11 // (8.0 * H * V))))
+        print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * flce.h - fused linear cross entropy (FLCE) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For hidden states x [N, H], an LM-head weight W [V, H]
+ * (nn.Linear layout: row j is the weight of vocabulary entry j), an optional
+ * bias b [V] and integer targets y [N]:
+ *
+ *   z[n, j]  = sum_h x[n, h] W[j, h] + b[j]                    (the logits)
+ *   lse[n]   = m + log d,  m = max_j z[n, j],  d = sum_j exp(z[n, j] - m)
+ *   l[n]     = lse[n] - (1 - eps) z[n, y_n] - (eps / V) sum_j z[n, j]
+ *              + s * lse[n]^2                        (0 when y_n == ignore_index)
+ *   loss     = sum_n l[n] / T (mean) | sum_n l[n] (sum) | l (none),
+ *              T = #{n : y_n != ignore_index};  all rows ignored gives loss 0.
+ *
+ * Sources: fla-org flash-linear-attention, fla/modules/
+ * fused_linear_cross_entropy.py (the F.linear logits, the cross_entropy_kernel
+ * loss with label smoothing, the mean over non-ignored rows); Liger-Kernel PR
+ * 239 "Support Z Loss in CE" (z-loss s * lse^2, the online max / sum-exp form
+ * of lse, and the gradient below); DeepSpeed PR 8792 (reduction "none", logits
+ * produced straight into fp32, statistics-only forward with the logits
+ * recomputed one vocabulary block at a time in backward).
+ *
+ * The backward returns, with c_n = g / T (mean), g (sum) or g_n (none), and
+ * c_n = 0 for ignored rows,
+ *   dz[n, j] = c_n [ (1 + 2 s lse[n]) softmax(z[n])_j - eps / V - (1 - eps) [j == y_n] ]
+ *   dx = dz W,   dW = dz^T x,   db = sum_n dz[n, :]
+ * accumulated in fp32 and written once in the input dtype.
+ *
+ * The [N, V] logits are never stored: the forward keeps only per-token
+ * statistics (lse), the backward recomputes the logits one vocabulary slab at
+ * a time.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and never synchronises the host.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the default stream) and completes
+ *    asynchronously in stream order.
+ *  - Tensors are dense and row-major: x [N, H] and W [V, H] with H contiguous,
+ *    b [V], targets [N] int64.  x, W and b share one dtype (flce_dtype).
+ *  - Pointers must be 16-byte aligned; H must be a multiple of 8.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed validation returns an error code and enqueues nothing.
+ *  - Targets outside [0, V) that are not ignore_index are a precondition
+ *    violation: the results for such rows are unspecified (no memory outside
+ *    the given buffers is touched).  An ignore_index inside [0, V) is honoured
+ *    (the row is ignored).
+ *  - Entry points are thread-safe; calls that share a workspace must be
+ *    ordered by the caller (same stream, or events).
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, misalignment, eps/s out of range */
+  FLCE_ERR_UNSUPPORTED = 2,      /* dtype or shape this build does not handle (e.g. H % 8 != 0) */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = 3,
+  FLCE_ERR_HIP = 4               /* a HIP launch failed; see hipGetLastError on the caller side */
+} flce_status;
+
+typedef enum {
+  FLCE_REDUCTION_NONE = 0,
+  FLCE_REDUCTION_SUM = 1,
+  FLCE_REDUCTION_MEAN = 2
+} flce_reduction;
+
+typedef enum {
+  FLCE_F32 = 0,  /* x, W, b are float32; gradients are float32 */
+  FLCE_BF16 = 1  /* x, W, b are bfloat16; gradients are bfloat16 (fp32 accumulation) */
+} flce_dtype;
+
+/*
+ * Workspace bytes that flce_forward (*fwd_bytes) and flce_backward
+ * (*bwd_bytes) need for this problem.  Pure host arithmetic: no HIP call.
+ * Either output pointer may be NULL.  The backward figure includes one
+ * vocabulary slab of dlogits [N, slab] in the input dtype and an fp32 [N, H]
+ * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch.
+ */
+flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias,
+                                int reduction, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/*
+ * Forward: writes
+ *   loss    float32, [1] for sum/mean, [N] for none
+ *   lse     float32 [N]   (kept by the caller for flce_backward)
+ *   n_valid int64 [1]     T, the non-ignored count (kept for flce_backward)
+ * b may be NULL (no bias).  eps = label_smoothing in [0, 1]; s = z_loss_scale
+ * >= 0; reduction is a flce_reduction.  workspace must hold at least
+ * *fwd_bytes from flce_workspace_size for the same arguments.
+ */
+flce_status flce_forward(const void* x, const void* W, const void* b, const int64_t* targets,
+                         int64_t N, int64_t H, int64_t V, int dtype,
+                         float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                         int reduction,
+                         float* loss, float* lse, int64_t* n_valid,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: given the forward's lse and n_valid and the upstream gradient
+ * grad_loss (float32: [1] for sum/mean, [N] for none), overwrites
+ *   dx [N, H]  (may be NULL: not needed)
+ *   dW [V, H]  (may be NULL: frozen weight)
+ *   db [V]     (may be NULL: no bias, or not needed; ignored when b is NULL)
+ * in the input dtype.  The other arguments must equal the forward's.
+ * workspace must hold at least *bwd_bytes from flce_workspace_size.
+ */
+flce_status flce_backward(const void* x, const void* W, const void* b, const int64_t* targets,
+                          int64_t N, int64_t H, int64_t V, int dtype,
+                          float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                          int reduction, const float* lse, const int64_t* n_valid,
+                          const float* grad_loss,
+                          void* dx, void* dW, void* db,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* flce_status_string(int status);
+
+/* Vocabulary slab width (columns of dlogits held at once) the backward uses
+ * for this problem; pure host arithmetic.  Returns 0 on invalid arguments. */
+int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

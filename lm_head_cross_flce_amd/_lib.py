@@ -1,0 +1,104 @@
+"""ctypes binding of libflce.so: the C entry points under their own names.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+library; if the library is missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+
+FLCE_OK = 0
+FLCE_ERR_INVALID_ARGUMENT = 1
+FLCE_ERR_UNSUPPORTED = 2
+FLCE_ERR_WORKSPACE_TOO_SMALL = 3
+FLCE_ERR_HIP = 4
+
+FLCE_F32 = 0
+FLCE_BF16 = 1
+
+REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+
+# Every symbol the public header declares.
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_status_string",
+           "flce_backward_slab_cols")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libflce.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m lm_head_cross_flce_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, sz, vp, f32, c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        lib.flce_workspace_size.argtypes = [i64, i64, i64, c_int, c_int, c_int,
+                                            ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        lib.flce_workspace_size.restype = c_int
+        lib.flce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int,
+                                     vp, vp, vp, vp, sz, vp]
+        lib.flce_forward.restype = c_int
+        lib.flce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int,
+                                      vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flce_backward.restype = c_int
+        lib.flce_status_string.argtypes = [c_int]
+        lib.flce_status_string.restype = ctypes.c_char_p
+        lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
+        lib.flce_backward_slab_cols.restype = i64
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().flce_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != FLCE_OK:
+        raise FlceError(status, where)
+
+
+def flce_workspace_size(N: int, H: int, V: int, dtype: int, has_bias: bool, reduction: int):
+    """(forward_bytes, backward_bytes) for this problem."""
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().flce_workspace_size(N, H, V, dtype, int(bool(has_bias)), reduction,
+                                      ctypes.byref(f), ctypes.byref(b)), "flce_workspace_size")
+    return f.value, b.value
+
+
+def flce_backward_slab_cols(N: int, H: int, V: int, dtype: int) -> int:
+    return int(load().flce_backward_slab_cols(N, H, V, dtype))
+
+
+def flce_forward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                 reduction, loss, lse, n_valid, workspace, workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_forward(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                               ignore_index, reduction, loss, lse, n_valid, workspace, workspace_bytes,
+                               stream or None), "flce_forward")
+
+
+def flce_backward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                  reduction, lse, n_valid, grad_loss, dx, dW, db, workspace, workspace_bytes,
+                  stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_backward(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                ignore_index, reduction, lse, n_valid, grad_loss, dx or None, dW or None,
+                                db or None, workspace, workspace_bytes, stream or None), "flce_backward")

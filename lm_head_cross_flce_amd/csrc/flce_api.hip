@@ -1,0 +1,224 @@
+// C-ABI entry points of the FLCE library: argument validation, workspace
+// layout and the launch sequence.  No allocation and no host synchronisation:
+// everything is enqueued on the caller's stream.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "flce.h"
+#include "flce_launch.hpp"
+
+namespace {
+
+constexpr int kCUs = 256;                      // MI355X compute units
+constexpr int kTile = 256;
+constexpr size_t kAlign = 256;
+constexpr size_t kSlabCapBytes = size_t(1) << 30;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Geometry {
+  int NT, VT, P;
+  int64_t slab_cols;
+  size_t off_partials, off_rowloss, fwd_total;
+  size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, bwd_total;
+};
+
+flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
+  if (N < 1 || H < 1 || V < 1) return FLCE_ERR_INVALID_ARGUMENT;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_UNSUPPORTED;
+  if (N > (int64_t(1) << 30) || V > (int64_t(1) << 30) || H > (int64_t(1) << 20)) return FLCE_ERR_UNSUPPORTED;
+  if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+// Vocabulary slab width for the backward: enough vocabulary tiles that the dW
+// contraction of one slab (H/256 x slab/256 output tiles) fills every CU,
+// capped so the dlogits slab stays under 1 GiB.  FLCE_DEBUG_SLAB_COLS (a
+// positive multiple of 256) overrides it; the tests use it to force many slabs.
+int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
+  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
+  const int64_t vmax = cdiv(V, kTile) * kTile;
+  if (const char* env = std::getenv("FLCE_DEBUG_SLAB_COLS")) {
+    const long long c = std::atoll(env);
+    if (c > 0 && c % kTile == 0) return c < vmax ? c : vmax;
+  }
+  const int64_t th = cdiv(H, kTile);
+  int64_t want = cdiv(kCUs, th) * kTile;
+  int64_t cap = (int64_t)(kSlabCapBytes / (size_t)(N * es)) / kTile * kTile;
+  if (cap < kTile) cap = kTile;
+  int64_t c = want < cap ? want : cap;
+  return c < vmax ? c : vmax;
+}
+
+Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias) {
+  Geometry g{};
+  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
+  g.NT = (int)cdiv(N, kTile);
+  g.VT = (int)cdiv(V, kTile);
+  int P = kCUs / g.NT;
+  if (P < 1) P = 1;
+  if (P > g.VT) P = g.VT;
+  g.P = P;
+  size_t off = 0;
+  g.off_partials = off;
+  off = align_up(off + (size_t)P * N * 16);
+  g.off_rowloss = off;
+  off = align_up(off + (size_t)N * 4);
+  g.fwd_total = off;
+
+  g.slab_cols = slab_cols(N, H, V, dtype);
+  off = 0;
+  g.off_slab = off;
+  off = align_up(off + (size_t)N * g.slab_cols * es);
+  g.off_dxacc = off;
+  off = align_up(off + (size_t)N * H * 4);
+  g.off_dbp = off;
+  if (has_bias) off = align_up(off + (size_t)g.NT * V * 4);
+  g.off_coef = off;
+  off = align_up(off + (size_t)N * 16);
+  g.off_yv = off;
+  off = align_up(off + (size_t)N * 4);
+  g.bwd_total = off;
+  return g;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+flce_status check_options(float eps, float s, int reduction) {
+  if (!(eps >= 0.f && eps <= 1.f)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!(s >= 0.f) || !std::isfinite(s)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (reduction != FLCE_REDUCTION_NONE && reduction != FLCE_REDUCTION_SUM && reduction != FLCE_REDUCTION_MEAN)
+    return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+flce_status check_inputs(const void* x, const void* W, const void* b, const int64_t* targets, int dtype) {
+  if (!x || !W || !targets) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(targets, 8)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (b && !aligned(b, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLCE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
+  if (check_shape(N, H, V, dtype) != FLCE_OK) return 0;
+  return slab_cols(N, H, V, dtype);
+}
+
+flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, int reduction,
+                                size_t* fwd_bytes, size_t* bwd_bytes) {
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  st = check_options(0.f, 0.f, reduction);
+  if (st != FLCE_OK) return st;
+  const Geometry g = geometry(N, H, V, dtype, has_bias);
+  if (fwd_bytes) *fwd_bytes = g.fwd_total;
+  if (bwd_bytes) *bwd_bytes = g.bwd_total;
+  return FLCE_OK;
+}
+
+flce_status flce_forward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                         int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
+                         int64_t ignore_index, int reduction, float* loss, float* lse, int64_t* n_valid,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
+  if ((st = check_inputs(x, W, b, targets, dtype)) != FLCE_OK) return st;
+  if (!loss || !lse || !n_valid || !aligned(loss, 4) || !aligned(lse, 4) || !aligned(n_valid, 8))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  const Geometry g = geometry(N, H, V, dtype, b != nullptr);
+  if (workspace_bytes < g.fwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+
+  char* ws = (char*)workspace;
+  flce::FwdLaunch a{};
+  a.x = x; a.W = W; a.b = b; a.targets = targets;
+  a.N = (int)N; a.H = (int)H; a.V = (int)V;
+  a.NT = g.NT; a.P = g.P; a.VT = g.VT;
+  a.ignore_index = ignore_index;
+  a.eps = label_smoothing;
+  a.eps_over_v = (float)((double)label_smoothing / (double)V);
+  a.s = z_loss_scale;
+  a.reduction = reduction;
+  a.partials = ws + g.off_partials;
+  a.rowloss = (float*)(ws + g.off_rowloss);
+  a.loss = loss; a.lse = lse; a.n_valid = n_valid;
+  (void)hipGetLastError();
+  if (flce::launch_forward(a, dtype, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
+flce_status flce_backward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                          int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
+                          int64_t ignore_index, int reduction, const float* lse, const int64_t* n_valid,
+                          const float* grad_loss, void* dx, void* dW, void* db, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
+  if ((st = check_inputs(x, W, b, targets, dtype)) != FLCE_OK) return st;
+  if (!lse || !n_valid || !grad_loss) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned(lse, 4) || !aligned(n_valid, 8) || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((dx && !aligned(dx, 16)) || (dW && !aligned(dW, 16))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (db && !aligned(db, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Geometry g = geometry(N, H, V, dtype, b != nullptr);
+  if (workspace_bytes < g.bwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  const bool want_db = b != nullptr && db != nullptr;
+  if (!dx && !dW && !want_db) return FLCE_OK;
+
+  char* ws = (char*)workspace;
+  flce::BwdLaunch a{};
+  a.x = x; a.W = W; a.b = b; a.targets = targets;
+  a.N = (int)N; a.H = (int)H; a.V = (int)V;
+  a.NT = g.NT;
+  a.ignore_index = ignore_index;
+  a.eps = label_smoothing;
+  a.eps_over_v = (float)((double)label_smoothing / (double)V);
+  a.s = z_loss_scale;
+  a.reduction = reduction;
+  a.lse = lse; a.n_valid = n_valid; a.grad = grad_loss;
+  a.coef = ws + g.off_coef;
+  a.yv = (int*)(ws + g.off_yv);
+  a.slab = ws + g.off_slab;
+  a.ldS = g.slab_cols;
+  a.dx_acc = (float*)(ws + g.off_dxacc);
+  a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
+  a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (flce::launch_bwd_prepare(a, s) != hipSuccess) return FLCE_ERR_HIP;
+  const int64_t cols = g.slab_cols;
+  const int64_t nslab = cdiv(V, cols);
+  for (int64_t k = 0; k < nslab; ++k) {
+    const int64_t vs = k * cols;
+    const int64_t width = (V - vs) < cols ? (V - vs) : cols;
+    int mode = flce::kDxAccum;
+    if (nslab == 1) mode = flce::kDxOnly;
+    else if (k == 0) mode = flce::kDxFirst;
+    else if (k == nslab - 1) mode = flce::kDxLast;
+    if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
+  }
+  if (want_db && flce::launch_bwd_db(a, dtype, s) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
+}  // extern "C"

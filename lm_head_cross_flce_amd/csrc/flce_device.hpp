@@ -1,0 +1,305 @@
+// Device building blocks for the FLCE kernels on gfx950 (CDNA4, wave64).
+//
+// Every contraction of the method is computed by one tile routine: a 256 x 256
+// output tile per 256-thread workgroup (4 waves in a 2 x 2 grid, 128 x 128 per
+// wave as 4 x 4 blocks of 32 x 32 MFMA accumulators), K streamed through
+// double-buffered LDS in 128-byte slices (64 bf16 or 32 fp32 per row).
+//
+//   C[m, n] = sum_k A[m, k] * B[n, k]
+//
+// Each operand is read from global memory either "K-contiguous" (element
+// (m, k) at p[m * ld + k]) or "M-contiguous" (element (m, k) at p[k * ld + m]).
+// LDS always holds [row][k] with K contiguous, so the MFMA fragment reads are
+// one or two 16-byte LDS loads per lane; M-contiguous operands are transposed
+// in registers (8 x 8 blocks of bf16, 4 x 4 of fp32) on their way to LDS.
+//
+// MFMA output layout (32 x 32 blocks): accumulator element r of lane l holds
+// row 8 * (r / 4) + 4 * (l / 32) + (r % 4) and column l % 32 of its block, so
+// one lane owns one column and 16 rows, four of them consecutive.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kTile = 256;                  // BM = BN
+constexpr int kWaveTile = 128;
+constexpr int kRowBytes = 144;              // 128 B of K per row + 16 B pad (bank spread)
+constexpr int kBufBytes = kTile * kRowBytes;
+constexpr int kSmemBytes = 4 * kBufBytes;   // {A, B} x 2 stages
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Storage type tags: bf16 values are carried as uint16_t bit patterns.
+template <class T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;    // elements per 16-byte chunk
+  static constexpr int kBK = 64;    // K per LDS stage
+};
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  static constexpr int kBK = 32;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+template <class T> __device__ __forceinline__ float load_as_f32(const T* p);
+template <> __device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_f32(*p);
+}
+
+// Round-to-nearest-even pack of two floats into bf16x2 (hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Store four consecutive output values (one lane's run of four rows) as T.
+template <class T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(f32x4*)p = f32x4{a, b, c, d};
+}
+template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  *(u32x2*)p = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Operands and global -> LDS staging
+// ---------------------------------------------------------------------------
+
+template <class T> struct Opnd {
+  const T* p;
+  int64_t ld;    // leading dimension in elements
+  int mext;      // valid extent along the tile's M (row) dimension
+  int kext;      // valid extent along K
+};
+
+// One stage of one operand: 256 rows x kBK, 8 x 16 bytes per thread.
+template <class T, bool KCONTIG> struct Stager;
+
+// K-contiguous: thread (kc = tid % 8, rr = tid / 8) loads 16 bytes of K at
+// column chunk kc of rows rr + 32 q.  Requires kext % kVec == 0.
+template <class T> struct Stager<T, true> {
+  u32x4 r[8];
+  __device__ __forceinline__ void load(const Opnd<T>& o, int m0, int k0, int tid) {
+    const int kc = tid & 7, rr = tid >> 3;
+    const int gk = k0 + kc * Elem<T>::kVec;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int gm = m0 + rr + 32 * q;
+      if (gm < o.mext && gk < o.kext)
+        r[q] = *(const u32x4*)(o.p + (int64_t)gm * o.ld + gk);
+      else
+        r[q] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    const int kc = tid & 7, rr = tid >> 3;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *(u32x4*)(buf + (rr + 32 * q) * kRowBytes + kc * 16) = r[q];
+  }
+};
+
+// M-contiguous bf16: thread (kc = tid % 8, mc = tid / 8) loads rows
+// k0 + 8 kc + e (e < 8) at columns m0 + 8 mc .. + 7, then writes the
+// transposed 8 x 8 block.  Requires mext % 8 == 0.
+template <> struct Stager<uint16_t, false> {
+  u32x4 r[8];
+  __device__ __forceinline__ void load(const Opnd<uint16_t>& o, int m0, int k0, int tid) {
+    const int kc = tid & 7, mc = tid >> 3;
+    const int gm = m0 + mc * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int gk = k0 + kc * 8 + e;
+      if (gk < o.kext && gm < o.mext)
+        r[e] = *(const u32x4*)(o.p + (int64_t)gk * o.ld + gm);
+      else
+        r[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    const int kc = tid & 7, mc = tid >> 3;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      u32x4 ev, od;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a = r[2 * w][p], b = r[2 * w + 1][p];
+        ev[w] = (a & 0xffffu) | (b << 16);
+        od[w] = (a >> 16) | (b & 0xffff0000u);
+      }
+      *(u32x4*)(buf + (mc * 8 + 2 * p) * kRowBytes + kc * 16) = ev;
+      *(u32x4*)(buf + (mc * 8 + 2 * p + 1) * kRowBytes + kc * 16) = od;
+    }
+  }
+};
+
+// M-contiguous fp32: 4 x 4 blocks, two per thread (mc = tid / 8 + 32 p).
+template <> struct Stager<float, false> {
+  u32x4 r[8];
+  __device__ __forceinline__ void load(const Opnd<float>& o, int m0, int k0, int tid) {
+    const int kc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int gm = m0 + ((tid >> 3) + 32 * p) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gk = k0 + kc * 4 + e;
+        if (gk < o.kext && gm < o.mext)
+          r[4 * p + e] = *(const u32x4*)(o.p + (int64_t)gk * o.ld + gm);
+        else
+          r[4 * p + e] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    const int kc = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int mc = (tid >> 3) + 32 * p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 t = {r[4 * p][i], r[4 * p + 1][i], r[4 * p + 2][i], r[4 * p + 3][i]};
+        *(u32x4*)(buf + (mc * 4 + i) * kRowBytes + kc * 16) = t;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA over one LDS stage
+// ---------------------------------------------------------------------------
+
+template <class T> struct Mma;
+
+template <> struct Mma<uint16_t> {
+  // 4 sub-steps of K = 16: v_mfma_f32_32x32x16_bf16.
+  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const char* bA, const char* bB,
+                                               int wm, int wn, int lane) {
+    const int rl = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[4], b[4];
+      const int koff = (s * 16 + 8 * kh) * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(bA + (wm * 128 + 32 * i + rl) * kRowBytes + koff);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *(const u32x4*)(bB + (wn * 128 + 32 * j + rl) * kRowBytes + koff);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+template <> struct Mma<float> {
+  // 2 sub-steps of K = 16, each 8 x v_mfma_f32_32x32x2_f32.  Lane half kh holds
+  // logical k = 16 s + 8 kh + e for register e; instruction e pairs k and k + 8.
+  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const char* bA, const char* bB,
+                                               int wm, int wn, int lane) {
+    const int rl = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f32x4 a[4][2], b[4][2];
+      const int koff = (s * 16 + 8 * kh) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = bA + (wm * 128 + 32 * i + rl) * kRowBytes + koff;
+        a[i][0] = *(const f32x4*)p;
+        a[i][1] = *(const f32x4*)(p + 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const char* p = bB + (wn * 128 + 32 * j + rl) * kRowBytes + koff;
+        b[j][0] = *(const f32x4*)p;
+        b[j][1] = *(const f32x4*)(p + 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e >> 2][e & 3], b[j][e >> 2][e & 3],
+                                                             acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.
+// Ends with a workgroup barrier, so LDS may be reused right after it returns.
+// ---------------------------------------------------------------------------
+
+template <class T, bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
+                                          const Opnd<T>& B, int n0, int K, char* smem, int tid) {
+  constexpr int kBK = Elem<T>::kBK;
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  char* bufA[2] = {smem, smem + kBufBytes};
+  char* bufB[2] = {smem + 2 * kBufBytes, smem + 3 * kBufBytes};
+  Stager<T, AK> sa;
+  Stager<T, BK> sb;
+  const int KT = (K + kBK - 1) / kBK;
+  sa.load(A, m0, 0, tid);
+  sb.load(B, n0, 0, tid);
+  sa.store(bufA[0], tid);
+  sb.store(bufB[0], tid);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      sa.load(A, m0, (kt + 1) * kBK, tid);
+      sb.load(B, n0, (kt + 1) * kBK, tid);
+    }
+    Mma<T>::stage(acc, bufA[cur], bufB[cur], wm, wn, lane);
+    if (more) {
+      sa.store(bufA[cur ^ 1], tid);
+      sb.store(bufB[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile scheduling
+// ---------------------------------------------------------------------------
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber so that 1/8 of the grid of consecutive logical tiles lands on
+// one XCD, then raster the logical tiles in groups of 8 M-tiles so those
+// neighbours share A and B panels in that L2.
+__device__ __forceinline__ void tile_coords(int w, int G, int TM, int TN, int& tm, int& tn) {
+  int t = w;
+  if ((G & 7) == 0) t = (w & 7) * (G >> 3) + (w >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * TN;
+  const int group = t / per_group;
+  const int fm = group * GM;
+  const int gm = min(GM, TM - fm);
+  const int within = t - group * per_group;
+  tm = fm + within % gm;
+  tn = within / gm;
+}
+
+}  // namespace flce

@@ -1,0 +1,501 @@
+// FLCE kernels for gfx950.
+//
+// Forward (statistics only; logits recomputed in backward, the schedule of
+// DeepSpeed PR 8792):
+//   fwd_lse_kernel     logits tiles z = W x^T (+ b) on MFMA; the epilogue folds
+//                      each tile into per-token online max / sum-exp (the
+//                      online softmax the fla kernel cites), the running sum of
+//                      logits (label smoothing) and the target logit.
+//   fwd_combine_kernel merges the per-phase partials: lse = m + log d and the
+//                      per-row loss of the label-smoothed CE plus z-loss.
+//   fwd_finalize       fixed-order sum and non-ignored count (no host sync).
+// Backward, one vocabulary slab at a time:
+//   bwd_coef_kernel    per-token c_n (upstream grad, 1/T for mean) folded with
+//                      the z-loss factor (1 + 2 s lse) of Liger PR 239.
+//   bwd_dz_kernel      recomputes a logits tile and turns it into dlogits
+//                      dz = c [(1 + 2 s lse) p - eps/V - (1 - eps) [j = y]],
+//                      written to the slab; optional db partial sums (fp32).
+//   bwd_dw_kernel      dW[slab] = dz^T x with K = all tokens, fp32 in
+//                      registers, written once in W's dtype.
+//   bwd_dx_kernel      dx += dz W[slab] into an fp32 accumulator; the last
+//                      slab writes dx in x's dtype.
+//   bwd_db_kernel      fixed-order sum of the db partials.
+#include "flce_device.hpp"
+#include "flce_launch.hpp"
+
+namespace flce {
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers.  Lane half g = lane / 32; for accumulator element e of
+// block (i, j) the row inside the wave tile is 32 i + 8 (e / 4) + 4 g + e % 4
+// and the column is 32 j + lane % 32.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int row_off(int i, int e) { return 32 * i + 8 * (e >> 2) + (e & 3); }
+
+// acc[i][j][e] += b[row] for every column; rb = first row of this lane.
+template <class T>
+__device__ __forceinline__ void add_bias(f32x16 (&acc)[4][4], const T* b, int rb, int V) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r0 = rb + 32 * i + 8 * q;
+      float bv[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bv[s] = (r0 + s < V) ? load_as_f32<T>(b + r0 + s) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[i][j][4 * q + s] += bv[s];
+    }
+  }
+}
+
+// Fold column j of the tile into the running (m, d) and sum of logits.
+template <bool SMOOTH, bool RAGGED>
+__device__ __forceinline__ void lse_col(f32x16 (&acc)[4][4], int j, float& m, float& d, float& sz, int rb,
+                                        int V) {
+  float tmax = -INFINITY, zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float z = acc[i][j][e];
+      if (RAGGED) {
+        const bool ok = rb + row_off(i, e) < V;
+        if (SMOOTH) zs += ok ? z : 0.f;
+        z = ok ? z : -INFINITY;
+        acc[i][j][e] = z;
+      } else if (SMOOTH) {
+        zs += z;
+      }
+      tmax = fmaxf(tmax, z);
+    }
+  const float mn = fmaxf(m, tmax);
+  if (!RAGGED || mn != -INFINITY) {
+    const float nml = -mn * kLog2e;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ps += fast_exp2(fmaf(acc[i][j][e], kLog2e, nml));
+    d = d * fast_exp2((m - mn) * kLog2e) + ps;  // m = -inf: the factor is 0
+    m = mn;
+  }
+  if (SMOOTH) sz += zs;
+}
+
+// If this lane's rows contain target row y, copy the logit.  Wave-uniform
+// branch: most tiles hold no target of any of the wave's columns.
+__device__ __forceinline__ void gather_target(const f32x16 (&acc)[4][4], int j, int y, int rb, float& zy) {
+  const int t = y - rb;
+  const bool own = (t >= 0) && (t < kWaveTile) && ((t & 4) == 0);
+  if (__ballot(own)) {
+    float val = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (t == row_off(i, e)) val = acc[i][j][e];
+    if (own) zy = val;
+  }
+}
+
+__device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2) {
+  const float mn = fmaxf(m, m2);
+  float r = 0.f;
+  if (m != -INFINITY) r += d * fast_exp2((m - mn) * kLog2e);
+  if (m2 != -INFINITY) r += d2 * fast_exp2((m2 - mn) * kLog2e);
+  m = mn;
+  d = r;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+
+// Workgroup w owns token tile nt and the vocabulary tiles ph, ph + P, ...
+// When NT % 8 == 0 the 1/8 of the grid on one XCD covers NT/8 token tiles
+// times all P phases, so each XCD streams W tiles that its neighbours reuse.
+template <class T, bool BIAS, bool SMOOTH>
+__global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int w = blockIdx.x;
+  int nt, ph;
+  if ((a.NT & 7) == 0) {
+    const int slot = w >> 3;
+    ph = slot % a.P;
+    nt = (w & 7) * (a.NT >> 3) + slot / a.P;
+  } else {
+    ph = w % a.P;
+    nt = w / a.P;
+  }
+  const int n0 = nt * kTile;
+  const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
+  const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
+
+  int ycol[4];
+  float m[4], d[4], sz[4], zy[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
+    const int64_t t = n < a.N ? a.targets[n] : a.ignore_index;
+    ycol[j] = (t == a.ignore_index) ? -1 : (int)t;
+    m[j] = -INFINITY;
+    d[j] = 0.f;
+    sz[j] = 0.f;
+    zy[j] = 0.f;
+  }
+
+  f32x16 acc[4][4];
+  for (int vt = ph; vt < a.VT; vt += a.P) {
+    const int v0 = vt * kTile;
+    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, smem, tid);
+    const int rb = v0 + wm * kWaveTile + 4 * (lane >> 5);
+    if (BIAS) add_bias<T>(acc, (const T*)a.b, rb, a.V);
+    if (v0 + kTile <= a.V) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gather_target(acc, j, ycol[j], rb, zy[j]);
+        lse_col<SMOOTH, false>(acc, j, m[j], d[j], sz[j], rb, a.V);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gather_target(acc, j, ycol[j], rb, zy[j]);
+        lse_col<SMOOTH, true>(acc, j, m[j], d[j], sz[j], rb, a.V);
+      }
+    }
+  }
+
+  // Lanes l and l + 32 hold the same columns (different rows): merge them.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float m2 = __shfl_xor(m[j], 32), d2 = __shfl_xor(d[j], 32);
+    const float s2 = __shfl_xor(sz[j], 32), y2 = __shfl_xor(zy[j], 32);
+    merge_md(m[j], d[j], m2, d2);
+    sz[j] += s2;
+    zy[j] += y2;
+  }
+  // Then the two waves that share columns (wm = 0, 1).
+  f32x4* red = (f32x4*)smem;
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wn * kWaveTile + 32 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+    f32x4* part = (f32x4*)a.partials;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 o = red[wn * kWaveTile + 32 * j + lane];
+      merge_md(m[j], d[j], o[0], o[1]);
+      const int n = n0 + wn * kWaveTile + 32 * j + lane;
+      if (n < a.N) part[(int64_t)ph * a.N + n] = f32x4{m[j], d[j], sz[j] + o[2], zy[j] + o[3]};
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) fwd_combine_kernel(FwdLaunch a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const f32x4* part = (const f32x4*)a.partials;
+  float m = -INFINITY, d = 0.f, sz = 0.f, zy = 0.f;
+  for (int p = 0; p < a.P; ++p) {
+    const f32x4 q = part[(int64_t)p * a.N + n];
+    merge_md(m, d, q[0], q[1]);
+    sz += q[2];
+    zy += q[3];
+  }
+  const float lse = m + logf(d);
+  const bool valid = a.targets[n] != a.ignore_index;
+  const float l = valid ? (lse - (1.f - a.eps) * zy - a.eps_over_v * sz + a.s * lse * lse) : 0.f;
+  a.lse[n] = lse;
+  a.rowloss[n] = l;
+  if (a.reduction == kNone) a.loss[n] = l;
+}
+
+__global__ void __launch_bounds__(1024) fwd_finalize_kernel(FwdLaunch a) {
+  __shared__ double ssum[1024];
+  __shared__ long long scnt[1024];
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  long long c = 0;
+  for (int n = tid; n < a.N; n += 1024) {
+    s += (double)a.rowloss[n];
+    c += (a.targets[n] != a.ignore_index) ? 1 : 0;
+  }
+  ssum[tid] = s;
+  scnt[tid] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) {
+      ssum[tid] += ssum[tid + w];
+      scnt[tid] += scnt[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.n_valid[0] = scnt[0];
+    if (a.reduction == kSum) a.loss[0] = (float)ssum[0];
+    if (a.reduction == kMean) a.loss[0] = scnt[0] > 0 ? (float)(ssum[0] / (double)scnt[0]) : 0.f;
+  }
+}
+
+template <class T>
+static hipError_t launch_forward_t(const FwdLaunch& a, hipStream_t st) {
+  const int G = a.NT * a.P;
+  const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
+  if (bias && smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, true, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) hipLaunchKernelGGL((fwd_lse_kernel<T, true, false>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, false, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((fwd_lse_kernel<T, false, false>), dim3(G), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
+  return dtype == 1 ? launch_forward_t<uint16_t>(a, st) : launch_forward_t<float>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const int64_t t = a.targets[n];
+  const bool valid = t != a.ignore_index;
+  const float g = a.reduction == kNone ? a.grad[n] : a.grad[0];
+  const long long T = a.n_valid[0];
+  float c = g;
+  if (a.reduction == kMean) c = T > 0 ? g / (float)T : 0.f;
+  if (!valid) c = 0.f;
+  const float lse = a.lse[n];
+  ((f32x4*)a.coef)[n] = f32x4{c * (1.f + 2.f * a.s * lse), c * a.eps_over_v, c * (1.f - a.eps), lse * kLog2e};
+  a.yv[n] = valid ? (int)t : -1;
+}
+
+// Sum 64 per-lane values over the 32 lanes of each wave half, halving the
+// values held per lane at every step; afterwards lane l holds the totals of
+// values 2 (l % 32) and 2 (l % 32) + 1.
+template <int HALF>
+__device__ __forceinline__ void xreduce_step(float (&v)[64], int lane) {
+  constexpr int mask = HALF / 2;
+  const bool up = (lane & mask) != 0;
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    const float keep = up ? v[HALF + k] : v[k];
+    const float send = up ? v[k] : v[HALF + k];
+    v[k] = keep + __shfl_xor(send, mask);
+  }
+}
+
+template <class T, bool RAGGED>
+__device__ __forceinline__ void dz_tile(f32x16 (&acc)[4][4], const BwdLaunch& a, int n0, int rb, int wn,
+                                        int lane) {
+  const f32x4* coef = (const f32x4*)a.coef;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
+    const f32x4 cf = n < a.N ? coef[n] : f32x4{0.f, 0.f, 0.f, INFINITY};
+    const int y = n < a.N ? a.yv[n] : -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(fmaf(acc[i][j][e], kLog2e, -cf[3]));
+        float dz = fmaf(cf[0], p, -cf[1]);
+        if (RAGGED && rb + row_off(i, e) >= a.V) dz = 0.f;
+        acc[i][j][e] = dz;
+      }
+    const int t = y - rb;
+    const bool own = (t >= 0) && (t < kWaveTile) && ((t & 4) == 0);
+    if (__ballot(own)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (own && t == row_off(i, e)) acc[i][j][e] -= cf[2];
+    }
+  }
+}
+
+template <class T, bool BIAS, bool DB>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
+  const int v0 = vs + tm * kTile, n0 = tn * kTile;
+  const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
+  const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
+  f32x16 acc[4][4];
+  gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, smem, tid);
+
+  const int g = lane >> 5;
+  const int rb = v0 + wm * kWaveTile + 4 * g;
+  if (BIAS) add_bias<T>(acc, (const T*)a.b, rb, a.V);
+  if (v0 + kTile <= a.V) dz_tile<T, false>(acc, a, n0, rb, wn, lane);
+  else dz_tile<T, true>(acc, a, n0, rb, wn, lane);
+
+  T* slab = (T*)a.slab;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
+    if (n < a.N) {
+      T* rowp = slab + (int64_t)n * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store4<T>(rowp + 32 * i + 8 * q, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]);
+    }
+  }
+
+  if (DB) {
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[16 * i + e] = acc[i][0][e] + acc[i][1][e] + acc[i][2][e] + acc[i][3][e];
+    xreduce_step<32>(v, lane);
+    xreduce_step<16>(v, lane);
+    xreduce_step<8>(v, lane);
+    xreduce_step<4>(v, lane);
+    xreduce_step<2>(v, lane);
+    float* red = (float*)smem;  // [wm][128 rows]; operand buffers are free now
+    if (wn == 1) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 2 * (lane & 31) + k;
+        red[wm * kWaveTile + row_off(e >> 4, e & 15) + 4 * g] = v[k];
+      }
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 2 * (lane & 31) + k;
+        const int rl = row_off(e >> 4, e & 15) + 4 * g;
+        const int row = v0 + wm * kWaveTile + rl;
+        if (row < a.V) a.dbp[(int64_t)tn * a.V + row] = v[k] + red[wm * kWaveTile + rl];
+      }
+    }
+  }
+}
+
+// dW[vs + v, h] for the slab: C[h][v] = sum_n x[n][h] dz[n][v].
+template <class T>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
+                                                             int TN) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, TM, TN, tm, tn);
+  const int h0 = tm * kTile, v0 = tn * kTile;
+  const Opnd<T> A{(const T*)a.x, a.H, a.H, a.N};
+  const Opnd<T> B{(const T*)a.slab, a.ldS, wpad, a.N};
+  f32x16 acc[4][4];
+  gemm_tile<T, false, false>(acc, A, h0, B, v0, a.N, smem, tid);
+  T* dW = (T*)a.dW;
+  const int g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = v0 + wn * kWaveTile + 32 * j + (lane & 31);
+    if (v >= width) continue;
+    T* rowp = dW + (int64_t)(vs + v) * a.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
+        if (h < a.H)
+          store4<T>(rowp + h, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+  }
+}
+
+// dx[n, h] += sum_{v in slab} dz[n][v] W[vs + v][h]: C[h][n].
+template <class T>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
+                                                             int mode) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
+  const int h0 = tm * kTile, n0 = tn * kTile;
+  const Opnd<T> A{(const T*)a.W + (int64_t)vs * a.H, a.H, a.H, width};
+  const Opnd<T> B{(const T*)a.slab, a.ldS, a.N, wpad};
+  f32x16 acc[4][4];
+  gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, smem, tid);
+  const int g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
+        if (h >= a.H) continue;
+        f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        f32x4* pa = (f32x4*)(a.dx_acc + (int64_t)n * a.H + h);
+        if (mode == kDxAccum || mode == kDxLast) v += *pa;
+        if (mode == kDxFirst || mode == kDxAccum) *pa = v;
+        else store4<T>((T*)a.dx + (int64_t)n * a.H + h, v[0], v[1], v[2], v[3]);
+      }
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= a.V) return;
+  float s = 0.f;
+  for (int t = 0; t < a.NT; ++t) s += a.dbp[(int64_t)t * a.V + v];
+  if (sizeof(T) == 4) ((float*)a.db)[v] = s;
+  else ((uint16_t*)a.db)[v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
+}
+
+hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_coef_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int dx_mode, bool want_db,
+                                    hipStream_t st) {
+  const int wpad = (width + 7) & ~7;
+  const int TV = (width + kTile - 1) / kTile;
+  const int TH = (a.H + kTile - 1) / kTile;
+  const bool bias = a.b != nullptr;
+  const dim3 blk(kThreads);
+  const dim3 gdz(TV * a.NT);
+  if (bias && want_db) hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
+  else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
+  else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
+  if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  if (a.dx) hipLaunchKernelGGL((bwd_dx_kernel<T>), dim3(TH * a.NT), blk, 0, st, a, vs, width, wpad, TH, dx_mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
+                           hipStream_t st) {
+  return dtype == 1 ? launch_bwd_slab_t<uint16_t>(a, vs, width, dx_mode, want_db, st)
+                    : launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, st);
+}
+
+hipError_t launch_bwd_db(const BwdLaunch& a, int dtype, hipStream_t st) {
+  if (dtype == 1) hipLaunchKernelGGL((bwd_db_kernel<uint16_t>), dim3((a.V + 255) / 256), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_db_kernel<float>), dim3((a.V + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace flce

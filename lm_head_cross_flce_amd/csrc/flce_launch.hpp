@@ -1,0 +1,49 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+enum Reduction { kNone = 0, kSum = 1, kMean = 2 };
+enum DxMode { kDxFirst = 0, kDxAccum = 1, kDxLast = 2, kDxOnly = 3 };
+
+struct FwdLaunch {
+  const void* x; const void* W; const void* b; const int64_t* targets;
+  int N, H, V;
+  int NT, P, VT;          // token tiles, vocabulary phases, vocabulary tiles
+  int64_t ignore_index;
+  float eps, eps_over_v, s;
+  int reduction;
+  void* partials;         // float4 [P][N]
+  float* rowloss;         // [N]
+  float* loss;            // [1] or [N]
+  float* lse;             // [N]
+  int64_t* n_valid;       // [1]
+};
+
+struct BwdLaunch {
+  const void* x; const void* W; const void* b; const int64_t* targets;
+  int N, H, V;
+  int NT;
+  int64_t ignore_index;
+  float eps, eps_over_v, s;
+  int reduction;
+  const float* lse; const int64_t* n_valid; const float* grad;
+  void* coef;             // float4 [N]
+  int* yv;                // [N]
+  void* slab; int64_t ldS;
+  float* dx_acc;          // [N][H]
+  float* dbp;             // [NT][V]
+  void* dx; void* dW; void* db;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  Each returns the launch error code.
+hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st);
+hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st);
+hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
+                           hipStream_t st);
+hipError_t launch_bwd_db(const BwdLaunch& a, int dtype, hipStream_t st);
+
+}  // namespace flce

@@ -1,0 +1,160 @@
+"""PyTorch-facing binding of the FLCE library.
+
+PyTorch supplies device memory and the current stream; every step of the
+computation runs in libflce.so.  ``flce_forward`` / ``flce_backward`` take
+tensors and mirror the C entry points of the same names; the autograd function
+and module wrap them the way fla's FusedLinearCrossEntropyLoss wraps its
+kernels (fla/modules/fused_linear_cross_entropy.py: the module flattens
+[batch, seq, hidden] to [tokens, hidden]), with reduction "none" added and the
+gradients produced in backward rather than in forward (DeepSpeed PR 8792).
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.FLCE_BF16, torch.float32: _lib.FLCE_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+    return _DTYPES[t.dtype]
+
+
+def _reduction_code(reduction: str) -> int:
+    if reduction not in _lib.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {tuple(_lib.REDUCTIONS)}")
+    return _lib.REDUCTIONS[reduction]
+
+
+def _prep(x, W, b, targets):
+    if x.dim() != 2 or W.dim() != 2:
+        raise ValueError("x must be [N, H] and W must be [V, H]")
+    if not x.is_cuda:
+        raise ValueError("tensors must live on a GPU")
+    if W.dtype != x.dtype or (b is not None and b.dtype != x.dtype):
+        raise TypeError("x, W and b must share one dtype")
+    x = x.contiguous()
+    W = W.contiguous()
+    b = b.contiguous() if b is not None else None
+    targets = targets.reshape(-1).to(torch.int64).contiguous()
+    return x, W, b, targets
+
+
+def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype, has_bias: bool,
+                        reduction: str = "mean") -> Tuple[int, int]:
+    return _lib.flce_workspace_size(N, H, V, _DTYPES[dtype], has_bias, _reduction_code(reduction))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
+                 label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
+                 reduction: str = "mean", workspace: Optional[torch.Tensor] = None):
+    """Returns (loss, lse, n_valid): loss float32 [1] (sum/mean) or [N] (none)."""
+    x, W, b, targets = _prep(x, W, b, targets)
+    N, H = x.shape
+    V = W.shape[0]
+    dt, red = _dtype_code(x), _reduction_code(reduction)
+    dev = x.device
+    fwd_bytes, _ = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    if workspace is None or workspace.numel() < fwd_bytes:
+        workspace = torch.empty(max(fwd_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(N if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_forward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                          float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                          loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), workspace.data_ptr(),
+                          workspace.numel(), stream)
+    return loss, lse, n_valid
+
+
+def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
+                  lse: torch.Tensor, n_valid: torch.Tensor, grad_loss: torch.Tensor,
+                  label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
+                  reduction: str = "mean", need_dx: bool = True, need_dW: bool = True,
+                  need_db: bool = True, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[Tuple] = None):
+    """Returns (dx, dW, db) in the input dtype (None where not requested)."""
+    x, W, b, targets = _prep(x, W, b, targets)
+    N, H = x.shape
+    V = W.shape[0]
+    dt, red = _dtype_code(x), _reduction_code(reduction)
+    dev = x.device
+    g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
+    if g.numel() != (N if reduction == "none" else 1):
+        raise ValueError("grad_loss must have N entries for none and one otherwise")
+    _, bwd_bytes = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    if workspace is None or workspace.numel() < bwd_bytes:
+        workspace = torch.empty(max(bwd_bytes, 1), dtype=torch.uint8, device=dev)
+    if out is not None:
+        dx, dW, db = out
+    else:
+        dx = torch.empty_like(x) if need_dx else None
+        dW = torch.empty_like(W) if need_dW else None
+        db = torch.empty_like(b) if (need_db and b is not None) else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                           float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                           lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db),
+                           workspace.data_ptr(), workspace.numel(), stream)
+    return dx, dW, db
+
+
+class FusedLinearCrossEntropyFunction(torch.autograd.Function):
+    """loss = FLCE(x, target, weight, bias); saves only lse and the count."""
+
+    @staticmethod
+    def forward(ctx, x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
+                z_loss_scale=0.0, reduction="mean"):
+        loss, lse, n_valid = flce_forward(x, weight, bias, target, label_smoothing, z_loss_scale,
+                                          ignore_index, reduction)
+        ctx.save_for_backward(x, target, weight, bias, lse, n_valid)
+        ctx.opts = (ignore_index, label_smoothing, z_loss_scale, reduction)
+        return loss if reduction == "none" else loss.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad):
+        x, target, weight, bias, lse, n_valid = ctx.saved_tensors
+        ignore_index, eps, s, reduction = ctx.opts
+        dx, dW, db = flce_backward(x, weight, bias, target, lse, n_valid, grad, eps, s, ignore_index,
+                                   reduction, need_dx=ctx.needs_input_grad[0],
+                                   need_dW=ctx.needs_input_grad[2],
+                                   need_db=bias is not None and ctx.needs_input_grad[3])
+        return dx, None, dW, db, None, None, None, None
+
+
+def fused_linear_cross_entropy_loss(x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
+                                    z_loss_scale=0.0, reduction="mean"):
+    """Functional form: x [N, H], target [N], weight [V, H], bias [V] or None."""
+    return FusedLinearCrossEntropyFunction.apply(x, target, weight, bias, ignore_index, label_smoothing,
+                                                 z_loss_scale, reduction)
+
+
+class FusedLinearCrossEntropyLoss(torch.nn.Module):
+    """Module form; x may be [..., H] and target [...]; they are flattened."""
+
+    def __init__(self, ignore_index: int = -100, label_smoothing: float = 0.0, z_loss_scale: float = 0.0,
+                 reduction: str = "mean"):
+        super().__init__()
+        _reduction_code(reduction)
+        self.ignore_index = ignore_index
+        self.label_smoothing = label_smoothing
+        self.z_loss_scale = z_loss_scale
+        self.reduction = reduction
+
+    def forward(self, x, target, weight, bias=None):
+        return fused_linear_cross_entropy_loss(x.reshape(-1, x.shape[-1]), target.reshape(-1), weight, bias,
+                                               self.ignore_index, self.label_smoothing, self.z_loss_scale,
+                                               self.reduction)

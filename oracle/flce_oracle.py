@@ -147,8 +147,12 @@ def _chunks(N, rows_per_chunk):
     return [(i, min(N, i + rows_per_chunk)) for i in range(0, N, rows_per_chunk)]
 
 
+def _workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def _pool():
-    return ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return ThreadPoolExecutor(_workers())
 
 
 def forward(x, W, b, targets, eps=0.0, s=0.0, ignore_index=-100, reduction="mean",
@@ -197,13 +201,20 @@ def backward(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
         dx[lo:hi] = dz @ W64
         parts[k] = (dz.T @ x64, dz.sum(axis=0))
 
-    with _pool() as ex:
-        list(ex.map(work, range(len(chunks))))
     dW = np.zeros((V, H))
     db = np.zeros(V)
-    for pw, pb in parts:  # fixed order
-        dW += pw
-        db += pb
+    # Chunks run in parallel batches sized so their [V, H] partials stay under
+    # ~2 GB; partials are added in chunk order.
+    batch = max(1, min(_workers(), int(2e9 // (8 * V * H + 1))))
+    with _pool() as ex:
+        for k0 in range(0, len(chunks), batch):
+            ks = range(k0, min(len(chunks), k0 + batch))
+            list(ex.map(work, ks))
+            for k in ks:
+                pw, pb = parts[k]
+                dW += pw
+                db += pb
+                parts[k] = None
     return BackwardResult(dx, dW, db if b is not None else None)
 
 

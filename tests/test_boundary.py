@@ -1,0 +1,153 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/flce.h declares, and
+reject bad arguments on the host before anything is enqueued.  Each call below
+carries exactly one invalid argument, caught by validation, so no kernel is
+ever launched with the placeholder addresses used here.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from lm_head_cross_flce_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+# Placeholder addresses: 256-byte aligned, never dereferenced (validation fails first).
+P = 0x100000
+P2 = 0x200000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from lm_head_cross_flce_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(flce_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and they are real dynamic symbols of the shared object
+    so = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(so, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert _lib.status_string(s) not in ("ok", "unknown status")
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_workspace_size_arithmetic(lib):
+    # forward: one fp32x4 partial per (phase, token) plus one fp32 per token
+    f, b = _lib.flce_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 2)
+    NT, VT = 32, 501
+    P = min(VT, 256 // NT)
+    assert f >= P * 8192 * 16 + 8192 * 4
+    slab = _lib.flce_backward_slab_cols(8192, 4096, 128256, _lib.FLCE_BF16)
+    assert slab % 256 == 0 and slab >= 256
+    need = 8192 * slab * 2 + 8192 * 4096 * 4 + NT * 128256 * 4 + 8192 * 20
+    assert need <= b <= need + 8 * 256
+    # extra memory at the Llama-3-sized head stays under 10% of the fp32 logits
+    assert f + b < 0.1 * 8192 * 128256 * 4
+    # no bias: no db partials
+    _, b_nobias = _lib.flce_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, False, 2)
+    assert b - b_nobias >= NT * 128256 * 4
+
+
+def test_slab_width_heuristic(lib):
+    # enough vocabulary tiles that one slab's dW tiles cover 256 CUs
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 4096
+    assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 8192
+    assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 16384
+    assert _lib.flce_backward_slab_cols(64, 128, 1000, 0) == 1024     # capped at V rounded up
+    assert _lib.flce_backward_slab_cols(64, 12, 1000, 0) == 0         # H % 8 != 0
+
+
+def test_slab_debug_override(lib, monkeypatch):
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 512
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "100")   # not a multiple of 256: ignored
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 4096
+
+
+def _fwd(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100,
+                red=2, loss=P2, lse=P2, nv=P2, ws=P2, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.flce_forward(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"], args["V"],
+                            args["dtype"], args["eps"], args["s"], args["ign"], args["red"], args["loss"],
+                            args["lse"], args["nv"], args["ws"], args["wsb"], args["stream"])
+
+
+def _bwd(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100,
+                red=2, lse=P2, nv=P2, g=P2, dx=P2, dW=P2, db=None, ws=P2, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.flce_backward(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"], args["V"],
+                             args["dtype"], args["eps"], args["s"], args["ign"], args["red"], args["lse"],
+                             args["nv"], args["g"], args["dx"], args["dW"], args["db"], args["ws"], args["wsb"],
+                             args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=0), 1), (dict(V=0), 1), (dict(N=-5), 1),
+    (dict(H=12), 2), (dict(dtype=7), 2),
+    (dict(eps=-0.1), 1), (dict(eps=1.5), 1), (dict(eps=float("nan")), 1),
+    (dict(s=-1.0), 1), (dict(s=float("inf")), 1),
+    (dict(red=3), 1), (dict(red=-1), 1),
+    (dict(x=None), 1), (dict(W=None), 1), (dict(targets=None), 1),
+    (dict(loss=None), 1), (dict(lse=None), 1), (dict(nv=None), 1),
+    (dict(x=P + 8), 1), (dict(W=P + 2), 1), (dict(targets=P + 4), 1),
+    (dict(wsb=16), 3), (dict(ws=None), 1), (dict(ws=P2 + 8), 1),
+])
+def test_forward_validation(lib, over, code):
+    assert _fwd(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=20), 2), (dict(eps=2.0), 1), (dict(s=-0.5), 1), (dict(red=9), 1),
+    (dict(lse=None), 1), (dict(nv=None), 1), (dict(g=None), 1), (dict(x=None), 1),
+    (dict(dx=P2 + 4), 1), (dict(dW=P2 + 8), 1),
+    (dict(wsb=100), 3), (dict(ws=None), 1),
+])
+def test_backward_validation(lib, over, code):
+    assert _bwd(lib, **over) == code
+
+
+def test_backward_with_nothing_requested_is_a_no_op(lib):
+    # dx, dW and db all NULL: returns OK without launching anything.
+    assert _bwd(lib, dx=None, dW=None, db=None) == 0
+
+
+def test_python_binding_raises_on_error(lib):
+    with pytest.raises(_lib.FlceError) as e:
+        _lib.flce_workspace_size(0, 128, 1000, 0, False, 2)
+    assert e.value.status == _lib.FLCE_ERR_INVALID_ARGUMENT
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "lm_head_cross_flce_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle, element by element.
+
+Sizes here let the oracle finish in seconds while spanning several 256-wide
+tiles in every dimension plus ragged tails (N, V not multiples of 256; H not a
+multiple of the 64-wide K stage).  The bar: loss relative error <= 1e-3 (for
+reduction "none" the relative 2-norm over rows), dx/dW/db relative Frobenius
+error <= 1e-2 for bf16 inputs and <= 1e-5 for fp32 inputs; exact zeros where
+the oracle's result is zero.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from lm_head_cross_flce_amd import functional as F
+from lm_head_cross_flce_amd import synth
+from oracle import flce_oracle as O
+
+from flce_gpu_util import GRAD_RTOL, LOSS_RTOL, LSE_RTOL, device_inputs, rel, run, to_f64
+
+pytestmark = pytest.mark.gpu
+
+W_ = synth.WORKLOADS
+
+
+def _case(base, name, **kw):
+    return synth.scaled(W_[base], name, **kw)
+
+
+# Reduced-size versions of the five workloads (same distributions and options).
+CASES = {
+    "tiny_f32": W_["tiny_f32"],
+    "c2_small": _case("n4096_h2048_v32000", "c2_small", N=520, H=256, V=3001),
+    "c3_small": _case("n8192_h4096_v128256", "c3_small", N=600, H=328, V=2083, n_ignored=30),
+    "c4_small": _case("n32768_h2048_v128000", "c4_small", N=1024, H=264, V=4000),
+    "c5_small": _case("n16384_h1024_v256000", "c5_small", N=777, H=128, V=5003),
+    "sum_bias": _case("n8192_h4096_v128256", "sum_bias", N=300, H=200, V=1500, n_ignored=7,
+                      reduction="sum", grad="scalar_normal", seed=7),
+    "f32_none": _case("tiny_f32", "f32_none", N=300, H=136, V=1100, n_ignored=11, label_smoothing=0.1,
+                      z_loss_scale=1e-3, reduction="none", grad="vector_normal", seed=8),
+    "f32_sum_nobias": _case("tiny_f32", "f32_sum_nobias", N=129, H=64, V=777, b_std=None, n_ignored=0,
+                            reduction="sum", grad="scalar_normal", seed=9),
+    "n1_v1": _case("tiny_f32", "n1_v1", N=1, H=8, V=1, n_ignored=0, z_loss_scale=0.01, seed=10),
+    "bf16_v_lt_tile": _case("n8192_h4096_v128256", "bf16_v_lt_tile", N=33, H=72, V=100, n_ignored=3, seed=11),
+}
+
+_oracle_cache = {}
+_input_cache = {}
+
+
+def inputs(name):
+    if name not in _input_cache:
+        _input_cache[name] = synth.make_inputs(CASES[name])
+    return _input_cache[name]
+
+
+def oracle(name, reduction=None):
+    key = (name, reduction)
+    if key not in _oracle_cache:
+        inp = inputs(name)
+        w = inp.w
+        red = reduction or w.reduction
+        g = inp.grad
+        if red != w.reduction:
+            g = np.full(w.N, g[0], dtype=np.float32) if red == "none" else g[:1]
+        x, W, b = inp.as_f64("x"), inp.as_f64("W"), inp.as_f64("b")
+        f = O.forward(x, W, b, inp.targets, w.label_smoothing, w.z_loss_scale, w.ignore_index, red)
+        bw = O.backward(x, W, b, inp.targets, g, w.label_smoothing, w.z_loss_scale, w.ignore_index, red)
+        _oracle_cache[key] = (f, bw)
+    return _oracle_cache[key]
+
+
+def check(name, got, f, bw, need=(True, True, True)):
+    w = CASES[name]
+    tol = GRAD_RTOL[w.dtype]
+    assert got["n_valid"] == f.n_valid
+    assert rel(got["loss"], f.loss) <= LOSS_RTOL, (rel(got["loss"], f.loss), got["loss"][:4], f.loss[:4])
+    assert rel(got["lse"], f.lse) <= LSE_RTOL, rel(got["lse"], f.lse)
+    if need[0]:
+        assert rel(got["dx"], bw.dx) <= tol, ("dx", rel(got["dx"], bw.dx))
+    if need[1]:
+        assert rel(got["dW"], bw.dW) <= tol, ("dW", rel(got["dW"], bw.dW))
+    if need[2] and bw.db is not None:
+        assert rel(got["db"], bw.db) <= tol, ("db", rel(got["db"], bw.db))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity(name):
+    print(f"[gpu] parity case {name}", flush=True)
+    got = run(inputs(name))
+    f, bw = oracle(name)
+    check(name, got, f, bw)
+
+
+@pytest.mark.parametrize("red", ["none", "sum", "mean"])
+def test_parity_all_reductions(red):
+    print(f"[gpu] reductions c3_small {red}", flush=True)
+    got = run(inputs("c3_small"), reduction=red)
+    f, bw = oracle("c3_small", red)
+    check("c3_small", got, f, bw)
+
+
+@pytest.mark.parametrize("cols", ["256", "512"])
+def test_forced_small_slabs(monkeypatch, cols):
+    # Many vocabulary slabs: the fp32 dx accumulator carries across launches.
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", cols)
+    for name in ("c3_small", "c5_small", "f32_none"):
+        print(f"[gpu] forced slabs {cols} {name}", flush=True)
+        got = run(inputs(name))
+        f, bw = oracle(name)
+        check(name, got, f, bw)
+
+
+@pytest.mark.parametrize("need", [(True, False, False), (False, True, False), (False, False, True),
+                                  (True, True, False)])
+def test_partial_gradients(need):
+    print(f"[gpu] partial gradients {need}", flush=True)
+    got = run(inputs("c3_small"), need=need)
+    f, bw = oracle("c3_small")
+    for k, flag in zip(("dx", "dW", "db"), need):
+        assert (got[k] is None) == (not flag)
+    check("c3_small", got, f, bw, need)
+
+
+def test_all_ignored_gives_exact_zeros():
+    w = _case("n8192_h4096_v128256", "all_ignored", N=300, H=64, V=700, n_ignored=300)
+    inp = synth.make_inputs(w)
+    print("[gpu] all ignored", flush=True)
+    got = run(inp)
+    assert got["n_valid"] == 0
+    assert np.all(got["loss"] == 0.0)
+    assert np.all(got["dx"] == 0.0) and np.all(got["dW"] == 0.0) and np.all(got["db"] == 0.0)
+    got = run(inp, reduction="none")
+    assert np.all(got["loss"] == 0.0)
+
+
+def test_ignore_index_inside_vocabulary():
+    w = _case("n8192_h4096_v128256", "ign5", N=260, H=64, V=300, n_ignored=0,
+              ignore_index=5, seed=12)
+    inp = synth.make_inputs(w)
+    inp.targets[::7] = 5
+    _input_cache["ign5"], CASES["ign5"] = inp, w
+    print("[gpu] ignore_index 5", flush=True)
+    got = run(inp)
+    f, bw = oracle("ign5")
+    assert f.n_valid == int(np.sum(inp.targets != 5))
+    check("ign5", got, f, bw)
+
+
+def test_deterministic():
+    inp = inputs("c3_small")
+    dev = device_inputs(inp)
+    print("[gpu] determinism", flush=True)
+    a = run(inp, dev_inputs=dev)
+    b = run(inp, dev_inputs=dev)
+    for k in ("loss", "lse", "dx", "dW", "db"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_autograd_module():
+    inp = inputs("c3_small")
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    x.requires_grad_(True)
+    W.requires_grad_(True)
+    b.requires_grad_(True)
+    mod = F.FusedLinearCrossEntropyLoss(w.ignore_index, w.label_smoothing, w.z_loss_scale, "mean")
+    print("[gpu] autograd module", flush=True)
+    loss = mod(x.view(2, w.N // 2, w.H), t.view(2, -1), W, b)
+    assert loss.shape == ()
+    loss.backward(g.reshape(()))
+    torch.cuda.synchronize()
+    f, bw = oracle("c3_small")
+    assert rel(np.array([loss.item()]), f.loss) <= LOSS_RTOL
+    assert rel(to_f64(x.grad), bw.dx) <= GRAD_RTOL["bf16"]
+    assert rel(to_f64(W.grad), bw.dW) <= GRAD_RTOL["bf16"]
+    assert rel(to_f64(b.grad), bw.db) <= GRAD_RTOL["bf16"]
+
+
+def test_module_frozen_weight_and_none_reduction():
+    inp = inputs("c5_small")
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    x.requires_grad_(True)
+    print("[gpu] frozen weight, none", flush=True)
+    loss = F.fused_linear_cross_entropy_loss(x, t, W, None, w.ignore_index, w.label_smoothing,
+                                             w.z_loss_scale, "none")
+    assert loss.shape == (w.N,)
+    loss.backward(g)
+    torch.cuda.synchronize()
+    f, bw = oracle("c5_small")
+    assert rel(loss.detach().cpu().numpy().astype(np.float64), f.loss) <= LOSS_RTOL
+    assert rel(to_f64(x.grad), bw.dx) <= GRAD_RTOL["bf16"]
+    assert W.grad is None
