@@ -75,6 +75,27 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
+// LDS and buffer-load primitives
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+__device__ __forceinline__ u32x4 lds_load16(const lds_t* p) { return *(const lds_u32x4*)p; }
+__device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
+
+// Buffer loads return zero for an offset past the descriptor's range, which
+// masks out-of-range rows and columns without branches.
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
 // Operands and global -> LDS staging
 // ---------------------------------------------------------------------------
 
@@ -85,29 +106,38 @@ template <class T> struct Opnd {
   int kext;      // valid extent along K
 };
 
-// One stage of one operand: 256 rows x kBK, 8 x 16 bytes per thread.
+// One stage of one operand: 256 rows x kBK, 8 x 16 bytes per thread.  The
+// descriptor is rebased on every stage (scalar arithmetic), so the per-lane
+// byte offsets are fixed for the whole tile and stay small.
 template <class T, bool KCONTIG> struct Stager;
 
 // K-contiguous: thread (kc = tid % 8, rr = tid / 8) loads 16 bytes of K at
 // column chunk kc of rows rr + 32 q.  Requires kext % kVec == 0.
 template <class T> struct Stager<T, true> {
   u32x4 r[8];
-  __device__ __forceinline__ void load(const Opnd<T>& o, int m0, int k0, int tid) {
+  uint32_t off[8];
+  const T* base;
+  int kc_elem;
+  __device__ __forceinline__ void init(const Opnd<T>& o, int m0, int tid) {
     const int kc = tid & 7, rr = tid >> 3;
-    const int gk = k0 + kc * Elem<T>::kVec;
+    kc_elem = kc * Elem<T>::kVec;
+    base = o.p + (int64_t)m0 * o.ld;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int gm = m0 + rr + 32 * q;
-      if (gm < o.mext && gk < o.kext)
-        r[q] = *(const u32x4*)(o.p + (int64_t)gm * o.ld + gk);
-      else
-        r[q] = u32x4{0u, 0u, 0u, 0u};
+      const int row = rr + 32 * q;
+      off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + kc_elem) * sizeof(T)) : kOOB;
     }
   }
-  __device__ __forceinline__ void store(char* buf, int tid) const {
+  __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
+    const bool kok = k0 + kc_elem < o.kext;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r[q] = buf_load16(rs, kok ? off[q] : kOOB);
+  }
+  __device__ __forceinline__ void store(lds_t* buf, int tid) const {
     const int kc = tid & 7, rr = tid >> 3;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) *(u32x4*)(buf + (rr + 32 * q) * kRowBytes + kc * 16) = r[q];
+    for (int q = 0; q < 8; ++q) lds_store16(buf + (rr + 32 * q) * kRowBytes + kc * 16, r[q]);
   }
 };
 
@@ -116,19 +146,25 @@ template <class T> struct Stager<T, true> {
 // transposed 8 x 8 block.  Requires mext % 8 == 0.
 template <> struct Stager<uint16_t, false> {
   u32x4 r[8];
-  __device__ __forceinline__ void load(const Opnd<uint16_t>& o, int m0, int k0, int tid) {
+  uint32_t off[8];
+  const uint16_t* base;
+  int krow;
+  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
     const int kc = tid & 7, mc = tid >> 3;
-    const int gm = m0 + mc * 8;
+    krow = kc * 8;
+    base = o.p + m0;
+    const bool mok = m0 + mc * 8 < o.mext;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int gk = k0 + kc * 8 + e;
-      if (gk < o.kext && gm < o.mext)
-        r[e] = *(const u32x4*)(o.p + (int64_t)gk * o.ld + gm);
-      else
-        r[e] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int e = 0; e < 8; ++e)
+      off[e] = mok ? (uint32_t)(((int64_t)(krow + e) * o.ld + mc * 8) * 2) : kOOB;
   }
-  __device__ __forceinline__ void store(char* buf, int tid) const {
+  __device__ __forceinline__ void load(const Opnd<uint16_t>& o, int k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * o.ld);
+    const int kleft = o.kext - k0 - krow;   // rows e < kleft are valid
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = buf_load16(rs, e < kleft ? off[e] : kOOB);
+  }
+  __device__ __forceinline__ void store(lds_t* buf, int tid) const {
     const int kc = tid & 7, mc = tid >> 3;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -139,8 +175,8 @@ template <> struct Stager<uint16_t, false> {
         ev[w] = (a & 0xffffu) | (b << 16);
         od[w] = (a >> 16) | (b & 0xffff0000u);
       }
-      *(u32x4*)(buf + (mc * 8 + 2 * p) * kRowBytes + kc * 16) = ev;
-      *(u32x4*)(buf + (mc * 8 + 2 * p + 1) * kRowBytes + kc * 16) = od;
+      lds_store16(buf + (mc * 8 + 2 * p) * kRowBytes + kc * 16, ev);
+      lds_store16(buf + (mc * 8 + 2 * p + 1) * kRowBytes + kc * 16, od);
     }
   }
 };
@@ -148,22 +184,29 @@ template <> struct Stager<uint16_t, false> {
 // M-contiguous fp32: 4 x 4 blocks, two per thread (mc = tid / 8 + 32 p).
 template <> struct Stager<float, false> {
   u32x4 r[8];
-  __device__ __forceinline__ void load(const Opnd<float>& o, int m0, int k0, int tid) {
+  uint32_t off[8];
+  const float* base;
+  int krow;
+  __device__ __forceinline__ void init(const Opnd<float>& o, int m0, int tid) {
     const int kc = tid & 7;
+    krow = kc * 4;
+    base = o.p + m0;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int gm = m0 + ((tid >> 3) + 32 * p) * 4;
+      const int mc = (tid >> 3) + 32 * p;
+      const bool mok = m0 + mc * 4 < o.mext;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gk = k0 + kc * 4 + e;
-        if (gk < o.kext && gm < o.mext)
-          r[4 * p + e] = *(const u32x4*)(o.p + (int64_t)gk * o.ld + gm);
-        else
-          r[4 * p + e] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int e = 0; e < 4; ++e)
+        off[4 * p + e] = mok ? (uint32_t)(((int64_t)(krow + e) * o.ld + mc * 4) * 4) : kOOB;
     }
   }
-  __device__ __forceinline__ void store(char* buf, int tid) const {
+  __device__ __forceinline__ void load(const Opnd<float>& o, int k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * o.ld);
+    const int kleft = o.kext - k0 - krow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = buf_load16(rs, (i & 3) < kleft ? off[i] : kOOB);
+  }
+  __device__ __forceinline__ void store(lds_t* buf, int tid) const {
     const int kc = tid & 7;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -171,7 +214,7 @@ template <> struct Stager<float, false> {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         u32x4 t = {r[4 * p][i], r[4 * p + 1][i], r[4 * p + 2][i], r[4 * p + 3][i]};
-        *(u32x4*)(buf + (mc * 4 + i) * kRowBytes + kc * 16) = t;
+        lds_store16(buf + (mc * 4 + i) * kRowBytes + kc * 16, t);
       }
     }
   }
@@ -185,17 +228,18 @@ template <class T> struct Mma;
 
 template <> struct Mma<uint16_t> {
   // 4 sub-steps of K = 16: v_mfma_f32_32x32x16_bf16.
-  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const char* bA, const char* bB,
+  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const lds_t* bA, const lds_t* bB,
                                                int wm, int wn, int lane) {
     const int rl = lane & 31, kh = lane >> 5;
+    const lds_t* pa = bA + (wm * 128 + rl) * kRowBytes + kh * 16;
+    const lds_t* pb = bB + (wn * 128 + rl) * kRowBytes + kh * 16;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 a[4], b[4];
-      const int koff = (s * 16 + 8 * kh) * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(bA + (wm * 128 + 32 * i + rl) * kRowBytes + koff);
+      for (int i = 0; i < 4; ++i) a[i] = lds_load16(pa + 32 * i * kRowBytes + s * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *(const u32x4*)(bB + (wn * 128 + 32 * j + rl) * kRowBytes + koff);
+      for (int j = 0; j < 4; ++j) b[j] = lds_load16(pb + 32 * j * kRowBytes + s * 32);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -209,24 +253,23 @@ template <> struct Mma<uint16_t> {
 template <> struct Mma<float> {
   // 2 sub-steps of K = 16, each 8 x v_mfma_f32_32x32x2_f32.  Lane half kh holds
   // logical k = 16 s + 8 kh + e for register e; instruction e pairs k and k + 8.
-  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const char* bA, const char* bB,
+  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const lds_t* bA, const lds_t* bB,
                                                int wm, int wn, int lane) {
     const int rl = lane & 31, kh = lane >> 5;
+    const lds_t* pa = bA + (wm * 128 + rl) * kRowBytes + kh * 32;
+    const lds_t* pb = bB + (wn * 128 + rl) * kRowBytes + kh * 32;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       f32x4 a[4][2], b[4][2];
-      const int koff = (s * 16 + 8 * kh) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const char* p = bA + (wm * 128 + 32 * i + rl) * kRowBytes + koff;
-        a[i][0] = *(const f32x4*)p;
-        a[i][1] = *(const f32x4*)(p + 16);
+        a[i][0] = __builtin_bit_cast(f32x4, lds_load16(pa + 32 * i * kRowBytes + s * 64));
+        a[i][1] = __builtin_bit_cast(f32x4, lds_load16(pa + 32 * i * kRowBytes + s * 64 + 16));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const char* p = bB + (wn * 128 + 32 * j + rl) * kRowBytes + koff;
-        b[j][0] = *(const f32x4*)p;
-        b[j][1] = *(const f32x4*)(p + 16);
+        b[j][0] = __builtin_bit_cast(f32x4, lds_load16(pb + 32 * j * kRowBytes + s * 64));
+        b[j][1] = __builtin_bit_cast(f32x4, lds_load16(pb + 32 * j * kRowBytes + s * 64 + 16));
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -247,7 +290,7 @@ template <> struct Mma<float> {
 
 template <class T, bool AK, bool BK>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
-                                          const Opnd<T>& B, int n0, int K, char* smem, int tid) {
+                                          const Opnd<T>& B, int n0, int K, lds_t* smem, int tid) {
   constexpr int kBK = Elem<T>::kBK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -255,27 +298,29 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  char* bufA[2] = {smem, smem + kBufBytes};
-  char* bufB[2] = {smem + 2 * kBufBytes, smem + 3 * kBufBytes};
+  lds_t* const bufA = smem;                 // stages at bufA + c * kBufBytes
+  lds_t* const bufB = smem + 2 * kBufBytes;
   Stager<T, AK> sa;
   Stager<T, BK> sb;
+  sa.init(A, m0, tid);
+  sb.init(B, n0, tid);
   const int KT = (K + kBK - 1) / kBK;
-  sa.load(A, m0, 0, tid);
-  sb.load(B, n0, 0, tid);
-  sa.store(bufA[0], tid);
-  sb.store(bufB[0], tid);
+  sa.load(A, 0);
+  sb.load(B, 0);
+  sa.store(bufA, tid);
+  sb.store(bufB, tid);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+    const int cur = (kt & 1) * kBufBytes, nxt = kBufBytes - cur;
     const bool more = kt + 1 < KT;
     if (more) {
-      sa.load(A, m0, (kt + 1) * kBK, tid);
-      sb.load(B, n0, (kt + 1) * kBK, tid);
+      sa.load(A, (kt + 1) * kBK);
+      sb.load(B, (kt + 1) * kBK);
     }
-    Mma<T>::stage(acc, bufA[cur], bufB[cur], wm, wn, lane);
+    Mma<T>::stage(acc, bufA + cur, bufB + cur, wm, wn, lane);
     if (more) {
-      sa.store(bufA[cur ^ 1], tid);
-      sb.store(bufB[cur ^ 1], tid);
+      sa.store(bufA + nxt, tid);
+      sb.store(bufB + nxt, tid);
     }
     __syncthreads();
   }

@@ -33,71 +33,53 @@ namespace flce {
 
 __device__ __forceinline__ int row_off(int i, int e) { return 32 * i + 8 * (e >> 2) + (e & 3); }
 
-// acc[i][j][e] += b[row] for every column; rb = first row of this lane.
+// Bias of the 16 rows a lane holds in row block i (zero past V).
 template <class T>
-__device__ __forceinline__ void add_bias(f32x16 (&acc)[4][4], const T* b, int rb, int V) {
+__device__ __forceinline__ void load_bias16(float (&bv)[16], const T* b, int rb, int i, int V) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r0 = rb + 32 * i + 8 * q;
-      float bv[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bv[s] = (r0 + s < V) ? load_as_f32<T>(b + r0 + s) : 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[i][j][4 * q + s] += bv[s];
-    }
+  for (int e = 0; e < 16; ++e) {
+    const int r = rb + row_off(i, e);
+    bv[e] = (b != nullptr && r < V) ? load_as_f32<T>(b + r) : 0.f;
   }
 }
 
-// Fold column j of the tile into the running (m, d) and sum of logits.
+// Fold one 32 x 32 block (16 values of one column per lane) into the running
+// (m, d) of that column, the running sum of logits, and the target logit.
 template <bool SMOOTH, bool RAGGED>
-__device__ __forceinline__ void lse_col(f32x16 (&acc)[4][4], int j, float& m, float& d, float& sz, int rb,
-                                        int V) {
-  float tmax = -INFINITY, zs = 0.f;
+__device__ __forceinline__ void lse_block(const f32x16& blk, const float (&bv)[16], int i, float& m, float& d,
+                                          float& sz, float& zy, int t, int rb, int V) {
+  float z[16];
+  float bmax = -INFINITY, zs = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float z = acc[i][j][e];
-      if (RAGGED) {
-        const bool ok = rb + row_off(i, e) < V;
-        if (SMOOTH) zs += ok ? z : 0.f;
-        z = ok ? z : -INFINITY;
-        acc[i][j][e] = z;
-      } else if (SMOOTH) {
-        zs += z;
-      }
-      tmax = fmaxf(tmax, z);
+  for (int e = 0; e < 16; ++e) {
+    z[e] = blk[e] + bv[e];
+    if (RAGGED) {
+      const bool ok = rb + row_off(i, e) < V;
+      if (SMOOTH) zs += ok ? z[e] : 0.f;
+      z[e] = ok ? z[e] : -INFINITY;
+    } else if (SMOOTH) {
+      zs += z[e];
     }
-  const float mn = fmaxf(m, tmax);
+    bmax = fmaxf(bmax, z[e]);
+  }
+  const float mn = fmaxf(m, bmax);
   if (!RAGGED || mn != -INFINITY) {
     const float nml = -mn * kLog2e;
     float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ps += fast_exp2(fmaf(acc[i][j][e], kLog2e, nml));
+    for (int e = 0; e < 16; ++e) ps += fast_exp2(fmaf(z[e], kLog2e, nml));
     d = d * fast_exp2((m - mn) * kLog2e) + ps;  // m = -inf: the factor is 0
     m = mn;
   }
   if (SMOOTH) sz += zs;
-}
-
-// If this lane's rows contain target row y, copy the logit.  Wave-uniform
-// branch: most tiles hold no target of any of the wave's columns.
-__device__ __forceinline__ void gather_target(const f32x16 (&acc)[4][4], int j, int y, int rb, float& zy) {
-  const int t = y - rb;
-  const bool own = (t >= 0) && (t < kWaveTile) && ((t & 4) == 0);
+  // Target row: wave-uniform branch, rarely taken.
+  const int tb = t - 32 * i;
+  const bool own = (tb >= 0) && (tb < 32) && ((tb & 4) == 0);
   if (__ballot(own)) {
     float val = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (t == row_off(i, e)) val = acc[i][j][e];
+    for (int e = 0; e < 16; ++e)
+      if (tb == row_off(0, e)) val = z[e];
     if (own) zy = val;
   }
 }
@@ -120,7 +102,8 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 // times all P phases, so each XCD streams W tiles that its neighbours reuse.
 template <class T, bool BIAS, bool SMOOTH>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* const smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int w = blockIdx.x;
   int nt, ph;
@@ -154,18 +137,15 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     const int v0 = vt * kTile;
     gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, smem, tid);
     const int rb = v0 + wm * kWaveTile + 4 * (lane >> 5);
-    if (BIAS) add_bias<T>(acc, (const T*)a.b, rb, a.V);
-    if (v0 + kTile <= a.V) {
+    const bool full = v0 + kTile <= a.V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float bv[16];
+      load_bias16<T>(bv, BIAS ? (const T*)a.b : nullptr, rb, i, a.V);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        gather_target(acc, j, ycol[j], rb, zy[j]);
-        lse_col<SMOOTH, false>(acc, j, m[j], d[j], sz[j], rb, a.V);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        gather_target(acc, j, ycol[j], rb, zy[j]);
-        lse_col<SMOOTH, true>(acc, j, m[j], d[j], sz[j], rb, a.V);
+        if (full) lse_block<SMOOTH, false>(acc[i][j], bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+        else lse_block<SMOOTH, true>(acc[i][j], bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
       }
     }
   }
@@ -180,7 +160,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     zy[j] += y2;
   }
   // Then the two waves that share columns (wm = 0, 1).
-  f32x4* red = (f32x4*)smem;
+  lds_f32x4* red = (lds_f32x4*)smem;
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[wn * kWaveTile + 32 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
@@ -280,54 +260,34 @@ __global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
   a.yv[n] = valid ? (int)t : -1;
 }
 
-// Sum 64 per-lane values over the 32 lanes of each wave half, halving the
-// values held per lane at every step; afterwards lane l holds the totals of
-// values 2 (l % 32) and 2 (l % 32) + 1.
+// Sum 16 per-lane values over the 32 lanes of each wave half, halving the
+// values held per lane at every step (masks 16, 8, 4, 2), then adding the
+// neighbour (mask 1).  Afterwards lanes l and l ^ 1 hold the total of value
+// e = (l % 32) / 2 (bits 1..4 of the lane index).
 template <int HALF>
-__device__ __forceinline__ void xreduce_step(float (&v)[64], int lane) {
-  constexpr int mask = HALF / 2;
+__device__ __forceinline__ void xreduce_step(float (&v)[16], int lane) {
+  constexpr int mask = HALF;   // lane bit that selects the kept half
   const bool up = (lane & mask) != 0;
 #pragma unroll
-  for (int k = 0; k < HALF; ++k) {
-    const float keep = up ? v[HALF + k] : v[k];
-    const float send = up ? v[k] : v[HALF + k];
+  for (int k = 0; k < HALF / 2; ++k) {
+    const float keep = up ? v[HALF / 2 + k] : v[k];
+    const float send = up ? v[k] : v[HALF / 2 + k];
     v[k] = keep + __shfl_xor(send, mask);
   }
 }
 
-template <class T, bool RAGGED>
-__device__ __forceinline__ void dz_tile(f32x16 (&acc)[4][4], const BwdLaunch& a, int n0, int rb, int wn,
-                                        int lane) {
-  const f32x4* coef = (const f32x4*)a.coef;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
-    const f32x4 cf = n < a.N ? coef[n] : f32x4{0.f, 0.f, 0.f, INFINITY};
-    const int y = n < a.N ? a.yv[n] : -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(fmaf(acc[i][j][e], kLog2e, -cf[3]));
-        float dz = fmaf(cf[0], p, -cf[1]);
-        if (RAGGED && rb + row_off(i, e) >= a.V) dz = 0.f;
-        acc[i][j][e] = dz;
-      }
-    const int t = y - rb;
-    const bool own = (t >= 0) && (t < kWaveTile) && ((t & 4) == 0);
-    if (__ballot(own)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (own && t == row_off(i, e)) acc[i][j][e] -= cf[2];
-    }
-  }
+__device__ __forceinline__ float row_sum16(float (&v)[16], int lane) {
+  xreduce_step<16>(v, lane);
+  xreduce_step<8>(v, lane);
+  xreduce_step<4>(v, lane);
+  xreduce_step<2>(v, lane);
+  return v[0] + __shfl_xor(v[0], 1);
 }
 
 template <class T, bool BIAS, bool DB>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* const smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
@@ -339,52 +299,72 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 
   const int g = lane >> 5;
   const int rb = v0 + wm * kWaveTile + 4 * g;
-  if (BIAS) add_bias<T>(acc, (const T*)a.b, rb, a.V);
-  if (v0 + kTile <= a.V) dz_tile<T, false>(acc, a, n0, rb, wn, lane);
-  else dz_tile<T, true>(acc, a, n0, rb, wn, lane);
-
-  T* slab = (T*)a.slab;
+  const bool full = v0 + kTile <= a.V;
+  const f32x4* coef = (const f32x4*)a.coef;
+  f32x4 cf[4];
+  int tcol[4];
+  T* rowp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
-    if (n < a.N) {
-      T* rowp = slab + (int64_t)n * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g;
+    const bool ok = n < a.N;
+    cf[j] = ok ? coef[n] : f32x4{0.f, 0.f, 0.f, INFINITY};
+    tcol[j] = (ok ? a.yv[n] : -1) - rb;
+    rowp[j] = ok ? (T*)a.slab + (int64_t)n * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g : nullptr;
+  }
+  float dbsum[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    float bv[16];
+    load_bias16<T>(bv, BIAS ? (const T*)a.b : nullptr, rb, i, a.V);
+    float rs[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float dz[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(fmaf(acc[i][j][e] + bv[e], kLog2e, -cf[j][3]));
+        dz[e] = fmaf(cf[j][0], p, -cf[j][1]);
+        if (!full && rb + row_off(i, e) >= a.V) dz[e] = 0.f;
+      }
+      const int tb = tcol[j] - 32 * i;
+      const bool own = (tb >= 0) && (tb < 32) && ((tb & 4) == 0);
+      if (__ballot(own)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (own && tb == row_off(0, e)) dz[e] -= cf[j][2];
+      }
+      if (rowp[j] != nullptr) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          store4<T>(rowp + 32 * i + 8 * q, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                    acc[i][j][4 * q + 3]);
+          store4<T>(rowp[j] + 32 * i + 8 * q, dz[4 * q], dz[4 * q + 1], dz[4 * q + 2], dz[4 * q + 3]);
+      }
+      if (DB) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rs[e] += dz[e];
+      }
     }
+    if (DB) dbsum[i] = row_sum16(rs, lane);
   }
 
   if (DB) {
-    float v[64];
+    // Lane l (even) holds the column sums of row e = (l % 32) / 2 of each row
+    // block i; add the two waves that share rows (wn = 0, 1).
+    __attribute__((address_space(3))) float* red = (__attribute__((address_space(3))) float*)smem;
+    const int e = (lane & 31) >> 1;
+    if (wn == 1 && (lane & 1) == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[16 * i + e] = acc[i][0][e] + acc[i][1][e] + acc[i][2][e] + acc[i][3][e];
-    xreduce_step<32>(v, lane);
-    xreduce_step<16>(v, lane);
-    xreduce_step<8>(v, lane);
-    xreduce_step<4>(v, lane);
-    xreduce_step<2>(v, lane);
-    float* red = (float*)smem;  // [wm][128 rows]; operand buffers are free now
-    if (wn == 1) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = 2 * (lane & 31) + k;
-        red[wm * kWaveTile + row_off(e >> 4, e & 15) + 4 * g] = v[k];
-      }
+      for (int i = 0; i < 4; ++i) red[wm * kWaveTile + row_off(i, e) + 4 * g] = dbsum[i];
     }
     __syncthreads();
-    if (wn == 0) {
+    if (wn == 0 && (lane & 1) == 0) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = 2 * (lane & 31) + k;
-        const int rl = row_off(e >> 4, e & 15) + 4 * g;
+      for (int i = 0; i < 4; ++i) {
+        const int rl = row_off(i, e) + 4 * g;
         const int row = v0 + wm * kWaveTile + rl;
-        if (row < a.V) a.dbp[(int64_t)tn * a.V + row] = v[k] + red[wm * kWaveTile + rl];
+        if (row < a.V) a.dbp[(int64_t)tn * a.V + row] = dbsum[i] + red[wm * kWaveTile + rl];
       }
     }
   }
@@ -394,7 +374,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int TN) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* const smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, TN, tm, tn);
@@ -425,7 +406,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int mode) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* const smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
