@@ -34,9 +34,11 @@ flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
 }
 
 // Vocabulary slab width for the backward: enough vocabulary tiles that the dW
-// contraction of one slab (H/256 x slab/256 output tiles) fills every CU,
-// capped so the dlogits slab stays under 1 GiB.  FLCE_DEBUG_SLAB_COLS (a
-// positive multiple of 256) overrides it; the tests use it to force many slabs.
+// contraction of one slab (H/256 x slab/256 output tiles) fills every CU twice,
+// capped so the dlogits slab stays within 1 GiB.  Wider slabs also mean fewer
+// read-modify-write passes over the fp32 dx accumulator.  FLCE_DEBUG_SLAB_COLS
+// (a positive multiple of 256) overrides it; the tests use it to force many
+// slabs.
 int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t vmax = cdiv(V, kTile) * kTile;
@@ -45,7 +47,7 @@ int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
     if (c > 0 && c % kTile == 0) return c < vmax ? c : vmax;
   }
   const int64_t th = cdiv(H, kTile);
-  int64_t want = cdiv(kCUs, th) * kTile;
+  int64_t want = cdiv(2 * kCUs, th) * kTile;
   int64_t cap = (int64_t)(kSlabCapBytes / (size_t)(N * es)) / kTile * kTile;
   if (cap < kTile) cap = kTile;
   int64_t c = want < cap ? want : cap;

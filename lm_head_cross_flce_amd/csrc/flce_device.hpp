@@ -25,6 +25,7 @@ namespace flce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -35,7 +36,6 @@ constexpr int kTile = 256;                  // BM = BN
 constexpr int kWaveTile = 128;
 constexpr int kRowBytes = 144;              // 128 B of K per row + 16 B pad (bank spread)
 constexpr int kBufBytes = kTile * kRowBytes;
-constexpr int kSmemBytes = 4 * kBufBytes;   // {A, B} x 2 stages
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Storage type tags: bf16 values are carried as uint16_t bit patterns.
@@ -83,6 +83,21 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 __device__ __forceinline__ u32x4 lds_load16(const lds_t* p) { return *(const lds_u32x4*)p; }
+
+// The four operand buffers ({A, B} x 2 stages).  Each is its own __shared__
+// object (declared by FLCE_LDS in every kernel) so the compiler can tell that
+// reads of one buffer never overlap a copy into another and need not wait for
+// it.
+struct Lds {
+  lds_t* a[2];
+  lds_t* b[2];
+};
+#define FLCE_LDS(name)                                                   \
+  __shared__ __attribute__((aligned(16))) char name##_a0[kBufBytes];     \
+  __shared__ __attribute__((aligned(16))) char name##_a1[kBufBytes];     \
+  __shared__ __attribute__((aligned(16))) char name##_b0[kBufBytes];     \
+  __shared__ __attribute__((aligned(16))) char name##_b1[kBufBytes];     \
+  const Lds name{{(lds_t*)name##_a0, (lds_t*)name##_a1}, {(lds_t*)name##_b0, (lds_t*)name##_b1}}
 __device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
 
 // Buffer loads return zero for an offset past the descriptor's range, which
@@ -135,9 +150,14 @@ template <class T> struct Stager<T, true> {
     for (int q = 0; q < 8; ++q) r[q] = buf_load16(rs, kok ? off[q] : kOOB);
   }
   __device__ __forceinline__ void store(lds_t* buf, int tid) const {
+    store_half<0>(buf, tid);
+    store_half<1>(buf, tid);
+  }
+  template <int HALF>
+  __device__ __forceinline__ void store_half(lds_t* buf, int tid) const {
     const int kc = tid & 7, rr = tid >> 3;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) lds_store16(buf + (rr + 32 * q) * kRowBytes + kc * 16, r[q]);
+    for (int q = 4 * HALF; q < 4 * HALF + 4; ++q) lds_store16(buf + (rr + 32 * q) * kRowBytes + kc * 16, r[q]);
   }
 };
 
@@ -165,9 +185,14 @@ template <> struct Stager<uint16_t, false> {
     for (int e = 0; e < 8; ++e) r[e] = buf_load16(rs, e < kleft ? off[e] : kOOB);
   }
   __device__ __forceinline__ void store(lds_t* buf, int tid) const {
+    store_half<0>(buf, tid);
+    store_half<1>(buf, tid);
+  }
+  template <int HALF>
+  __device__ __forceinline__ void store_half(lds_t* buf, int tid) const {
     const int kc = tid & 7, mc = tid >> 3;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 2 * HALF; p < 2 * HALF + 2; ++p) {
       u32x4 ev, od;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -284,46 +309,283 @@ template <> struct Mma<float> {
 };
 
 // ---------------------------------------------------------------------------
-// One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.
-// Ends with a workgroup barrier, so LDS may be reused right after it returns.
+// Tile mainloops
 // ---------------------------------------------------------------------------
 
-template <class T, bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
-                                          const Opnd<T>& B, int n0, int K, lds_t* smem, int tid) {
-  constexpr int kBK = Elem<T>::kBK;
+// fp32 operands (correctness-oriented; no fine-grained interleave).
+template <bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<float>& A, int m0,
+                                              const Opnd<float>& B, int n0, int K, const Lds& L, int tid) {
+  constexpr int kBK = Elem<float>::kBK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  lds_t* const bufA = smem;                 // stages at bufA + c * kBufBytes
-  lds_t* const bufB = smem + 2 * kBufBytes;
-  Stager<T, AK> sa;
-  Stager<T, BK> sb;
+  Stager<float, AK> sa;
+  Stager<float, BK> sb;
   sa.init(A, m0, tid);
   sb.init(B, n0, tid);
   const int KT = (K + kBK - 1) / kBK;
   sa.load(A, 0);
   sb.load(B, 0);
-  sa.store(bufA, tid);
-  sb.store(bufB, tid);
+  sa.store(L.a[0], tid);
+  sb.store(L.b[0], tid);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = (kt & 1) * kBufBytes, nxt = kBufBytes - cur;
+    const int cur = kt & 1;
     const bool more = kt + 1 < KT;
     if (more) {
       sa.load(A, (kt + 1) * kBK);
       sb.load(B, (kt + 1) * kBK);
     }
-    Mma<T>::stage(acc, bufA + cur, bufB + cur, wm, wn, lane);
+    Mma<float>::stage(acc, cur ? L.a[1] : L.a[0], cur ? L.b[1] : L.b[0], wm, wn, lane);
     if (more) {
-      sa.store(bufA + nxt, tid);
-      sb.store(bufB + nxt, tid);
+      sa.store(cur ? L.a[0] : L.a[1], tid);
+      sb.store(cur ? L.b[0] : L.b[1], tid);
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 mainloop: operands are copied global -> LDS by the buffer unit
+// (buffer_load ... lds, 16 bytes per lane, each wave instruction filling 1 KB
+// of LDS contiguously), so no registers or LDS-write instructions carry them.
+//
+// K-contiguous operand, one stage = 256 rows x 64 k: LDS rows of 128 bytes;
+// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 1) & 7).  A
+// fragment read (16 lanes = 16 consecutive rows, one logical chunk) then
+// touches every one of the 64 banks once.
+//
+// M-contiguous operand, one stage = 64 k x 256 m in its global layout: LDS
+// rows (one per k) of 512 bytes; chunk p of row k holds logical chunk
+// p ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16, which within
+// each 16-lane group hands lane l element l % 4 of the 8-byte pieces addressed
+// by lanes 4 e + l / 4 (e = 0..3): lane j of a group addresses row
+// k = 8 kh + 4 r + j / 4 at columns m .. m + 3 with m = 16 (group & 1) +
+// 4 (j % 4), so lane l receives column l % 32 at k = 8 kh + 4 r + e, the same
+// K order as a 16-byte read of a K-contiguous row.  The 32 lanes read together
+// cover 4 rows x 4 chunks, again all 64 banks.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
+template <bool KCONTIG> struct Dma;
+
+template <> struct Dma<true> {
+  uint32_t off[8];
+  const uint16_t* base;
+  int wave;
+  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    base = o.p + (int64_t)m0 * o.ld;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 8 * (4 * q + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
+    // Branch-free so that a stage body stays one basic block.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
+    const int kleft = o.kext - k0;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 8 * (4 * q + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      dma16(rs, buf + (4 * q + wave) * 1024, 8 * c < kleft ? off[q] : kOOB);
+    }
+  }
+};
+
+template <> struct Dma<false> {
+  uint32_t off[8];
+  const uint16_t* base;
+  int wave;
+  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    base = o.p + m0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 2 * (4 * q + wave) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      off[q] = (m0 + 8 * c < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * o.ld);
+    const int kleft = o.kext - k0;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 2 * (4 * q + wave) + (lane >> 5);
+      dma16(rs, buf + (4 * q + wave) * 1024, row < kleft ? off[q] : kOOB);
+    }
+  }
+};
+
+// Per-lane LDS addresses of one operand's fragments.
+template <bool KCONTIG> struct FragAddr;
+
+template <> struct FragAddr<true> {
+  int a[4];   // per sub-step s; block i adds 32 * 128 * i
+  __device__ __forceinline__ void init(int wbase, int lane) {
+    const int rl = lane & 31, kh = lane >> 5, f = (rl >> 1) & 7;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = (wbase + rl) * 128 + 16 * ((2 * s + kh) ^ f);
+  }
+  __device__ __forceinline__ u32x4 read(const lds_t* buf, int i, int s) const {
+    return lds_load16(buf + a[s] + 4096 * i);
+  }
+};
+
+template <> struct FragAddr<false> {
+  int a[4];   // per block i; sub-step s and half r add (16 s + 4 r) * 512
+  __device__ __forceinline__ void init(int wbase, int lane) {
+    const int j = lane & 15, kh = lane >> 5, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wbase + 32 * i + 16 * g + 4 * (j & 3);
+      const int c = (m >> 3) ^ (4 * (j >> 2));
+      a[i] = (8 * kh + (j >> 2)) * 512 + 16 * c + 8 * (j & 1);
+    }
+  }
+  __device__ __forceinline__ u32x4 read(const lds_t* buf, int i, int s) const {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const lds_t* p = buf + a[i] + 16 * 512 * s;
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * 512)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+// bf16 fragments of one K = 16 sub-step for this wave: 4 A blocks, 4 B blocks.
+struct FragBF16 {
+  u32x4 a[4], b[4];
+};
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void load_frag(FragBF16& f, const FragAddr<AK>& fa, const FragAddr<BK>& fb,
+                                          const lds_t* bA, const lds_t* bB, int s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = fa.read(bA, i, s);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = fb.read(bB, j, s);
+}
+
+__device__ __forceinline__ void mma_frag(f32x16 (&acc)[4][4], const FragBF16& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
+                                                           __builtin_bit_cast(bf16x8, f.b[j]), acc[i][j], 0, 0, 0);
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
+
+// One stage of the bf16 pipeline, for the stage held in LDS buffer CUR.  The
+// workgroup barrier sits between K sub-steps 2 and 3, so each stage body
+// starts with the previous stage's sub-step 3 MFMAs (registers f1) while
+// this stage's sub-step 0 fragments are read and the next stage is copied into
+// the other buffer:
+//   [mma f1 (previous s3) | read f0 <- s0 | copy next stage -> other buffer]
+//   [mma f0 (s0) | read f1 <- s1]  [mma f1 (s1) | read f0 <- s2]
+//   [mma f0 (s2) | read f1 <- s3]  wait for the copies, barrier
+template <int CUR, bool FIRST, bool AK, bool BK>
+__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, FragBF16& f1,
+                                           const FragAddr<AK>& fa, const FragAddr<BK>& fb, const Lds& L, int tid,
+                                           const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, const Dma<AK>& da,
+                                           const Dma<BK>& db, int k_next) {
+  constexpr int kReads = (AK ? 4 : 8) + (BK ? 4 : 8);   // LDS read instructions per sub-step
+  const lds_t* bA = L.a[CUR];
+  const lds_t* bB = L.b[CUR];
+  load_frag<AK, BK>(f0, fa, fb, bA, bB, 0);
+  if (!FIRST) mma_frag(acc, f1);
+  da.issue(A, k_next, L.a[1 - CUR], tid);
+  db.issue(B, k_next, L.b[1 - CUR], tid);
+  load_frag<AK, BK>(f1, fa, fb, bA, bB, 1);
+  mma_frag(acc, f0);
+  load_frag<AK, BK>(f0, fa, fb, bA, bB, 2);
+  mma_frag(acc, f1);
+  load_frag<AK, BK>(f1, fa, fb, bA, bB, 3);
+  mma_frag(acc, f0);
+  if (FIRST) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgVmem, 16, 0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmem, 2, 0);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  }
+  __syncthreads();
+}
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A, int m0,
+                                               const Opnd<uint16_t>& B, int n0, int K, const Lds& L, int tid) {
+  constexpr int kBK = Elem<uint16_t>::kBK;
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  FragAddr<AK> fa;
+  FragAddr<BK> fb;
+  fa.init(wm * 128, lane);
+  fb.init(wn * 128, lane);
+  Dma<AK> da;
+  Dma<BK> db;
+  da.init(A, m0, tid);
+  db.init(B, n0, tid);
+  const int KT = (K + kBK - 1) / kBK;
+  // Copies past K read zeros (out-of-range offsets), so the stage bodies need
+  // no branches.
+  da.issue(A, 0, L.a[0], tid);
+  db.issue(B, 0, L.b[0], tid);
+  __syncthreads();
+  FragBF16 f0, f1;
+  stage_bf16<0, true, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, kBK);
+  int kt = 1;
+  for (; kt + 1 < KT; kt += 2) {
+    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 1) * kBK);
+    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 2) * kBK);
+  }
+  if (kt < KT) stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 1) * kBK);
+  mma_frag(acc, f1);  // sub-step 3 of the last stage
+}
+
+// One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.
+// Ends with a workgroup barrier, so LDS may be reused right after it returns.
+template <class T, bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
+                                          const Opnd<T>& B, int n0, int K, const Lds& L, int tid) {
+  if constexpr (sizeof(T) == 2) gemm_tile_bf16<AK, BK>(acc, A, m0, B, n0, K, L, tid);
+  else gemm_tile_f32<AK, BK>(acc, A, m0, B, n0, K, L, tid);
 }
 
 // ---------------------------------------------------------------------------

@@ -102,8 +102,7 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 // times all P phases, so each XCD streams W tiles that its neighbours reuse.
 template <class T, bool BIAS, bool SMOOTH>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
-  lds_t* const smem = (lds_t*)smem_raw;
+  FLCE_LDS(L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int w = blockIdx.x;
   int nt, ph;
@@ -135,7 +134,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   f32x16 acc[4][4];
   for (int vt = ph; vt < a.VT; vt += a.P) {
     const int v0 = vt * kTile;
-    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, smem, tid);
+    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
     const int rb = v0 + wm * kWaveTile + 4 * (lane >> 5);
     const bool full = v0 + kTile <= a.V;
 #pragma unroll
@@ -160,7 +159,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     zy[j] += y2;
   }
   // Then the two waves that share columns (wm = 0, 1).
-  lds_f32x4* red = (lds_f32x4*)smem;
+  lds_f32x4* red = (lds_f32x4*)L.a[0];
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[wn * kWaveTile + 32 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
@@ -286,8 +285,7 @@ __device__ __forceinline__ float row_sum16(float (&v)[16], int lane) {
 
 template <class T, bool BIAS, bool DB>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
-  lds_t* const smem = (lds_t*)smem_raw;
+  FLCE_LDS(L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
@@ -295,7 +293,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
   f32x16 acc[4][4];
-  gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, smem, tid);
+  gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
 
   const int g = lane >> 5;
   const int rb = v0 + wm * kWaveTile + 4 * g;
@@ -352,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   if (DB) {
     // Lane l (even) holds the column sums of row e = (l % 32) / 2 of each row
     // block i; add the two waves that share rows (wn = 0, 1).
-    __attribute__((address_space(3))) float* red = (__attribute__((address_space(3))) float*)smem;
+    __attribute__((address_space(3))) float* red = (__attribute__((address_space(3))) float*)L.a[0];
     const int e = (lane & 31) >> 1;
     if (wn == 1 && (lane & 1) == 0) {
 #pragma unroll
@@ -374,8 +372,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int TN) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
-  lds_t* const smem = (lds_t*)smem_raw;
+  FLCE_LDS(L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, TN, tm, tn);
@@ -383,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
   const Opnd<T> A{(const T*)a.x, a.H, a.H, a.N};
   const Opnd<T> B{(const T*)a.slab, a.ldS, wpad, a.N};
   f32x16 acc[4][4];
-  gemm_tile<T, false, false>(acc, A, h0, B, v0, a.N, smem, tid);
+  gemm_tile<T, false, false>(acc, A, h0, B, v0, a.N, L, tid);
   T* dW = (T*)a.dW;
   const int g = lane >> 5;
 #pragma unroll
@@ -406,8 +403,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int mode) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
-  lds_t* const smem = (lds_t*)smem_raw;
+  FLCE_LDS(L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
@@ -415,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   const Opnd<T> A{(const T*)a.W + (int64_t)vs * a.H, a.H, a.H, width};
   const Opnd<T> B{(const T*)a.slab, a.ldS, a.N, wpad};
   f32x16 acc[4][4];
-  gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, smem, tid);
+  gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, L, tid);
   const int g = lane >> 5;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

@@ -74,10 +74,12 @@ def test_workspace_size_arithmetic(lib):
 
 
 def test_slab_width_heuristic(lib):
-    # enough vocabulary tiles that one slab's dW tiles cover 256 CUs
-    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 4096
-    assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 8192
-    assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 16384
+    # enough vocabulary tiles that one slab's dW tiles cover 256 CUs twice,
+    # with the dlogits slab capped at 1 GiB
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
+    assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 16384
+    assert _lib.flce_backward_slab_cols(32768, 2048, 128000, 1) == 16384
+    assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 32768
     assert _lib.flce_backward_slab_cols(64, 128, 1000, 0) == 1024     # capped at V rounded up
     assert _lib.flce_backward_slab_cols(64, 12, 1000, 0) == 0         # H % 8 != 0
 
@@ -86,7 +88,7 @@ def test_slab_debug_override(lib, monkeypatch):
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
     assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 512
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "100")   # not a multiple of 256: ignored
-    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 4096
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
 
 
 def _fwd(lib, **over):
