@@ -1,6 +1,9 @@
 """FLCE forward + backward throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe BYTES          # one plain device copy of BYTES (counter calibration)
+    python bench.py --summarize-trace DIR       # markdown table from a rocprofv3 --kernel-trace run
+    python bench.py --summarize-pmc DIR         # markdown table from a rocprofv3 --pmc run
 
 A step is one pass of the whole hot path over one batch: flce_forward (logits
 GEMM with the online log-sum-exp epilogue, combine, reduction) then
@@ -13,8 +16,12 @@ distributions (random weights; no dataset).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,7 +42,87 @@ def parse():
     p.add_argument("--workload", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0: automatic)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    p.add_argument("--summarize-trace", default=None, metavar="DIR")
+    p.add_argument("--summarize-pmc", default=None, metavar="DIR")
     return p.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; a traffic figure is valid only for this hash."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "lm_head_cross_flce_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    from the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source hash: `([0-9a-f]+)`", text)
+    t = re.search(r"traffic_bytes_per_launch: ([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def _kernel_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    if files:
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                rows.append((r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        return rows
+    import sqlite3
+    for db in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        c = sqlite3.connect(db)
+        rows += [(n, int(e) - int(s)) for n, s, e in c.execute("select name, start, end from kernels")]
+    return rows
+
+
+def summarize_trace(d):
+    rows = _kernel_rows(d)
+    agg = {}
+    for name, dur in rows:
+        key = name.split("(")[0].replace("void ", "")
+        n, t = agg.get(key, (0, 0))
+        agg[key] = (n + 1, t + dur)
+    total = sum(t for _, t in agg.values())
+    print("| kernel | calls | avg us | total ms | share |")
+    print("|---|---:|---:|---:|---:|")
+    for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{k}` | {n} | {t / n / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.1f}% |")
+
+
+def summarize_pmc(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    agg, disp = {}, {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"].split("(")[0].replace("void ", ""), r["Counter_Name"])
+            agg[key] = agg.get(key, 0.0) + float(r["Counter_Value"])
+            disp.setdefault(key[0], set()).add(r["Dispatch_Id"])
+    print("| kernel | counter | per dispatch | dispatches |")
+    print("|---|---|---:|---:|")
+    for (k, c), v in sorted(agg.items()):
+        n = len(disp[k])
+        print(f"| `{k}` | {c} | {v / n:.6g} | {n} |")
+
+
+def copy_probe(nbytes):
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copy_probe_bytes_written": b.numel() * 4}))
 
 
 def cpu_baseline(inp, rows):
@@ -62,6 +149,15 @@ def cpu_baseline(inp, rows):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path would shard "
               "tokens across GPUs with a dW reduce-scatter, which this build does not implement)",
@@ -163,14 +259,15 @@ def main():
         "extra_hbm_mb": extra / 1e6,
         "extra_hbm_frac_of_fp32_logits": extra / (N * V * 4.0),
         "roofline": {"kernel": "fwd_lse_kernel", "bound": "mfma", "achieved": fwd_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": fwd_tflops / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": fwd_tflops / peak,
+                     "traffic": recorded_traffic("fwd_lse_kernel", name),
                      "note": "2NHV flops per launch / average duration of the forward call "
                              "(HIP events on the launch stream; the call adds two O(N) kernels)"},
     }
     if not args.no_cpu_baseline:
         del x, W, b, dx, dW, db, ws_f, ws_b
         torch.cuda.empty_cache()
-        rows = args.cpu_rows or max(8, min(N, int(2.5e11 // (8.0 * H * V))))
+        rows = args.cpu_rows or max(8, min(N, int(1.0e13 // (8.0 * H * V))))
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, rows)
     print(json.dumps(out), flush=True)
