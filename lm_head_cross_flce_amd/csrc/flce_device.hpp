@@ -84,21 +84,34 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 __device__ __forceinline__ u32x4 lds_load16(const lds_t* p) { return *(const lds_u32x4*)p; }
 
-// The four operand buffers ({A, B} x 2 stages).  Each is its own __shared__
-// object (declared by FLCE_LDS in every kernel) so the compiler can tell that
-// reads of one buffer never overlap a copy into another and need not wait for
-// it.
-struct Lds {
-  lds_t* a[2];
-  lds_t* b[2];
-};
-#define FLCE_LDS(name)                                                   \
-  __shared__ __attribute__((aligned(16))) char name##_a0[kBufBytes];     \
-  __shared__ __attribute__((aligned(16))) char name##_a1[kBufBytes];     \
-  __shared__ __attribute__((aligned(16))) char name##_b0[kBufBytes];     \
-  __shared__ __attribute__((aligned(16))) char name##_b1[kBufBytes];     \
-  const Lds name{{(lds_t*)name##_a0, (lds_t*)name##_a1}, {(lds_t*)name##_b0, (lds_t*)name##_b1}}
 __device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
+
+// Operand buffers: bf16 tiles use a ring of four 16 KB stages per operand; fp32
+// tiles use two 36 KB stages per operand (a[0..1], b[0..1]).  Each buffer is its
+// own __shared__ object (declared by FLCE_LDS in every kernel) so the compiler
+// can tell that reads of one buffer never overlap a copy into another and need
+// not wait for it.
+struct Lds {
+  lds_t* a[4];
+  lds_t* b[4];
+};
+template <class T> struct LdsSize {
+  static constexpr int kBig = sizeof(T) == 2 ? 16384 : kBufBytes;  // stages 0, 1
+  static constexpr int kSmall = sizeof(T) == 2 ? 16384 : 16;       // stages 2, 3 (bf16 only)
+};
+#define FLCE_LDS(name, T)                                                                          \
+  __shared__ __attribute__((aligned(16))) char name##_a0[LdsSize<T>::kBig];                        \
+  __shared__ __attribute__((aligned(16))) char name##_a1[LdsSize<T>::kBig];                        \
+  __shared__ __attribute__((aligned(16))) char name##_a2[LdsSize<T>::kSmall];                      \
+  __shared__ __attribute__((aligned(16))) char name##_a3[LdsSize<T>::kSmall];                      \
+  __shared__ __attribute__((aligned(16))) char name##_b0[LdsSize<T>::kBig];                        \
+  __shared__ __attribute__((aligned(16))) char name##_b1[LdsSize<T>::kBig];                        \
+  __shared__ __attribute__((aligned(16))) char name##_b2[LdsSize<T>::kSmall];                      \
+  __shared__ __attribute__((aligned(16))) char name##_b3[LdsSize<T>::kSmall];                      \
+  const Lds name {                                                                                 \
+    {(lds_t*)name##_a0, (lds_t*)name##_a1, (lds_t*)name##_a2, (lds_t*)name##_a3},                  \
+    { (lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3 }                 \
+  }
 
 // Buffer loads return zero for an offset past the descriptor's range, which
 // masks out-of-range rows and columns without branches.
@@ -349,16 +362,18 @@ __device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<fl
 }
 
 // ---------------------------------------------------------------------------
-// bf16 mainloop: operands are copied global -> LDS by the buffer unit
-// (buffer_load ... lds, 16 bytes per lane, each wave instruction filling 1 KB
-// of LDS contiguously), so no registers or LDS-write instructions carry them.
+// bf16 mainloop.  K advances in stages of 32 through a ring of four LDS
+// buffers per operand; each stage is copied three stages ahead by the buffer
+// unit (buffer_load ... lds, 16 bytes per lane, each wave instruction filling
+// 1 KB of LDS contiguously), so no registers or LDS-write instructions carry
+// operands and about three stages of MFMA work cover the copy latency.
 //
-// K-contiguous operand, one stage = 256 rows x 64 k: LDS rows of 128 bytes;
-// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 1) & 7).  A
+// K-contiguous operand, one stage = 256 rows x 32 k: LDS rows of 64 bytes;
+// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 2) & 3).  A
 // fragment read (16 lanes = 16 consecutive rows, one logical chunk) then
-// touches every one of the 64 banks once.
+// touches each of the 64 banks once.
 //
-// M-contiguous operand, one stage = 64 k x 256 m in its global layout: LDS
+// M-contiguous operand, one stage = 32 k x 256 m in its global layout: LDS
 // rows (one per k) of 512 bytes; chunk p of row k holds logical chunk
 // p ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16, which within
 // each 16-lane group hands lane l element l % 4 of the 8-byte pieces addressed
@@ -369,14 +384,23 @@ __device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<fl
 // cover 4 rows x 4 chunks, again all 64 banks.
 // ---------------------------------------------------------------------------
 
+constexpr int kStageK = 32;
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]): wait until at most N vector-memory operations are
+// outstanding and all LDS operations are done.
+template <int N> constexpr int waitcnt_vm_lgkm0() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
+
 template <bool KCONTIG> struct Dma;
 
+// 16 wave instructions per stage (4 per wave): instruction idx fills rows
+// 16 idx .. 16 idx + 15.
 template <> struct Dma<true> {
-  uint32_t off[8];
+  uint32_t off[4];
   const uint16_t* base;
   int wave;
   __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
@@ -384,47 +408,51 @@ template <> struct Dma<true> {
     const int lane = tid & 63;
     base = o.p + (int64_t)m0 * o.ld;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = 8 * (4 * q + wave) + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
+    for (int q = 0; q < 4; ++q) {
+      const int row = 16 * (4 * q + wave) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
       off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
+  // Branch-free so that a stage body stays one basic block.
   __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
-    // Branch-free so that a stage body stays one basic block.
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
     const int kleft = o.kext - k0;
     const int lane = tid & 63;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = 8 * (4 * q + wave) + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
+    for (int q = 0; q < 4; ++q) {
+      const int row = 16 * (4 * q + wave) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
       dma16(rs, buf + (4 * q + wave) * 1024, 8 * c < kleft ? off[q] : kOOB);
     }
   }
 };
 
+// 16 wave instructions per stage (4 per wave): instruction idx fills k rows
+// 2 idx and 2 idx + 1.
 template <> struct Dma<false> {
-  uint32_t off[8];
+  uint32_t off[4];
   const uint16_t* base;
+  int64_t ld;
   int wave;
   __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = o.p + m0;
+    ld = o.ld;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int row = 2 * (4 * q + wave) + (lane >> 5);
       const int c = (lane & 31) ^ (4 * (row & 3));
       off[q] = (m0 + 8 * c < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
   __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * o.ld);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * ld);
     const int kleft = o.kext - k0;
     const int lane = tid & 63;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int row = 2 * (4 * q + wave) + (lane >> 5);
       dma16(rs, buf + (4 * q + wave) * 1024, row < kleft ? off[q] : kOOB);
     }
@@ -435,14 +463,14 @@ template <> struct Dma<false> {
 template <bool KCONTIG> struct FragAddr;
 
 template <> struct FragAddr<true> {
-  int a[4];   // per sub-step s; block i adds 32 * 128 * i
+  int a[2];   // per sub-step s; block i adds 32 * 64 * i
   __device__ __forceinline__ void init(int wbase, int lane) {
-    const int rl = lane & 31, kh = lane >> 5, f = (rl >> 1) & 7;
+    const int rl = lane & 31, kh = lane >> 5, f = (rl >> 2) & 3;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = (wbase + rl) * 128 + 16 * ((2 * s + kh) ^ f);
+    for (int s = 0; s < 2; ++s) a[s] = (wbase + rl) * 64 + 16 * ((2 * s + kh) ^ f);
   }
   __device__ __forceinline__ u32x4 read(const lds_t* buf, int i, int s) const {
-    return lds_load16(buf + a[s] + 4096 * i);
+    return lds_load16(buf + a[s] + 2048 * i);
   }
 };
 
@@ -492,35 +520,30 @@ __device__ __forceinline__ void mma_frag(f32x16 (&acc)[4][4], const FragBF16& f)
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
 
-// One stage of the bf16 pipeline, for the stage held in LDS buffer CUR.  The
-// workgroup barrier sits between K sub-steps 2 and 3, so each stage body
-// starts with the previous stage's sub-step 3 MFMAs (registers f1) while
-// this stage's sub-step 0 fragments are read and the next stage is copied into
-// the other buffer:
-//   [mma f1 (previous s3) | read f0 <- s0 | copy next stage -> other buffer]
-//   [mma f0 (s0) | read f1 <- s1]  [mma f1 (s1) | read f0 <- s2]
-//   [mma f0 (s2) | read f1 <- s3]  wait for the copies, barrier
+// One stage of the bf16 pipeline, for the stage held in ring slot CUR.  The
+// barrier sits between the stage's two K sub-steps' worth of MFMAs, so each
+// body starts with the previous stage's second sub-step (registers f1) while
+// this stage's first fragments are read and the stage three ahead is copied:
+//   [mma f1 (previous s1) | read f0 <- s0 | copy stage + 3 -> slot CUR + 3]
+//   [mma f0 (s0) | read f1 <- s1]   wait for the copy of the next stage, barrier
 template <int CUR, bool FIRST, bool AK, bool BK>
 __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, FragBF16& f1,
                                            const FragAddr<AK>& fa, const FragAddr<BK>& fb, const Lds& L, int tid,
                                            const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, const Dma<AK>& da,
-                                           const Dma<BK>& db, int k_next) {
+                                           const Dma<BK>& db, int k_copy) {
   constexpr int kReads = (AK ? 4 : 8) + (BK ? 4 : 8);   // LDS read instructions per sub-step
+  constexpr int NXT = (CUR + 3) & 3;
   const lds_t* bA = L.a[CUR];
   const lds_t* bB = L.b[CUR];
   load_frag<AK, BK>(f0, fa, fb, bA, bB, 0);
   if (!FIRST) mma_frag(acc, f1);
-  da.issue(A, k_next, L.a[1 - CUR], tid);
-  db.issue(B, k_next, L.b[1 - CUR], tid);
+  da.issue(A, k_copy, L.a[NXT], tid);
+  db.issue(B, k_copy, L.b[NXT], tid);
   load_frag<AK, BK>(f1, fa, fb, bA, bB, 1);
-  mma_frag(acc, f0);
-  load_frag<AK, BK>(f0, fa, fb, bA, bB, 2);
-  mma_frag(acc, f1);
-  load_frag<AK, BK>(f1, fa, fb, bA, bB, 3);
   mma_frag(acc, f0);
   if (FIRST) {
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgVmem, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgVmem, 8, 0);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -530,25 +553,27 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, Fr
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmem, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
     }
   }
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
   }
-  __syncthreads();
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  // Keep the trailing MFMAs ahead of the barrier: they cover the latency of
+  // the last fragment reads, which the barrier waits for.
+  __builtin_amdgcn_sched_barrier(0);
+  // The next stage's copies were issued two bodies ago; 16 newer copy
+  // instructions (the next two stages) may stay in flight.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<16>());
+  __builtin_amdgcn_s_barrier();
 }
 
 template <bool AK, bool BK>
 __device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A, int m0,
                                                const Opnd<uint16_t>& B, int n0, int K, const Lds& L, int tid) {
-  constexpr int kBK = Elem<uint16_t>::kBK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -562,21 +587,30 @@ __device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<u
   Dma<BK> db;
   da.init(A, m0, tid);
   db.init(B, n0, tid);
-  const int KT = (K + kBK - 1) / kBK;
+  const int KT = (K + kStageK - 1) / kStageK;
   // Copies past K read zeros (out-of-range offsets), so the stage bodies need
-  // no branches.
-  da.issue(A, 0, L.a[0], tid);
-  db.issue(B, 0, L.b[0], tid);
-  __syncthreads();
-  FragBF16 f0, f1;
-  stage_bf16<0, true, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, kBK);
-  int kt = 1;
-  for (; kt + 1 < KT; kt += 2) {
-    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 1) * kBK);
-    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 2) * kBK);
+  // no branches; the ones still in flight are drained before returning.
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    da.issue(A, st * kStageK, L.a[st], tid);
+    db.issue(B, st * kStageK, L.b[st], tid);
   }
-  if (kt < KT) stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 1) * kBK);
-  mma_frag(acc, f1);  // sub-step 3 of the last stage
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<16>());
+  __builtin_amdgcn_s_barrier();
+  FragBF16 f0, f1;
+  stage_bf16<0, true, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 3 * kStageK);
+  int kt = 1;
+  for (; kt + 3 < KT; kt += 4) {
+    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
+    stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
+    stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
+    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 6) * kStageK);
+  }
+  if (kt < KT) stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
+  if (kt + 1 < KT) stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
+  if (kt + 2 < KT) stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
+  mma_frag(acc, f1);  // second sub-step of the last stage
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
 }
 
 // One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.

@@ -102,7 +102,7 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 // times all P phases, so each XCD streams W tiles that its neighbours reuse.
 template <class T, bool BIAS, bool SMOOTH>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
-  FLCE_LDS(L);
+  FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int w = blockIdx.x;
   int nt, ph;
@@ -285,7 +285,7 @@ __device__ __forceinline__ float row_sum16(float (&v)[16], int lane) {
 
 template <class T, bool BIAS, bool DB>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
-  FLCE_LDS(L);
+  FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int TN) {
-  FLCE_LDS(L);
+  FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, TN, tm, tn);
@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
 template <class T>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int mode) {
-  FLCE_LDS(L);
+  FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
