@@ -2,16 +2,16 @@
 //
 // Every contraction of the method is computed by one tile routine: a 256 x 256
 // output tile per 256-thread workgroup (4 waves in a 2 x 2 grid, 128 x 128 per
-// wave as 4 x 4 blocks of 32 x 32 MFMA accumulators), K streamed through
-// double-buffered LDS in 128-byte slices (64 bf16 or 32 fp32 per row).
+// wave as 4 x 4 blocks of 32 x 32 MFMA accumulators).
 //
 //   C[m, n] = sum_k A[m, k] * B[n, k]
 //
 // Each operand is read from global memory either "K-contiguous" (element
 // (m, k) at p[m * ld + k]) or "M-contiguous" (element (m, k) at p[k * ld + m]).
-// LDS always holds [row][k] with K contiguous, so the MFMA fragment reads are
-// one or two 16-byte LDS loads per lane; M-contiguous operands are transposed
-// in registers (8 x 8 blocks of bf16, 4 x 4 of fp32) on their way to LDS.
+// bf16 operands are copied global -> LDS by the buffer unit in their global
+// layout (32-wide K stages, a ring of four LDS slots per operand) and read with
+// 16-byte LDS loads (K-contiguous) or transposing 8-byte loads (M-contiguous).
+// fp32 operands go through registers into two padded LDS buffers.
 //
 // MFMA output layout (32 x 32 blocks): accumulator element r of lane l holds
 // row 8 * (r / 4) + 4 * (l / 32) + (r % 4) and column l % 32 of its block, so
@@ -34,7 +34,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kTile = 256;                  // BM = BN
 constexpr int kWaveTile = 128;
-constexpr int kRowBytes = 144;              // 128 B of K per row + 16 B pad (bank spread)
+constexpr int kRowBytes = 144;              // fp32 LDS rows: 128 B of K + 16 B pad (bank spread)
 constexpr int kBufBytes = kTile * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -91,9 +91,12 @@ __device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(lds_u32x4*)p 
 // own __shared__ object (declared by FLCE_LDS in every kernel) so the compiler
 // can tell that reads of one buffer never overlap a copy into another and need
 // not wait for it.
+typedef __attribute__((address_space(3))) float lds_f32;
+
 struct Lds {
   lds_t* a[4];
   lds_t* b[4];
+  lds_f32* bias;   // 256 fp32: the bias of the current tile's rows
 };
 template <class T> struct LdsSize {
   static constexpr int kBig = sizeof(T) == 2 ? 16384 : kBufBytes;  // stages 0, 1
@@ -108,10 +111,19 @@ template <class T> struct LdsSize {
   __shared__ __attribute__((aligned(16))) char name##_b1[LdsSize<T>::kBig];                        \
   __shared__ __attribute__((aligned(16))) char name##_b2[LdsSize<T>::kSmall];                      \
   __shared__ __attribute__((aligned(16))) char name##_b3[LdsSize<T>::kSmall];                      \
+  __shared__ __attribute__((aligned(16))) float name##_bias[kTile];                                \
   const Lds name {                                                                                 \
     {(lds_t*)name##_a0, (lds_t*)name##_a1, (lds_t*)name##_a2, (lds_t*)name##_a3},                  \
-    { (lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3 }                 \
+    {(lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3},                  \
+    (lds_f32*)name##_bias                                                                          \
   }
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its vector-memory copies (which may be the next tile's, still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 // Buffer loads return zero for an offset past the descriptor's range, which
 // masks out-of-range rows and columns without branches.
@@ -121,6 +133,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Bias of the 256 rows r0 .. r0 + 255 of a tile (r0 < V).  fetch() has thread
+// t read row r0 + t through a descriptor that ends at row V, so rows past V
+// read zero with no branch; it is issued before the mainloop and lands in a
+// register.  publish() stores it to LDS after the mainloop (followed by an
+// lds_barrier), and read_bias16() gives a lane the 16 rows it holds in row block i.
+template <class T> struct BiasTile {
+  float v;
+  __device__ __forceinline__ void fetch(const T* b, int64_t V, int64_t r0, int tid) {
+    const int64_t left = V - r0;
+    const int nrec = (int)((left < kTile ? left : kTile) * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(b + r0), (short)0, nrec, 0x00020000);
+    if constexpr (sizeof(T) == 2) {
+      v = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)tid * 2u, 0, 0));
+    } else {
+      v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)tid * 4u, 0, 0));
+    }
+  }
+  __device__ __forceinline__ void publish(lds_f32* dst, int tid) const { dst[tid] = v; }
+};
+
+// bv[e] = bias of row rloc + 32 i + 8 (e / 4) + e % 4 of the tile (rloc a multiple of 4).
+__device__ __forceinline__ void read_bias16(float (&bv)[16], const lds_f32* src, int rloc, int i) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 t = *(const __attribute__((address_space(3))) f32x4*)(src + rloc + 32 * i + 8 * q);
+    bv[4 * q] = t[0];
+    bv[4 * q + 1] = t[1];
+    bv[4 * q + 2] = t[2];
+    bv[4 * q + 3] = t[3];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -571,10 +616,35 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, Fr
   __builtin_amdgcn_s_barrier();
 }
 
+// Copy state of one bf16 tile.  start() issues the copies of the first three
+// stages; it may run while the previous tile's epilogue is still working, as
+// long as every wave has finished that tile's mainloop (whose last barrier
+// follows the last fragment read of every slot).
+template <bool AK, bool BK> struct TileCopy {
+  Dma<AK> da;
+  Dma<BK> db;
+  __device__ __forceinline__ void start(const Opnd<uint16_t>& A, int m0, const Opnd<uint16_t>& B, int n0,
+                                        const Lds& L, int tid) {
+    da.init(A, m0, tid);
+    db.init(B, n0, tid);
+    // Copies past K read zeros (out-of-range offsets), so the stage bodies
+    // need no branches; the ones still in flight are drained at the end.
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      da.issue(A, st * kStageK, L.a[st], tid);
+      db.issue(B, st * kStageK, L.b[st], tid);
+    }
+  }
+};
+
+// Mainloop of a tile whose copies TileCopy::start has issued.
 template <bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A, int m0,
-                                               const Opnd<uint16_t>& B, int n0, int K, const Lds& L, int tid) {
+__device__ __forceinline__ void gemm_tile_bf16_run(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A,
+                                                   const Opnd<uint16_t>& B, int K, const Lds& L, int tid,
+                                                   const TileCopy<AK, BK>& tc) {
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const Dma<AK>& da = tc.da;
+  const Dma<BK>& db = tc.db;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -583,18 +653,7 @@ __device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<u
   FragAddr<BK> fb;
   fa.init(wm * 128, lane);
   fb.init(wn * 128, lane);
-  Dma<AK> da;
-  Dma<BK> db;
-  da.init(A, m0, tid);
-  db.init(B, n0, tid);
   const int KT = (K + kStageK - 1) / kStageK;
-  // Copies past K read zeros (out-of-range offsets), so the stage bodies need
-  // no branches; the ones still in flight are drained before returning.
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    da.issue(A, st * kStageK, L.a[st], tid);
-    db.issue(B, st * kStageK, L.b[st], tid);
-  }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<16>());
   __builtin_amdgcn_s_barrier();
   FragBF16 f0, f1;
@@ -613,8 +672,17 @@ __device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<u
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
 }
 
+template <bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A, int m0,
+                                               const Opnd<uint16_t>& B, int n0, int K, const Lds& L, int tid) {
+  TileCopy<AK, BK> tc;
+  tc.start(A, m0, B, n0, L, tid);
+  gemm_tile_bf16_run<AK, BK>(acc, A, B, K, L, tid, tc);
+}
+
 // One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.
-// Ends with a workgroup barrier, so LDS may be reused right after it returns.
+// Every wave's last LDS read precedes the mainloop's last barrier, so LDS may
+// be reused right after it returns.
 template <class T, bool AK, bool BK>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
                                           const Opnd<T>& B, int n0, int K, const Lds& L, int tid) {

@@ -33,26 +33,35 @@ namespace flce {
 
 __device__ __forceinline__ int row_off(int i, int e) { return 32 * i + 8 * (e >> 2) + (e & 3); }
 
-// Bias of the 16 rows a lane holds in row block i (zero past V).
-template <class T>
-__device__ __forceinline__ void load_bias16(float (&bv)[16], const T* b, int rb, int i, int V) {
+// Copy one 32 x 32 accumulator block to VGPRs where the epilogue needs it.
+// Left to itself the register allocator copies all 256 accumulators at the end
+// of the mainloop, which overflows the VGPRs and spills; volatile reads keep
+// each block's copies in program order.  The caller has let the MFMA pipeline
+// drain (acc_drain) before the first read.
+__device__ __forceinline__ void read_acc16(float (&z)[16], const f32x16& blk) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int r = rb + row_off(i, e);
-    bv[e] = (b != nullptr && r < V) ? load_as_f32<T>(b + r) : 0.f;
-  }
+  for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[e]) : "a"(blk[e]));
 }
 
-// Fold one 32 x 32 block (16 values of one column per lane) into the running
-// (m, d) of that column, the running sum of logits, and the target logit.
+// Wait states between the last MFMA and a read of its accumulators (more than
+// the longest MFMA used here needs).  The scheduling barrier keeps every MFMA
+// of the mainloop ahead of the wait.
+__device__ __forceinline__ void acc_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// Fold one 32 x 32 block (16 values of one column per lane, already in
+// VGPRs) into the running (m, d) of that column, the running sum of logits,
+// and the target logit.
 template <bool SMOOTH, bool RAGGED>
-__device__ __forceinline__ void lse_block(const f32x16& blk, const float (&bv)[16], int i, float& m, float& d,
+__device__ __forceinline__ void lse_block(const float (&acc)[16], const float (&bv)[16], int i, float& m, float& d,
                                           float& sz, float& zy, int t, int rb, int V) {
   float z[16];
   float bmax = -INFINITY, zs = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    z[e] = blk[e] + bv[e];
+    z[e] = acc[e] + bv[e];
     if (RAGGED) {
       const bool ok = rb + row_off(i, e) < V;
       if (SMOOTH) zs += ok ? z[e] : 0.f;
@@ -132,19 +141,46 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   }
 
   f32x16 acc[4][4];
+  const int rloc = wm * kWaveTile + 4 * (lane >> 5);   // first tile row of this lane's row block 0
+  // bf16: the next tile's first stages are copied while this tile's epilogue runs.
+  TileCopy<true, true> tc;
+  if constexpr (sizeof(T) == 2) {
+    if (ph < a.VT) tc.start(A, ph * kTile, B, n0, L, tid);
+  }
   for (int vt = ph; vt < a.VT; vt += a.P) {
     const int v0 = vt * kTile;
-    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
-    const int rb = v0 + wm * kWaveTile + 4 * (lane >> 5);
+    BiasTile<T> bt;
+    if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
+    if constexpr (sizeof(T) == 2) {
+      gemm_tile_bf16_run<true, true>(acc, A, B, a.H, L, tid, tc);
+      if (vt + a.P < a.VT) tc.start(A, v0 + a.P * kTile, B, n0, L, tid);
+    } else {
+      gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
+    }
+    if (BIAS) {
+      bt.publish(L.bias, tid);
+      lds_barrier();
+    }
+    const int rb = v0 + rloc;
     const bool full = v0 + kTile <= a.V;
+    acc_drain();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float bv[16];
-      load_bias16<T>(bv, BIAS ? (const T*)a.b : nullptr, rb, i, a.V);
+      if (BIAS) {
+        read_bias16(bv, L.bias, rloc, i);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bv[e] = 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (full) lse_block<SMOOTH, false>(acc[i][j], bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
-        else lse_block<SMOOTH, true>(acc[i][j], bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+        float z[16];
+        read_acc16(z, acc[i][j]);
+        if (full) lse_block<SMOOTH, false>(z, bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+        else lse_block<SMOOTH, true>(z, bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+        // One block at a time: interleaving blocks buys little and spills.
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -293,10 +329,17 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
   f32x16 acc[4][4];
+  BiasTile<T> bt;
+  if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
   gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
+  if (BIAS) {
+    bt.publish(L.bias, tid);
+    lds_barrier();
+  }
 
   const int g = lane >> 5;
-  const int rb = v0 + wm * kWaveTile + 4 * g;
+  const int rloc = wm * kWaveTile + 4 * g;
+  const int rb = v0 + rloc;
   const bool full = v0 + kTile <= a.V;
   const f32x4* coef = (const f32x4*)a.coef;
   f32x4 cf[4];
@@ -314,7 +357,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float bv[16];
-    load_bias16<T>(bv, BIAS ? (const T*)a.b : nullptr, rb, i, a.V);
+    if (BIAS) {
+      read_bias16(bv, L.bias, rloc, i);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bv[e] = 0.f;
+    }
     float rs[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) rs[e] = 0.f;
