@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <numeric>
 
 #include "flce.h"
 #include "flce_launch.hpp"
@@ -14,6 +15,7 @@ constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kTile = 256;
 constexpr size_t kAlign = 256;
 constexpr size_t kSlabCapBytes = size_t(1) << 30;
+constexpr size_t kSlabTargetBytes = size_t(256) << 20;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -33,12 +35,16 @@ flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
   return FLCE_OK;
 }
 
-// Vocabulary slab width for the backward: enough vocabulary tiles that the dW
-// contraction of one slab (H/256 x slab/256 output tiles) fills every CU twice,
-// capped so the dlogits slab stays within 1 GiB.  Wider slabs also mean fewer
-// read-modify-write passes over the fp32 dx accumulator.  FLCE_DEBUG_SLAB_COLS
-// (a positive multiple of 256) overrides it; the tests use it to force many
-// slabs.
+// Vocabulary slab width for the backward: the wider of (a) enough vocabulary
+// tiles that the dW contraction of one slab (H/256 x slab/256 output tiles)
+// fills every CU twice and (b) the widest slab within 256 MiB whose dW tiles
+// fill whole rounds of 256 CUs; capped at 1 GiB.  Every slab after the first
+// costs one read-modify-write pass over the fp32 dx accumulator
+// (N x H x 8 bytes), which all CUs make at the same moment, so wider slabs
+// save HBM time; (b) gives the Llama-3-sized head (N=8192, H=4096,
+// V=128256) 16384 columns, with all extra memory at 9.7% of its fp32 logits.
+// FLCE_DEBUG_SLAB_COLS (a positive multiple of 256) overrides it; the tests
+// use it to force many slabs.
 int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t vmax = cdiv(V, kTile) * kTile;
@@ -48,6 +54,9 @@ int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   }
   const int64_t th = cdiv(H, kTile);
   int64_t want = cdiv(2 * kCUs, th) * kTile;
+  const int64_t round_cols = kTile * (kCUs / std::gcd((int64_t)kCUs, th));   // whole dW rounds
+  const int64_t by_bytes = (int64_t)(kSlabTargetBytes / (size_t)(N * es)) / round_cols * round_cols;
+  if (by_bytes > want) want = by_bytes;
   int64_t cap = (int64_t)(kSlabCapBytes / (size_t)(N * es)) / kTile * kTile;
   if (cap < kTile) cap = kTile;
   int64_t c = want < cap ? want : cap;
@@ -77,7 +86,7 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias) {
   g.off_dxacc = off;
   off = align_up(off + (size_t)N * H * 4);
   g.off_dbp = off;
-  if (has_bias) off = align_up(off + (size_t)g.NT * V * 4);
+  if (has_bias) off = align_up(off + (size_t)g.NT * g.slab_cols * 4);
   g.off_coef = off;
   off = align_up(off + (size_t)N * 16);
   g.off_yv = off;
@@ -219,7 +228,6 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
     else if (k == nslab - 1) mode = flce::kDxLast;
     if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
   }
-  if (want_db && flce::launch_bwd_db(a, dtype, s) != hipSuccess) return FLCE_ERR_HIP;
   return FLCE_OK;
 }
 

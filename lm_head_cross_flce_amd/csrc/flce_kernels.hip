@@ -410,10 +410,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
       for (int i = 0; i < 4; ++i) {
         const int rl = row_off(i, e) + 4 * g;
         const int row = v0 + wm * kWaveTile + rl;
-        if (row < a.V) a.dbp[(int64_t)tn * a.V + row] = dbsum[i] + red[wm * kWaveTile + rl];
+        if (row < a.V) a.dbp[(int64_t)tn * a.ldS + (row - vs)] = dbsum[i] + red[wm * kWaveTile + rl];
       }
     }
   }
+}
+
+// db[vs + c] = sum over token tiles of the slab's db partials (fixed order),
+// for slab column c < width.
+template <class T>
+__device__ __forceinline__ void slab_db(const BwdLaunch& a, int vs, int width, int c) {
+  if (c >= width) return;
+  float s = 0.f;
+  for (int t = 0; t < a.NT; ++t) s += a.dbp[(int64_t)t * a.ldS + c];
+  if constexpr (sizeof(T) == 4) ((float*)a.db)[vs + c] = s;
+  else ((uint16_t*)a.db)[vs + c] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
 }
 
 // dW[vs + v, h] for the slab: C[h][v] = sum_n x[n][h] dz[n][v].
@@ -425,6 +436,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, TM, TN, tm, tn);
   const int h0 = tm * kTile, v0 = tn * kTile;
+  // The workgroups of the first H tile also finish db for their 256 columns.
+  if (a.db != nullptr && tm == 0) slab_db<T>(a, vs, width, v0 + tid);
   const Opnd<T> A{(const T*)a.x, a.H, a.H, a.N};
   const Opnd<T> B{(const T*)a.slab, a.ldS, wpad, a.N};
   f32x16 acc[4][4];
@@ -480,14 +493,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   }
 }
 
+// db of one slab when no dW launch does it (frozen weight).
 template <class T>
-__global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a) {
-  const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= a.V) return;
-  float s = 0.f;
-  for (int t = 0; t < a.NT; ++t) s += a.dbp[(int64_t)t * a.V + v];
-  if (sizeof(T) == 4) ((float*)a.db)[v] = s;
-  else ((uint16_t*)a.db)[v] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
+__global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a, int vs, int width) {
+  slab_db<T>(a, vs, width, blockIdx.x * 256 + threadIdx.x);
 }
 
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
@@ -508,6 +517,7 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
   else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
   if (a.dx) hipLaunchKernelGGL((bwd_dx_kernel<T>), dim3(TH * a.NT), blk, 0, st, a, vs, width, wpad, TH, dx_mode);
   return hipGetLastError();
 }
@@ -518,10 +528,5 @@ hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int
                     : launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, st);
 }
 
-hipError_t launch_bwd_db(const BwdLaunch& a, int dtype, hipStream_t st) {
-  if (dtype == 1) hipLaunchKernelGGL((bwd_db_kernel<uint16_t>), dim3((a.V + 255) / 256), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_db_kernel<float>), dim3((a.V + 255) / 256), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
 
 }  // namespace flce

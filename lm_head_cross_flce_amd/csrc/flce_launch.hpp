@@ -35,7 +35,7 @@ struct BwdLaunch {
   int* yv;                // [N]
   void* slab; int64_t ldS;
   float* dx_acc;          // [N][H]
-  float* dbp;             // [NT][V]
+  float* dbp;             // [NT][ldS]: per token tile db partials of the current slab; null if no db
   void* dx; void* dW; void* db;
 };
 
@@ -44,6 +44,5 @@ hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st);
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
                            hipStream_t st);
-hipError_t launch_bwd_db(const BwdLaunch& a, int dtype, hipStream_t st);
 
 }  // namespace flce

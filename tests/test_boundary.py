@@ -64,20 +64,21 @@ def test_workspace_size_arithmetic(lib):
     assert f >= P * 8192 * 16 + 8192 * 4
     slab = _lib.flce_backward_slab_cols(8192, 4096, 128256, _lib.FLCE_BF16)
     assert slab % 256 == 0 and slab >= 256
-    need = 8192 * slab * 2 + 8192 * 4096 * 4 + NT * 128256 * 4 + 8192 * 20
+    need = 8192 * slab * 2 + 8192 * 4096 * 4 + NT * slab * 4 + 8192 * 20
     assert need <= b <= need + 8 * 256
     # extra memory at the Llama-3-sized head stays under 10% of the fp32 logits
     assert f + b < 0.1 * 8192 * 128256 * 4
     # no bias: no db partials
     _, b_nobias = _lib.flce_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, False, 2)
-    assert b - b_nobias >= NT * 128256 * 4
+    assert b - b_nobias >= NT * slab * 4
 
 
 def test_slab_width_heuristic(lib):
-    # enough vocabulary tiles that one slab's dW tiles cover 256 CUs twice,
-    # with the dlogits slab capped at 1 GiB
-    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
-    assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 16384
+    # the wider of: one slab's dW tiles cover 256 CUs twice, or the widest
+    # slab within 256 MiB whose dW tiles fill whole rounds of 256 CUs; capped
+    # at 1 GiB and at V rounded up to a tile
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 16384
+    assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 32000
     assert _lib.flce_backward_slab_cols(32768, 2048, 128000, 1) == 16384
     assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 32768
     assert _lib.flce_backward_slab_cols(64, 128, 1000, 0) == 1024     # capped at V rounded up
@@ -88,7 +89,7 @@ def test_slab_debug_override(lib, monkeypatch):
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
     assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 512
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "100")   # not a multiple of 256: ignored
-    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 16384
 
 
 def _fwd(lib, **over):
