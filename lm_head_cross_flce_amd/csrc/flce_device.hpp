@@ -32,6 +32,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kPersistGrid = 256;              // one workgroup per CU (MI355X: 256 CUs)
 constexpr int kTile = 256;                  // BM = BN
 constexpr int kWaveTile = 128;
 constexpr int kRowBytes = 144;              // fp32 LDS rows: 128 B of K + 16 B pad (bank spread)
@@ -571,7 +572,7 @@ constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
 // this stage's first fragments are read and the stage three ahead is copied:
 //   [mma f1 (previous s1) | read f0 <- s0 | copy stage + 3 -> slot CUR + 3]
 //   [mma f0 (s0) | read f1 <- s1]   wait for the copy of the next stage, barrier
-template <int CUR, bool FIRST, bool AK, bool BK>
+template <int CUR, bool FIRST, bool AK, bool BK, int VMW = 16>
 __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, FragBF16& f1,
                                            const FragAddr<AK>& fa, const FragAddr<BK>& fb, const Lds& L, int tid,
                                            const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, const Dma<AK>& da,
@@ -610,9 +611,10 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, Fr
   // Keep the trailing MFMAs ahead of the barrier: they cover the latency of
   // the last fragment reads, which the barrier waits for.
   __builtin_amdgcn_sched_barrier(0);
-  // The next stage's copies were issued two bodies ago; 16 newer copy
-  // instructions (the next two stages) may stay in flight.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<16>());
+  // The next stage's copies were issued two bodies ago; the 16 newer copy
+  // instructions (the next two stages) may stay in flight, and VMW - 16 more
+  // where the caller issued other memory operations in between.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VMW>());
   __builtin_amdgcn_s_barrier();
 }
 
@@ -637,11 +639,19 @@ template <bool AK, bool BK> struct TileCopy {
   }
 };
 
-// Mainloop of a tile whose copies TileCopy::start has issued.
-template <bool AK, bool BK>
+// Mainloop of a tile whose copies TileCopy::start has issued.  EXTRA is a
+// lower bound on the vector-memory instructions each wave issued after
+// start() and before this call (an epilogue's stores and loads): vmcnt counts
+// stores too, in issue order, so the waits for stages 0-2, whose copies are
+// older than those instructions, allow EXTRA more to stay in flight instead
+// of draining the epilogue's stores.  Counting too few only costs a stall;
+// every counted instruction must be issued unconditionally by every wave.
+template <bool AK, bool BK, int EXTRA = 0>
 __device__ __forceinline__ void gemm_tile_bf16_run(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A,
                                                    const Opnd<uint16_t>& B, int K, const Lds& L, int tid,
                                                    const TileCopy<AK, BK>& tc) {
+  static_assert(EXTRA >= 0 && 16 + EXTRA <= 63, "vmcnt holds at most 63");
+  constexpr int W0 = 16 + EXTRA;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Dma<AK>& da = tc.da;
   const Dma<BK>& db = tc.db;
@@ -654,20 +664,23 @@ __device__ __forceinline__ void gemm_tile_bf16_run(f32x16 (&acc)[4][4], const Op
   fa.init(wm * 128, lane);
   fb.init(wn * 128, lane);
   const int KT = (K + kStageK - 1) / kStageK;
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<16>());
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<W0>());
   __builtin_amdgcn_s_barrier();
   FragBF16 f0, f1;
-  stage_bf16<0, true, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 3 * kStageK);
-  int kt = 1;
+  // Stages 0 and 1 end by waiting for the copies of stages 1 and 2, which
+  // start() issued; from stage 2 on, the waited-for copies are the body's own.
+  stage_bf16<0, true, AK, BK, W0>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 3 * kStageK);
+  if (KT > 1) stage_bf16<1, false, AK, BK, W0>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 4 * kStageK);
+  int kt = 2;
   for (; kt + 3 < KT; kt += 4) {
-    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
-    stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
-    stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
-    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 6) * kStageK);
+    stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
+    stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
+    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
+    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 6) * kStageK);
   }
-  if (kt < KT) stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
-  if (kt + 1 < KT) stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
-  if (kt + 2 < KT) stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
+  if (kt < KT) stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
+  if (kt + 1 < KT) stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
+  if (kt + 2 < KT) stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
   mma_frag(acc, f1);  // second sub-step of the last stage
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
 }

@@ -319,40 +319,88 @@ __device__ __forceinline__ float row_sum16(float (&v)[16], int lane) {
   return v[0] + __shfl_xor(v[0], 1);
 }
 
-template <class T, bool BIAS, bool DB>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
-  FLCE_LDS(L, T);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
-  const int v0 = vs + tm * kTile, n0 = tn * kTile;
+// Store one 32 x 32 block of dlogits (a lane's column n = lane % 32 and rows
+// 8 q + 4 (lane / 32) + r) into the slab, whose rows are tokens with the
+// vocabulary contiguous.  Written directly, every lane would store 8 bytes
+// into a different token row; instead the block goes through a 2 KB LDS
+// buffer of this wave ([token][64 bytes], 16-byte chunk c of row n at
+// c ^ (n & 3)) and comes back as 16 contiguous bytes per lane, four lanes
+// per 64-byte row segment.  Rows nrow + row at or past nlimit are not
+// stored.  Two buffer stores per block, issued by every lane whatever the
+// rows.  The buffer is private to the wave, whose LDS operations complete in
+// order, so no barrier is needed.
+__device__ __forceinline__ void store_block_bf16(lds_t* sb, const float (&dz)[16], __amdgpu_buffer_rsrc_t rslab,
+                                                 int64_t ldS, int nrow, int nlimit, int vcol, int lane) {
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(lds_u32x2*)(sb + n * 64 + 16 * (q ^ (n & 3)) + 8 * g) =
+        u32x2{pack_bf16x2(dz[4 * q], dz[4 * q + 1]), pack_bf16x2(dz[4 * q + 2], dz[4 * q + 3])};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row = 16 * k + (lane >> 2), c = lane & 3;
+    const u32x4 v = lds_load16(sb + row * 64 + 16 * (c ^ (row & 3)));
+    const uint32_t off = nrow + row < nlimit ? (uint32_t)(((int64_t)(nrow + row) * ldS + vcol + 8 * c) * 2) : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rslab, off, 0, 0);
+  }
+}
+
+// One tile of the recompute kernel.  EXTRA: the vector-memory instructions
+// every wave has issued since this tile's copies started (see
+// gemm_tile_bf16_run).
+template <class T, bool BIAS, bool DB, int EXTRA>
+__device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
+                                        const Lds& L, lds_f32* red, lds_t* stage, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
-  f32x16 acc[4][4];
-  BiasTile<T> bt;
-  if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
-  gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
-  if (BIAS) {
-    bt.publish(L.bias, tid);
-    lds_barrier();
-  }
-
   const int g = lane >> 5;
   const int rloc = wm * kWaveTile + 4 * g;
+  const f32x4* coef = (const f32x4*)a.coef;
+  int tm, tn;
+  tile_coords(t, G, TM, a.NT, tm, tn);
+  const int v0 = vs + tm * kTile, n0 = tn * kTile;
   const int rb = v0 + rloc;
   const bool full = v0 + kTile <= a.V;
-  const f32x4* coef = (const f32x4*)a.coef;
+  // Per-token coefficients and targets are fetched before the mainloop,
+  // through descriptors that start at token n0 (rows past N read zero).
+  const __amdgpu_buffer_rsrc_t rcoef = make_rsrc(coef + n0);
+  const __amdgpu_buffer_rsrc_t ryv = make_rsrc(a.yv + n0);
   f32x4 cf[4];
   int tcol[4];
   T* rowp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
-    const bool ok = n < a.N;
-    cf[j] = ok ? coef[n] : f32x4{0.f, 0.f, 0.f, INFINITY};
-    tcol[j] = (ok ? a.yv[n] : -1) - rb;
-    rowp[j] = ok ? (T*)a.slab + (int64_t)n * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g : nullptr;
+    const int nl = wn * kWaveTile + 32 * j + (lane & 31);
+    const bool ok = n0 + nl < a.N;
+    const f32x4 c = __builtin_bit_cast(f32x4, buf_load16(rcoef, ok ? (uint32_t)nl * 16u : kOOB));
+    const int y = (int)__builtin_amdgcn_raw_buffer_load_b32(ryv, ok ? (uint32_t)nl * 4u : kOOB, 0, 0);
+    cf[j] = ok ? c : f32x4{0.f, 0.f, 0.f, INFINITY};
+    tcol[j] = (ok ? y : -1) - rb;
+    rowp[j] = ok ? (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g : nullptr;
   }
+  f32x16 acc[4][4];
+  BiasTile<T> bt;
+  if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
+  if constexpr (sizeof(T) == 2) {
+    gemm_tile_bf16_run<true, true, EXTRA>(acc, A, B, a.H, L, tid, tc);
+    const int tnext = t + gridDim.x;
+    if (tnext < G) {
+      int tm2, tn2;
+      tile_coords(tnext, G, TM, a.NT, tm2, tn2);
+      tc.start(A, vs + tm2 * kTile, B, tn2 * kTile, L, tid);
+    }
+  } else {
+    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
+  }
+  if (BIAS) {
+    bt.publish(L.bias, tid);
+    lds_barrier();
+  }
+  acc_drain();
+  // Slab rows of this tile's tokens, from token n0 on.
+  const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
   float dbsum[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -368,10 +416,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
     for (int e = 0; e < 16; ++e) rs[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      float z[16];
+      read_acc16(z, acc[i][j]);
       float dz[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(fmaf(acc[i][j][e] + bv[e], kLog2e, -cf[j][3]));
+        const float p = fast_exp2(fmaf(z[e] + bv[e], kLog2e, -cf[j][3]));
         dz[e] = fmaf(cf[j][0], p, -cf[j][1]);
         if (!full && rb + row_off(i, e) >= a.V) dz[e] = 0.f;
       }
@@ -382,7 +432,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
         for (int e = 0; e < 16; ++e)
           if (own && tb == row_off(0, e)) dz[e] -= cf[j][2];
       }
-      if (rowp[j] != nullptr) {
+      if constexpr (sizeof(T) == 2) {
+        store_block_bf16(stage, dz, rslab, a.ldS, wn * kWaveTile + 32 * j, a.N - n0,
+                         (v0 - vs) + wm * kWaveTile + 32 * i, lane);
+      } else if (rowp[j] != nullptr) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           store4<T>(rowp[j] + 32 * i + 8 * q, dz[4 * q], dz[4 * q + 1], dz[4 * q + 2], dz[4 * q + 3]);
@@ -391,20 +444,22 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
 #pragma unroll
         for (int e = 0; e < 16; ++e) rs[e] += dz[e];
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (DB) dbsum[i] = row_sum16(rs, lane);
   }
 
   if (DB) {
     // Lane l (even) holds the column sums of row e = (l % 32) / 2 of each row
-    // block i; add the two waves that share rows (wn = 0, 1).
-    __attribute__((address_space(3))) float* red = (__attribute__((address_space(3))) float*)L.a[0];
+    // block i; add the two waves that share rows (wn = 0, 1).  The next
+    // tile's mainloop barriers keep this tile's reads of red ahead of the
+    // next tile's writes.
     const int e = (lane & 31) >> 1;
     if (wn == 1 && (lane & 1) == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wm * kWaveTile + row_off(i, e) + 4 * g] = dbsum[i];
     }
-    __syncthreads();
+    lds_barrier();
     if (wn == 0 && (lane & 1) == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -414,6 +469,40 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
       }
     }
   }
+}
+
+// Persistent over the slab's tiles (TM vocabulary tiles x NT token tiles): a
+// workgroup takes logical tiles blockIdx.x, + gridDim.x, ..., so the tiles in
+// flight together are the ones a one-tile-per-workgroup launch would run
+// together (same XCD mapping), and each tile's first copies are issued while
+// the previous tile's epilogue runs.  The first tile is peeled: only later
+// tiles start with the previous tile's slab stores still in flight.
+template <class T, bool BIAS, bool DB>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
+  FLCE_LDS(L, T);
+  __shared__ __attribute__((aligned(16))) float red_s[kTile];   // db: the two waves sharing rows
+  __shared__ __attribute__((aligned(16))) char stage_s[4][2048];  // bf16 store staging, one 32 x 32 block per wave
+  lds_f32* red = (lds_f32*)red_s;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  lds_t* stage = (lds_t*)stage_s[wave];
+  const int G = TM * a.NT;
+  TileCopy<true, true> tc;
+  int t = blockIdx.x;
+  if constexpr (sizeof(T) == 2) {
+    const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
+    const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
+    int tm, tn;
+    tile_coords(t, G, TM, a.NT, tm, tn);
+    tc.start(A, vs + tm * kTile, B, tn * kTile, L, tid);
+  }
+  // Vector-memory instructions every wave issues between starting a tile's
+  // copies and its mainloop: the per-token loads (8) and the bias fetch, plus,
+  // after the first tile, the previous tile's slab stores (32).
+  constexpr int kLoadsVm = 8 + (BIAS ? 1 : 0);
+  constexpr int kStoresVm = 32;
+  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, stage, tid);
+  for (t += gridDim.x; t < G; t += gridDim.x)
+    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, stage, tid);
 }
 
 // db[vs + c] = sum over token tiles of the slab's db partials (fixed order),
@@ -460,10 +549,24 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
   }
 }
 
-// dx[n, h] += sum_{v in slab} dz[n][v] W[vs + v][h]: C[h][n].
+// dx[n, h] += sum_{v in slab} dz[n][v] W[vs + v][h]: C[h][n].  MODE says
+// whether the fp32 accumulator is written (first slab), read and written
+// (middle slabs), read with dx written in its dtype (last slab), or skipped
+// (a single slab).  The epilogue is branch-free (buffer accesses with
+// out-of-range offsets for rows past N or columns past H) and reads each
+// accumulator block one block ahead of adding and storing it, so the
+// read-modify-write does not wait once per 16 bytes.
 template <class T>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
-                                                             int mode) {
+__device__ __forceinline__ void store4_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, r, off, 0, 0);
+  }
+}
+
+template <class T, int MODE>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   int tm, tn;
@@ -473,23 +576,53 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   const Opnd<T> B{(const T*)a.slab, a.ldS, a.N, wpad};
   f32x16 acc[4][4];
   gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, L, tid);
+
+  constexpr bool kRead = MODE == kDxAccum || MODE == kDxLast;
+  constexpr bool kAcc = MODE == kDxFirst || MODE == kDxAccum;   // write the fp32 accumulator
+  // Descriptors start at token row n0, so offsets stay below 256 * H * 4 bytes.
+  const __amdgpu_buffer_rsrc_t racc = make_rsrc(a.dx_acc + (int64_t)n0 * a.H);
+  const __amdgpu_buffer_rsrc_t rdx = make_rsrc((const T*)a.dx + (int64_t)n0 * a.H);
   const int g = lane >> 5;
+  // Byte offset of block (i, j), group q (row n = n0 + nl, column h) for
+  // elements of es bytes; kOOB past N or H.
+  auto boff = [&](int i, int j, int q, uint32_t es) -> uint32_t {
+    const int nl = wn * kWaveTile + 32 * j + (lane & 31);
+    const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
+    return (n0 + nl < a.N && h < a.H) ? (uint32_t)(nl * a.H + h) * es : kOOB;
+  };
+  acc_drain();
+  // Loads run kAhead blocks ahead (12 x 1 KB in flight per wave), about what
+  // one CU's share of HBM bandwidth needs while every CU makes its
+  // read-modify-write at the same moment.
+  constexpr int kAhead = 3;
+  f32x4 old[kAhead + 1][4];
+  if (kRead) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
-    if (n >= a.N) continue;
+    for (int b = 0; b < kAhead; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 4; ++q) old[b][q] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b & 3, b >> 2, q, 4u)));
+  }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
-        if (h >= a.H) continue;
-        f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        f32x4* pa = (f32x4*)(a.dx_acc + (int64_t)n * a.H + h);
-        if (mode == kDxAccum || mode == kDxLast) v += *pa;
-        if (mode == kDxFirst || mode == kDxAccum) *pa = v;
-        else store4<T>((T*)a.dx + (int64_t)n * a.H + h, v[0], v[1], v[2], v[3]);
+  for (int b = 0; b < 16; ++b) {
+    const int i = b & 3, j = b >> 2;
+    const int bn = b + kAhead;
+    if (kRead && bn < 16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        old[bn % (kAhead + 1)][q] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn & 3, bn >> 2, q, 4u)));
+    }
+    float z[16];
+    read_acc16(z, acc[i][j]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v = {z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+      if (kRead) v += old[b % (kAhead + 1)][q];
+      if (kAcc) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(i, j, q, 4u), 0, 0);
+      } else {
+        store4_buf<T>(rdx, boff(i, j, q, (uint32_t)sizeof(T)), v);
       }
+    }
   }
 }
 
@@ -512,13 +645,19 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   const int TH = (a.H + kTile - 1) / kTile;
   const bool bias = a.b != nullptr;
   const dim3 blk(kThreads);
-  const dim3 gdz(TV * a.NT);
+  const dim3 gdz(TV * a.NT < kPersistGrid ? TV * a.NT : kPersistGrid);
   if (bias && want_db) hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
   else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
   else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
   else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
-  if (a.dx) hipLaunchKernelGGL((bwd_dx_kernel<T>), dim3(TH * a.NT), blk, 0, st, a, vs, width, wpad, TH, dx_mode);
+  if (a.dx) {
+    const dim3 gdx(TH * a.NT);
+    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+  }
   return hipGetLastError();
 }
 
