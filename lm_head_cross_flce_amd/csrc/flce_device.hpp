@@ -26,7 +26,6 @@ namespace flce {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -39,24 +38,7 @@ constexpr int kRowBytes = 144;              // fp32 LDS rows: 128 B of K + 16 B 
 constexpr int kBufBytes = kTile * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Storage type tags: bf16 values are carried as uint16_t bit patterns.
-template <class T> struct Elem;
-template <> struct Elem<uint16_t> {
-  static constexpr int kVec = 8;    // elements per 16-byte chunk
-  static constexpr int kBK = 64;    // K per LDS stage
-};
-template <> struct Elem<float> {
-  static constexpr int kVec = 4;
-  static constexpr int kBK = 32;
-};
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
-
-template <class T> __device__ __forceinline__ float load_as_f32(const T* p);
-template <> __device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) {
-  return bf16_bits_to_f32(*p);
-}
 
 // Round-to-nearest-even pack of two floats into bf16x2 (hardware convert).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -140,7 +122,7 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // t read row r0 + t through a descriptor that ends at row V, so rows past V
 // read zero with no branch; it is issued before the mainloop and lands in a
 // register.  publish() stores it to LDS after the mainloop (followed by an
-// lds_barrier), and read_bias16() gives a lane the 16 rows it holds in row block i.
+// lds_barrier), and read_bias4() gives a lane the bias of four consecutive rows.
 template <class T> struct BiasTile {
   float v;
   __device__ __forceinline__ void fetch(const T* b, int64_t V, int64_t r0, int tid) {
@@ -157,20 +139,13 @@ template <class T> struct BiasTile {
   __device__ __forceinline__ void publish(lds_f32* dst, int tid) const { dst[tid] = v; }
 };
 
-// bv[e] = bias of row rloc + 32 i + 8 (e / 4) + e % 4 of the tile (rloc a multiple of 4).
-__device__ __forceinline__ void read_bias16(float (&bv)[16], const lds_f32* src, int rloc, int i) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 t = *(const __attribute__((address_space(3))) f32x4*)(src + rloc + 32 * i + 8 * q);
-    bv[4 * q] = t[0];
-    bv[4 * q + 1] = t[1];
-    bv[4 * q + 2] = t[2];
-    bv[4 * q + 3] = t[3];
-  }
+// Bias of tile rows row .. row + 3 (row a multiple of 4).
+__device__ __forceinline__ f32x4 read_bias4(const lds_f32* src, int row) {
+  return *(const __attribute__((address_space(3))) f32x4*)(src + row);
 }
 
 // ---------------------------------------------------------------------------
-// Operands and global -> LDS staging
+// Operands, accumulators and the MFMA
 // ---------------------------------------------------------------------------
 
 template <class T> struct Opnd {
@@ -180,92 +155,88 @@ template <class T> struct Opnd {
   int kext;      // valid extent along K
 };
 
-// One stage of one operand: 256 rows x kBK, 8 x 16 bytes per thread.  The
-// descriptor is rebased on every stage (scalar arithmetic), so the per-lane
-// byte offsets are fixed for the whole tile and stay small.
+// A wave's 128 x 128 tile as 8 x 8 blocks of 16 x 16.  Element r of block
+// (i, j) in lane l is row 16 i + 4 (l / 16) + r, column 16 j + l % 16.
+typedef f32x4 Acc[8][8];
+
+// One v_mfma_f32_16x16x32_bf16 into an accumulator kept in AGPRs.  The
+// accumulator is tied to the destination in inline asm: the compiler's own
+// register choice for this instruction moves accumulators between registers
+// on every step.  ZERO starts the accumulator at zero.  The compiler does not
+// see the instruction's latency: acc_drain() must precede any read of the
+// accumulators (acc_read4).
+template <bool ZERO>
+__device__ __forceinline__ void mfma16(f32x4& c, const u32x4& a, const u32x4& b) {
+  if (ZERO) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <bool ZERO>
+__device__ __forceinline__ void mfma16_f32(f32x4& c, float a, float b) {
+  if (ZERO) asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA of a tile and reads of its accumulators
+// (more than the longest MFMA used here needs).  The scheduling barrier keeps
+// every MFMA ahead of the wait.
+__device__ __forceinline__ void acc_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// One block's accumulators in VGPRs.  Volatile reads keep each block's copies
+// where the epilogue uses them; left to itself the register allocator copies
+// all 256 accumulators at once and spills.
+__device__ __forceinline__ f32x4 acc_read4(const f32x4& blk) {
+  f32x4 z;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[0]) : "a"(blk[0]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[1]) : "a"(blk[1]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[2]) : "a"(blk[2]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[3]) : "a"(blk[3]));
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 operands: register-staged copies and v_mfma_f32_16x16x4_f32
+// (correctness-oriented; no fine-grained interleave)
+// ---------------------------------------------------------------------------
+
+// One stage of one operand: 256 rows x 32 fp32, 8 x 16 bytes per thread,
+// stored to LDS rows of kRowBytes with K contiguous.
 template <class T, bool KCONTIG> struct Stager;
 
 // K-contiguous: thread (kc = tid % 8, rr = tid / 8) loads 16 bytes of K at
-// column chunk kc of rows rr + 32 q.  Requires kext % kVec == 0.
-template <class T> struct Stager<T, true> {
+// column chunk kc of rows rr + 32 q.
+template <> struct Stager<float, true> {
   u32x4 r[8];
   uint32_t off[8];
-  const T* base;
+  const float* base;
   int kc_elem;
-  __device__ __forceinline__ void init(const Opnd<T>& o, int m0, int tid) {
+  __device__ __forceinline__ void init(const Opnd<float>& o, int m0, int tid) {
     const int kc = tid & 7, rr = tid >> 3;
-    kc_elem = kc * Elem<T>::kVec;
+    kc_elem = kc * 4;
     base = o.p + (int64_t)m0 * o.ld;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = rr + 32 * q;
-      off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + kc_elem) * sizeof(T)) : kOOB;
+      off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + kc_elem) * 4) : kOOB;
     }
   }
-  __device__ __forceinline__ void load(const Opnd<T>& o, int k0) {
+  __device__ __forceinline__ void load(const Opnd<float>& o, int k0) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
     const bool kok = k0 + kc_elem < o.kext;
 #pragma unroll
     for (int q = 0; q < 8; ++q) r[q] = buf_load16(rs, kok ? off[q] : kOOB);
   }
   __device__ __forceinline__ void store(lds_t* buf, int tid) const {
-    store_half<0>(buf, tid);
-    store_half<1>(buf, tid);
-  }
-  template <int HALF>
-  __device__ __forceinline__ void store_half(lds_t* buf, int tid) const {
     const int kc = tid & 7, rr = tid >> 3;
 #pragma unroll
-    for (int q = 4 * HALF; q < 4 * HALF + 4; ++q) lds_store16(buf + (rr + 32 * q) * kRowBytes + kc * 16, r[q]);
+    for (int q = 0; q < 8; ++q) lds_store16(buf + (rr + 32 * q) * kRowBytes + kc * 16, r[q]);
   }
 };
 
-// M-contiguous bf16: thread (kc = tid % 8, mc = tid / 8) loads rows
-// k0 + 8 kc + e (e < 8) at columns m0 + 8 mc .. + 7, then writes the
-// transposed 8 x 8 block.  Requires mext % 8 == 0.
-template <> struct Stager<uint16_t, false> {
-  u32x4 r[8];
-  uint32_t off[8];
-  const uint16_t* base;
-  int krow;
-  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
-    const int kc = tid & 7, mc = tid >> 3;
-    krow = kc * 8;
-    base = o.p + m0;
-    const bool mok = m0 + mc * 8 < o.mext;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      off[e] = mok ? (uint32_t)(((int64_t)(krow + e) * o.ld + mc * 8) * 2) : kOOB;
-  }
-  __device__ __forceinline__ void load(const Opnd<uint16_t>& o, int k0) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * o.ld);
-    const int kleft = o.kext - k0 - krow;   // rows e < kleft are valid
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = buf_load16(rs, e < kleft ? off[e] : kOOB);
-  }
-  __device__ __forceinline__ void store(lds_t* buf, int tid) const {
-    store_half<0>(buf, tid);
-    store_half<1>(buf, tid);
-  }
-  template <int HALF>
-  __device__ __forceinline__ void store_half(lds_t* buf, int tid) const {
-    const int kc = tid & 7, mc = tid >> 3;
-#pragma unroll
-    for (int p = 2 * HALF; p < 2 * HALF + 2; ++p) {
-      u32x4 ev, od;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = r[2 * w][p], b = r[2 * w + 1][p];
-        ev[w] = (a & 0xffffu) | (b << 16);
-        od[w] = (a >> 16) | (b & 0xffff0000u);
-      }
-      lds_store16(buf + (mc * 8 + 2 * p) * kRowBytes + kc * 16, ev);
-      lds_store16(buf + (mc * 8 + 2 * p + 1) * kRowBytes + kc * 16, od);
-    }
-  }
-};
-
-// M-contiguous fp32: 4 x 4 blocks, two per thread (mc = tid / 8 + 32 p).
+// M-contiguous fp32: 4 x 4 blocks transposed in registers, two per thread
+// (mc = tid / 8 + 32 p).
 template <> struct Stager<float, false> {
   u32x4 r[8];
   uint32_t off[8];
@@ -304,83 +275,42 @@ template <> struct Stager<float, false> {
   }
 };
 
-// ---------------------------------------------------------------------------
-// MFMA over one LDS stage
-// ---------------------------------------------------------------------------
-
-template <class T> struct Mma;
-
-template <> struct Mma<uint16_t> {
-  // 4 sub-steps of K = 16: v_mfma_f32_32x32x16_bf16.
-  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const lds_t* bA, const lds_t* bB,
-                                               int wm, int wn, int lane) {
-    const int rl = lane & 31, kh = lane >> 5;
-    const lds_t* pa = bA + (wm * 128 + rl) * kRowBytes + kh * 16;
-    const lds_t* pb = bB + (wn * 128 + rl) * kRowBytes + kh * 16;
+// One 32-deep fp32 stage: per 16 x 16 block, 8 x v_mfma_f32_16x16x4_f32.  A
+// 16-byte read gives lane l four consecutive k at 4 (l / 16) (+ 16 for the
+// second half of the stage); instruction e uses element e, so lane group g
+// supplies k = 4 g + e: over e = 0..3 the four groups cover k = 0..15 in a
+// permuted order, the same for A and B.
+template <bool FIRST>
+__device__ __forceinline__ void mma_stage_f32(Acc& acc, const lds_t* bA, const lds_t* bB, int wm, int wn, int lane) {
+  const int rl = lane & 15, g = lane >> 4;
+  const lds_t* pa = bA + (wm * 128 + rl) * kRowBytes + g * 16;
+  const lds_t* pb = bB + (wn * 128 + rl) * kRowBytes + g * 16;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 a[4], b[4];
+  for (int h = 0; h < 2; ++h) {
+    f32x4 a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_load16(pa + 32 * i * kRowBytes + s * 32);
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(f32x4, lds_load16(pa + 16 * i * kRowBytes + 64 * h));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_load16(pb + 32 * j * kRowBytes + s * 32);
+    for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(f32x4, lds_load16(pb + 16 * j * kRowBytes + 64 * h));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
-    }
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (FIRST && h == 0 && e == 0) mfma16_f32<true>(acc[i][j], a[i][e], b[j][e]);
+          else mfma16_f32<false>(acc[i][j], a[i][e], b[j][e]);
+        }
   }
-};
+}
 
-template <> struct Mma<float> {
-  // 2 sub-steps of K = 16, each 8 x v_mfma_f32_32x32x2_f32.  Lane half kh holds
-  // logical k = 16 s + 8 kh + e for register e; instruction e pairs k and k + 8.
-  static __device__ __forceinline__ void stage(f32x16 (&acc)[4][4], const lds_t* bA, const lds_t* bB,
-                                               int wm, int wn, int lane) {
-    const int rl = lane & 31, kh = lane >> 5;
-    const lds_t* pa = bA + (wm * 128 + rl) * kRowBytes + kh * 32;
-    const lds_t* pb = bB + (wn * 128 + rl) * kRowBytes + kh * 32;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f32x4 a[4][2], b[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i][0] = __builtin_bit_cast(f32x4, lds_load16(pa + 32 * i * kRowBytes + s * 64));
-        a[i][1] = __builtin_bit_cast(f32x4, lds_load16(pa + 32 * i * kRowBytes + s * 64 + 16));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b[j][0] = __builtin_bit_cast(f32x4, lds_load16(pb + 32 * j * kRowBytes + s * 64));
-        b[j][1] = __builtin_bit_cast(f32x4, lds_load16(pb + 32 * j * kRowBytes + s * 64 + 16));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e >> 2][e & 3], b[j][e >> 2][e & 3],
-                                                             acc[i][j], 0, 0, 0);
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Tile mainloops
-// ---------------------------------------------------------------------------
-
-// fp32 operands (correctness-oriented; no fine-grained interleave).
+// fp32 tile mainloop: two padded LDS buffers per operand, register staging.
+// Ends with a barrier; the accumulators need acc_drain() before they are read.
 template <bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<float>& A, int m0,
-                                              const Opnd<float>& B, int n0, int K, const Lds& L, int tid) {
-  constexpr int kBK = Elem<float>::kBK;
+__device__ __forceinline__ void gemm_tile_f32(Acc& acc, const Opnd<float>& A, int m0, const Opnd<float>& B, int n0,
+                                              int K, const Lds& L, int tid) {
+  constexpr int kBK = 32;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   Stager<float, AK> sa;
   Stager<float, BK> sb;
   sa.init(A, m0, tid);
@@ -398,7 +328,8 @@ __device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<fl
       sa.load(A, (kt + 1) * kBK);
       sb.load(B, (kt + 1) * kBK);
     }
-    Mma<float>::stage(acc, cur ? L.a[1] : L.a[0], cur ? L.b[1] : L.b[0], wm, wn, lane);
+    if (kt == 0) mma_stage_f32<true>(acc, L.a[0], L.b[0], wm, wn, lane);
+    else mma_stage_f32<false>(acc, cur ? L.a[1] : L.a[0], cur ? L.b[1] : L.b[0], wm, wn, lane);
     if (more) {
       sa.store(cur ? L.a[0] : L.a[1], tid);
       sb.store(cur ? L.b[0] : L.b[1], tid);
@@ -412,22 +343,21 @@ __device__ __forceinline__ void gemm_tile_f32(f32x16 (&acc)[4][4], const Opnd<fl
 // buffers per operand; each stage is copied three stages ahead by the buffer
 // unit (buffer_load ... lds, 16 bytes per lane, each wave instruction filling
 // 1 KB of LDS contiguously), so no registers or LDS-write instructions carry
-// operands and about three stages of MFMA work cover the copy latency.
+// operands.
 //
 // K-contiguous operand, one stage = 256 rows x 32 k: LDS rows of 64 bytes;
-// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 2) & 3).  A
-// fragment read (16 lanes = 16 consecutive rows, one logical chunk) then
-// touches each of the 64 banks once.
+// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 1) & 3).  A
+// fragment (16 rows, lane l: row l % 16, K chunk l / 16) is one 16-byte read
+// per lane, free of bank conflicts on gfx950's 64 banks (measured).
 //
 // M-contiguous operand, one stage = 32 k x 256 m in its global layout: LDS
 // rows (one per k) of 512 bytes; chunk p of row k holds logical chunk
 // p ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16, which within
-// each 16-lane group hands lane l element l % 4 of the 8-byte pieces addressed
-// by lanes 4 e + l / 4 (e = 0..3): lane j of a group addresses row
-// k = 8 kh + 4 r + j / 4 at columns m .. m + 3 with m = 16 (group & 1) +
-// 4 (j % 4), so lane l receives column l % 32 at k = 8 kh + 4 r + e, the same
-// K order as a 16-byte read of a K-contiguous row.  The 32 lanes read together
-// cover 4 rows x 4 chunks, again all 64 banks.
+// each 16-lane group hands lane l element l % 4 of the 8-byte pieces
+// addressed by lanes 4 e + l / 4 (e = 0..3): lane j of group G addresses row
+// k = 8 G + 4 h + j / 4 at columns m0 + 4 (j % 4) .. + 3, so lane l receives
+// column m0 + l % 16 at k = 8 G + 4 h + e, the K order of a 16-byte read of
+// a K-contiguous row; two reads (h = 0, 1) give the lane its 8 values.
 // ---------------------------------------------------------------------------
 
 constexpr int kStageK = 32;
@@ -441,41 +371,40 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint
 // outstanding and all LDS operations are done.
 template <int N> constexpr int waitcnt_vm_lgkm0() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
 
+// Copies of one operand: 16 wave instructions per stage, 4 per wave
+// (q = 0..3, instruction index 4 q + wave).  issue(q) fills them one at a
+// time so a stage body can spread them between MFMAs; TAIL masks K chunks
+// past K (stages that are not wholly inside K).
 template <bool KCONTIG> struct Dma;
 
-// 16 wave instructions per stage (4 per wave): instruction idx fills rows
-// 16 idx .. 16 idx + 15.
+// K-contiguous: instruction idx fills rows 16 idx .. 16 idx + 15.
 template <> struct Dma<true> {
   uint32_t off[4];
   const uint16_t* base;
+  int64_t ld;
   int wave;
   __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = o.p + (int64_t)m0 * o.ld;
+    ld = o.ld;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = 16 * (4 * q + wave) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
       off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
-  // Branch-free so that a stage body stays one basic block.
-  __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0);
-    const int kleft = o.kext - k0;
-    const int lane = tid & 63;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 16 * (4 * q + wave) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      dma16(rs, buf + (4 * q + wave) * 1024, 8 * c < kleft ? off[q] : kOOB);
-    }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const { return make_rsrc(base + k0); }
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kleft, lds_t* buf, int lane, int q) const {
+    const int row = 16 * (4 * q + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    dma16(rs, buf + (4 * q + wave) * 1024, (!TAIL || 8 * c < kleft) ? off[q] : kOOB);
   }
 };
 
-// 16 wave instructions per stage (4 per wave): instruction idx fills k rows
-// 2 idx and 2 idx + 1.
+// M-contiguous: instruction idx fills k rows 2 idx and 2 idx + 1.
 template <> struct Dma<false> {
   uint32_t off[4];
   const uint16_t* base;
@@ -493,15 +422,11 @@ template <> struct Dma<false> {
       off[q] = (m0 + 8 * c < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(const Opnd<uint16_t>& o, int k0, lds_t* buf, int tid) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)k0 * ld);
-    const int kleft = o.kext - k0;
-    const int lane = tid & 63;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 2 * (4 * q + wave) + (lane >> 5);
-      dma16(rs, buf + (4 * q + wave) * 1024, row < kleft ? off[q] : kOOB);
-    }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const { return make_rsrc(base + (int64_t)k0 * ld); }
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kleft, lds_t* buf, int lane, int q) const {
+    const int row = 2 * (4 * q + wave) + (lane >> 5);
+    dma16(rs, buf + (4 * q + wave) * 1024, (!TAIL || row < kleft) ? off[q] : kOOB);
   }
 };
 
@@ -509,113 +434,126 @@ template <> struct Dma<false> {
 template <bool KCONTIG> struct FragAddr;
 
 template <> struct FragAddr<true> {
-  int a[2];   // per sub-step s; block i adds 32 * 64 * i
+  static constexpr int kReads = 1;   // LDS read instructions per 16-row block
+  int base;                          // block i adds 16 * 64 * i
   __device__ __forceinline__ void init(int wbase, int lane) {
-    const int rl = lane & 31, kh = lane >> 5, f = (rl >> 2) & 3;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) a[s] = (wbase + rl) * 64 + 16 * ((2 * s + kh) ^ f);
+    const int rl = lane & 15, c = lane >> 4;
+    base = (wbase + rl) * 64 + 16 * (c ^ ((rl >> 1) & 3));
   }
-  __device__ __forceinline__ u32x4 read(const lds_t* buf, int i, int s) const {
-    return lds_load16(buf + a[s] + 2048 * i);
+  template <int H>
+  __device__ __forceinline__ void read(u32x4& f, const lds_t* buf, int i) const {
+    f = lds_load16(buf + base + 1024 * i);
   }
 };
 
 template <> struct FragAddr<false> {
-  int a[4];   // per block i; sub-step s and half r add (16 s + 4 r) * 512
+  static constexpr int kReads = 2;
+  int a[2][8];   // per half h and block i
   __device__ __forceinline__ void init(int wbase, int lane) {
-    const int j = lane & 15, kh = lane >> 5, g = (lane >> 4) & 1;
+    const int j = lane & 15, G = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wbase + 32 * i + 16 * g + 4 * (j & 3);
-      const int c = (m >> 3) ^ (4 * (j >> 2));
-      a[i] = (8 * kh + (j >> 2)) * 512 + 16 * c + 8 * (j & 1);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 8 * G + 4 * h + (j >> 2);
+        const int m = wbase + 16 * i + 4 * (j & 3);
+        a[h][i] = k * 512 + 16 * ((m >> 3) ^ (4 * (k & 3))) + 2 * (m & 7);
+      }
   }
-  __device__ __forceinline__ u32x4 read(const lds_t* buf, int i, int s) const {
+  // Half H of block i: elements 2H, 2H + 1 of the fragment's dwords.
+  template <int H>
+  __device__ __forceinline__ void read(u32x4& f, const lds_t* buf, int i) const {
     typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    const lds_t* p = buf + a[i] + 16 * 512 * s;
-    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
-    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * 512)));
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + a[H][i])));
+    f[2 * H] = v[0];
+    f[2 * H + 1] = v[1];
   }
 };
 
-// bf16 fragments of one K = 16 sub-step for this wave: 4 A blocks, 4 B blocks.
-struct FragBF16 {
-  u32x4 a[4], b[4];
+// bf16 fragments of one stage for this wave: 8 A blocks, 8 B blocks.
+struct Frag {
+  u32x4 a[8], b[8];
 };
 
+// One read instruction of a stage's fragments, by index: A blocks 0..3 come
+// first (kReads each), then B blocks 0..7, then A blocks 4..7.
 template <bool AK, bool BK>
-__device__ __forceinline__ void load_frag(FragBF16& f, const FragAddr<AK>& fa, const FragAddr<BK>& fb,
-                                          const lds_t* bA, const lds_t* bB, int s) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = fa.read(bA, i, s);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = fb.read(bB, j, s);
+__device__ __forceinline__ void frag_read(Frag& f, const FragAddr<AK>& fa, const FragAddr<BK>& fb, const lds_t* bA,
+                                          const lds_t* bB, int idx) {
+  constexpr int RA = FragAddr<AK>::kReads, RB = FragAddr<BK>::kReads;
+  if (idx < 4 * RA) {
+    const int i = idx / RA;
+    if (RA == 1 || (idx % RA) == 0) fa.template read<0>(f.a[i], bA, i);
+    else fa.template read<1>(f.a[i], bA, i);
+  } else if (idx < 4 * RA + 8 * RB) {
+    const int t = idx - 4 * RA, j = t / RB;
+    if (RB == 1 || (t % RB) == 0) fb.template read<0>(f.b[j], bB, j);
+    else fb.template read<1>(f.b[j], bB, j);
+  } else {
+    const int t = idx - 4 * RA - 8 * RB, i = 4 + t / RA;
+    if (RA == 1 || (t % RA) == 0) fa.template read<0>(f.a[i], bA, i);
+    else fa.template read<1>(f.a[i], bA, i);
+  }
 }
 
-__device__ __forceinline__ void mma_frag(f32x16 (&acc)[4][4], const FragBF16& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
-                                                           __builtin_bit_cast(bf16x8, f.b[j]), acc[i][j], 0, 0, 0);
-}
-
-// Instruction classes for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
-
-// One stage of the bf16 pipeline, for the stage held in ring slot CUR.  The
-// barrier sits between the stage's two K sub-steps' worth of MFMAs, so each
-// body starts with the previous stage's second sub-step (registers f1) while
-// this stage's first fragments are read and the stage three ahead is copied:
-//   [mma f1 (previous s1) | read f0 <- s0 | copy stage + 3 -> slot CUR + 3]
-//   [mma f0 (s0) | read f1 <- s1]   wait for the copy of the next stage, barrier
-template <int CUR, bool FIRST, bool AK, bool BK, int VMW = 16>
-__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[4][4], FragBF16& f0, FragBF16& f1,
-                                           const FragAddr<AK>& fa, const FragAddr<BK>& fb, const Lds& L, int tid,
-                                           const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, const Dma<AK>& da,
-                                           const Dma<BK>& db, int k_copy) {
-  constexpr int kReads = (AK ? 4 : 8) + (BK ? 4 : 8);   // LDS read instructions per sub-step
+// One stage body, for the stage held in ring slot CUR.  Its 64 MFMAs per wave
+// are split by A block: the first 32 slots run the previous stage's blocks
+// i = 4..7 (fragments P) while this stage's A 0..3 and B 0..7 fragments are
+// read and the stage three ahead is copied (one instruction per MFMA slot);
+// the next 32 run this stage's blocks i = 0..3 while A 4..7 are read.  Then
+// one wait (copies of the next stage done; VMW newer memory operations may
+// stay in flight) and one barrier.  FIRST: the tile's first stage (no previous
+// MFMAs; blocks 0..3 start from zero); SECOND: blocks 4..7 start from zero.
+// Every instruction slot ends in a scheduling barrier, which pins this order.
+template <int CUR, bool FIRST, bool SECOND, bool AK, bool BK, int VMW, bool TAIL>
+__device__ __forceinline__ void stage_bf16(Acc& acc, Frag& P, Frag& C, const FragAddr<AK>& fa,
+                                           const FragAddr<BK>& fb, const Lds& L, int lane, const Opnd<uint16_t>& A,
+                                           const Opnd<uint16_t>& B, const Dma<AK>& da, const Dma<BK>& db,
+                                           int k_copy) {
   constexpr int NXT = (CUR + 3) & 3;
+  constexpr int RA = FragAddr<AK>::kReads, RB = FragAddr<BK>::kReads;
+  constexpr int kReads1 = 4 * RA + 8 * RB;          // reads in the first half
+  constexpr int kSlots1 = kReads1 + 8;              // plus 8 copy instructions
+  static_assert(kSlots1 <= 32, "first half holds at most one read or copy per MFMA");
   const lds_t* bA = L.a[CUR];
   const lds_t* bB = L.b[CUR];
-  load_frag<AK, BK>(f0, fa, fb, bA, bB, 0);
-  if (!FIRST) mma_frag(acc, f1);
-  da.issue(A, k_copy, L.a[NXT], tid);
-  db.issue(B, k_copy, L.b[NXT], tid);
-  load_frag<AK, BK>(f1, fa, fb, bA, bB, 1);
-  mma_frag(acc, f0);
-  if (FIRST) {
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgVmem, 8, 0);
-  } else {
+  const __amdgpu_buffer_rsrc_t rsa = da.rsrc(k_copy);
+  const __amdgpu_buffer_rsrc_t rsb = db.rsrc(k_copy);
+  const int kla = A.kext - k_copy, klb = B.kext - k_copy;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
+  for (int k = 0; k < 32; ++k) {
+    if (!FIRST) mfma16<SECOND>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
+    // reads fill the slots before the copies; copies take every other slot
+    // after that while there is room, else the next free slots
+    constexpr int kGap = (32 - kReads1) >= 16 ? 2 : 1;
+    if (k < kReads1) {
+      frag_read<AK, BK>(C, fa, fb, bA, bB, k);
+    } else if ((k - kReads1) % kGap == 0 && (k - kReads1) / kGap < 8) {
+      const int q = (k - kReads1) / kGap;
+      if (q < 4) da.template issue<TAIL>(rsa, kla, L.a[NXT], lane, q);
+      else db.template issue<TAIL>(rsb, klb, L.b[NXT], lane, q - 4);
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kReads / 8, 0);
+  for (int k = 0; k < 32; ++k) {
+    mfma16<FIRST>(acc[k / 8][k % 8], C.a[k / 8], C.b[k % 8]);
+    if (k < 4 * RA) frag_read<AK, BK>(C, fa, fb, bA, bB, kReads1 + k);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
-  // Keep the trailing MFMAs ahead of the barrier: they cover the latency of
-  // the last fragment reads, which the barrier waits for.
-  __builtin_amdgcn_sched_barrier(0);
-  // The next stage's copies were issued two bodies ago; the 16 newer copy
-  // instructions (the next two stages) may stay in flight, and VMW - 16 more
-  // where the caller issued other memory operations in between.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VMW>());
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The upper half (blocks 4..7) of a tile's last stage.
+template <bool ZERO>
+__device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    mfma16<ZERO>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Copy state of one bf16 tile.  start() issues the copies of the first three
@@ -629,12 +567,16 @@ template <bool AK, bool BK> struct TileCopy {
                                         const Lds& L, int tid) {
     da.init(A, m0, tid);
     db.init(B, n0, tid);
+    const int lane = tid & 63;
     // Copies past K read zeros (out-of-range offsets), so the stage bodies
     // need no branches; the ones still in flight are drained at the end.
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
-      da.issue(A, st * kStageK, L.a[st], tid);
-      db.issue(B, st * kStageK, L.b[st], tid);
+      const int k0 = st * kStageK;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) da.template issue<true>(da.rsrc(k0), A.kext - k0, L.a[st], lane, q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) db.template issue<true>(db.rsrc(k0), B.kext - k0, L.b[st], lane, q);
     }
   }
 };
@@ -646,48 +588,60 @@ template <bool AK, bool BK> struct TileCopy {
 // older than those instructions, allow EXTRA more to stay in flight instead
 // of draining the epilogue's stores.  Counting too few only costs a stall;
 // every counted instruction must be issued unconditionally by every wave.
+// Returns with all copies complete; the accumulators need acc_drain() before
+// they are read.
 template <bool AK, bool BK, int EXTRA = 0>
-__device__ __forceinline__ void gemm_tile_bf16_run(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A,
-                                                   const Opnd<uint16_t>& B, int K, const Lds& L, int tid,
-                                                   const TileCopy<AK, BK>& tc) {
+__device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, int K,
+                                                   const Lds& L, int tid, const TileCopy<AK, BK>& tc) {
   static_assert(EXTRA >= 0 && 16 + EXTRA <= 63, "vmcnt holds at most 63");
   constexpr int W0 = 16 + EXTRA;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Dma<AK>& da = tc.da;
   const Dma<BK>& db = tc.db;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   FragAddr<AK> fa;
   FragAddr<BK> fb;
   fa.init(wm * 128, lane);
   fb.init(wn * 128, lane);
+  // Stages run in groups of four (one per ring slot); the count is rounded
+  // up to a multiple of four, the extra stages reading zeros (their copies
+  // lie past K).  The loops then hold whole groups and no stage body is
+  // conditional: the register allocator keeps the tied accumulators in place
+  // only along straight-line paths.  Stage s keeps its fragments in X (s
+  // even) or Y (s odd).
   const int KT = (K + kStageK - 1) / kStageK;
+  const int KTp = KT <= 4 ? 4 : (KT + 3) & ~3;
+  const int KF = K / kStageK;   // stages wholly inside K
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<W0>());
   __builtin_amdgcn_s_barrier();
-  FragBF16 f0, f1;
+  Frag X, Y;
   // Stages 0 and 1 end by waiting for the copies of stages 1 and 2, which
-  // start() issued; from stage 2 on, the waited-for copies are the body's own.
-  stage_bf16<0, true, AK, BK, W0>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 3 * kStageK);
-  if (KT > 1) stage_bf16<1, false, AK, BK, W0>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, 4 * kStageK);
-  int kt = 2;
-  for (; kt + 3 < KT; kt += 4) {
-    stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
-    stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
-    stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
-    stage_bf16<1, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 6) * kStageK);
+  // start() issued (EXTRA newer instructions may be in flight); from stage 2
+  // on, the waited-for copies are the body's own.
+  stage_bf16<0, true, false, AK, BK, W0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 3 * kStageK);
+  stage_bf16<1, false, true, AK, BK, W0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 4 * kStageK);
+  stage_bf16<2, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 5 * kStageK);
+  stage_bf16<3, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 6 * kStageK);
+  int kt = 4;
+  // copies of stages kt + 3 .. kt + 6 wholly inside K: no masking
+  for (; kt + 7 <= KF; kt += 4) {
+    stage_bf16<0, false, false, AK, BK, 16, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 3) * kStageK);
+    stage_bf16<1, false, false, AK, BK, 16, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 4) * kStageK);
+    stage_bf16<2, false, false, AK, BK, 16, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 5) * kStageK);
+    stage_bf16<3, false, false, AK, BK, 16, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 6) * kStageK);
   }
-  if (kt < KT) stage_bf16<2, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 3) * kStageK);
-  if (kt + 1 < KT) stage_bf16<3, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 4) * kStageK);
-  if (kt + 2 < KT) stage_bf16<0, false, AK, BK>(acc, f0, f1, fa, fb, L, tid, A, B, da, db, (kt + 5) * kStageK);
-  mma_frag(acc, f1);  // second sub-step of the last stage
+  for (; kt < KTp; kt += 4) {
+    stage_bf16<0, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 3) * kStageK);
+    stage_bf16<1, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 4) * kStageK);
+    stage_bf16<2, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 5) * kStageK);
+    stage_bf16<3, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 6) * kStageK);
+  }
+  stage_last_half<false>(acc, Y);   // upper half of stage KTp - 1 (odd)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
 }
 
 template <bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<uint16_t>& A, int m0,
-                                               const Opnd<uint16_t>& B, int n0, int K, const Lds& L, int tid) {
+__device__ __forceinline__ void gemm_tile_bf16(Acc& acc, const Opnd<uint16_t>& A, int m0, const Opnd<uint16_t>& B,
+                                               int n0, int K, const Lds& L, int tid) {
   TileCopy<AK, BK> tc;
   tc.start(A, m0, B, n0, L, tid);
   gemm_tile_bf16_run<AK, BK>(acc, A, B, K, L, tid, tc);
@@ -695,10 +649,10 @@ __device__ __forceinline__ void gemm_tile_bf16(f32x16 (&acc)[4][4], const Opnd<u
 
 // One 256 x 256 output tile: acc = A[m0:m0+256, :K] * B[n0:n0+256, :K]^T.
 // Every wave's last LDS read precedes the mainloop's last barrier, so LDS may
-// be reused right after it returns.
+// be reused right after it returns.  Call acc_drain() before reading acc.
 template <class T, bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], const Opnd<T>& A, int m0,
-                                          const Opnd<T>& B, int n0, int K, const Lds& L, int tid) {
+__device__ __forceinline__ void gemm_tile(Acc& acc, const Opnd<T>& A, int m0, const Opnd<T>& B, int n0, int K,
+                                          const Lds& L, int tid) {
   if constexpr (sizeof(T) == 2) gemm_tile_bf16<AK, BK>(acc, A, m0, B, n0, K, L, tid);
   else gemm_tile_f32<AK, BK>(acc, A, m0, B, n0, K, L, tid);
 }

@@ -26,72 +26,11 @@
 namespace flce {
 
 // ---------------------------------------------------------------------------
-// Epilogue helpers.  Lane half g = lane / 32; for accumulator element e of
-// block (i, j) the row inside the wave tile is 32 i + 8 (e / 4) + 4 g + e % 4
-// and the column is 32 j + lane % 32.
+// Epilogue helpers.  Accumulator layout (Acc): element r of block (i, j) in
+// lane l is row 16 i + 4 g + r and column 16 j + l % 16 of the wave tile,
+// with g = l / 16.  A lane thus holds, for each of its 8 columns, 32 rows:
+// four consecutive ones in each of the 8 row blocks.
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int row_off(int i, int e) { return 32 * i + 8 * (e >> 2) + (e & 3); }
-
-// Copy one 32 x 32 accumulator block to VGPRs where the epilogue needs it.
-// Left to itself the register allocator copies all 256 accumulators at the end
-// of the mainloop, which overflows the VGPRs and spills; volatile reads keep
-// each block's copies in program order.  The caller has let the MFMA pipeline
-// drain (acc_drain) before the first read.
-__device__ __forceinline__ void read_acc16(float (&z)[16], const f32x16& blk) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[e]) : "a"(blk[e]));
-}
-
-// Wait states between the last MFMA and a read of its accumulators (more than
-// the longest MFMA used here needs).  The scheduling barrier keeps every MFMA
-// of the mainloop ahead of the wait.
-__device__ __forceinline__ void acc_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
-// Fold one 32 x 32 block (16 values of one column per lane, already in
-// VGPRs) into the running (m, d) of that column, the running sum of logits,
-// and the target logit.
-template <bool SMOOTH, bool RAGGED>
-__device__ __forceinline__ void lse_block(const float (&acc)[16], const float (&bv)[16], int i, float& m, float& d,
-                                          float& sz, float& zy, int t, int rb, int V) {
-  float z[16];
-  float bmax = -INFINITY, zs = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    z[e] = acc[e] + bv[e];
-    if (RAGGED) {
-      const bool ok = rb + row_off(i, e) < V;
-      if (SMOOTH) zs += ok ? z[e] : 0.f;
-      z[e] = ok ? z[e] : -INFINITY;
-    } else if (SMOOTH) {
-      zs += z[e];
-    }
-    bmax = fmaxf(bmax, z[e]);
-  }
-  const float mn = fmaxf(m, bmax);
-  if (!RAGGED || mn != -INFINITY) {
-    const float nml = -mn * kLog2e;
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ps += fast_exp2(fmaf(z[e], kLog2e, nml));
-    d = d * fast_exp2((m - mn) * kLog2e) + ps;  // m = -inf: the factor is 0
-    m = mn;
-  }
-  if (SMOOTH) sz += zs;
-  // Target row: wave-uniform branch, rarely taken.
-  const int tb = t - 32 * i;
-  const bool own = (tb >= 0) && (tb < 32) && ((tb & 4) == 0);
-  if (__ballot(own)) {
-    float val = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (tb == row_off(0, e)) val = z[e];
-    if (own) zy = val;
-  }
-}
 
 __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2) {
   const float mn = fmaxf(m, m2);
@@ -100,6 +39,53 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
   if (m2 != -INFINITY) r += d2 * fast_exp2((m2 - mn) * kLog2e);
   m = mn;
   d = r;
+}
+
+// Fold column j of a tile (this lane's 32 rows of one token) into the running
+// (m, d) of that token, the running sum of logits, and the target logit.
+// rb: tile row index of the lane's row 0 (v0 + wave row offset + 4 g); t: the
+// token's target minus rb (negative if ignored or elsewhere).
+template <bool SMOOTH, bool RAGGED>
+__device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&bias)[8], float& m, float& d,
+                                           float& sz, float& zy, int t, int rb, int V) {
+  float z[32];
+  float bmax = -INFINITY, zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 v = acc_read4(acc[i][j]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = v[r] + bias[i][r];
+      if (RAGGED) {
+        const bool ok = rb + 16 * i + r < V;
+        if (SMOOTH) zs += ok ? x : 0.f;
+        x = ok ? x : -INFINITY;
+      } else if (SMOOTH) {
+        zs += x;
+      }
+      z[4 * i + r] = x;
+      bmax = fmaxf(bmax, x);
+    }
+  }
+  const float mn = fmaxf(m, bmax);
+  if (!RAGGED || mn != -INFINITY) {
+    const float nml = -mn * kLog2e;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ps += fast_exp2(fmaf(z[e], kLog2e, nml));
+    d = d * fast_exp2((m - mn) * kLog2e) + ps;  // m = -inf: the factor is 0
+    m = mn;
+  }
+  if (SMOOTH) sz += zs;
+  // Target row (t = 16 i + r for the owning lane): wave-uniform branch, rarely taken.
+  const bool own = t >= 0 && t < 128 && ((t >> 2) & 3) == 0;
+  if (__ballot(own)) {
+    float val = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (t == 16 * (e >> 2) + (e & 3)) val = z[e];
+    if (own) zy = val;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -113,6 +99,7 @@ template <class T, bool BIAS, bool SMOOTH>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
   const int w = blockIdx.x;
   int nt, ph;
   if ((a.NT & 7) == 0) {
@@ -127,11 +114,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
 
-  int ycol[4];
-  float m[4], d[4], sz[4], zy[4];
+  // This lane's 8 tokens: n0 + wn * 128 + 16 j + lane % 16.
+  int ycol[8];
+  float m[8], d[8], sz[8], zy[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * kWaveTile + 32 * j + (lane & 31);
+  for (int j = 0; j < 8; ++j) {
+    const int n = n0 + wn * kWaveTile + 16 * j + (lane & 15);
     const int64_t t = n < a.N ? a.targets[n] : a.ignore_index;
     ycol[j] = (t == a.ignore_index) ? -1 : (int)t;
     m[j] = -INFINITY;
@@ -140,8 +128,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     zy[j] = 0.f;
   }
 
-  f32x16 acc[4][4];
-  const int rloc = wm * kWaveTile + 4 * (lane >> 5);   // first tile row of this lane's row block 0
+  Acc acc;
+  const int rloc = wm * kWaveTile + 4 * g;   // tile row of this lane's row 0
   // bf16: the next tile's first stages are copied while this tile's epilogue runs.
   TileCopy<true, true> tc;
   if constexpr (sizeof(T) == 2) {
@@ -152,62 +140,59 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     BiasTile<T> bt;
     if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
     if constexpr (sizeof(T) == 2) {
-      gemm_tile_bf16_run<true, true>(acc, A, B, a.H, L, tid, tc);
+      gemm_tile_bf16_run<true, true, BIAS ? 1 : 0>(acc, A, B, a.H, L, tid, tc);
       if (vt + a.P < a.VT) tc.start(A, v0 + a.P * kTile, B, n0, L, tid);
     } else {
       gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
     }
+    f32x4 bias[8];
     if (BIAS) {
       bt.publish(L.bias, tid);
       lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bias[i] = read_bias4(L.bias, rloc + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bias[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int rb = v0 + rloc;
     const bool full = v0 + kTile <= a.V;
     acc_drain();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float bv[16];
-      if (BIAS) {
-        read_bias16(bv, L.bias, rloc, i);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) bv[e] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float z[16];
-        read_acc16(z, acc[i][j]);
-        if (full) lse_block<SMOOTH, false>(z, bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
-        else lse_block<SMOOTH, true>(z, bv, i, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
-        // One block at a time: interleaving blocks buys little and spills.
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < 8; ++j) {
+      if (full) lse_column<SMOOTH, false>(acc, j, bias, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      else lse_column<SMOOTH, true>(acc, j, bias, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      // One column at a time keeps the live logits to 32 registers.
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Lanes l and l + 32 hold the same columns (different rows): merge them.
+  // The four lanes l % 16 + 16 g' hold the same tokens (different rows): merge them.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float m2 = __shfl_xor(m[j], 32), d2 = __shfl_xor(d[j], 32);
-    const float s2 = __shfl_xor(sz[j], 32), y2 = __shfl_xor(zy[j], 32);
-    merge_md(m[j], d[j], m2, d2);
-    sz[j] += s2;
-    zy[j] += y2;
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float m2 = __shfl_xor(m[j], mask), d2 = __shfl_xor(d[j], mask);
+      const float s2 = __shfl_xor(sz[j], mask), y2 = __shfl_xor(zy[j], mask);
+      merge_md(m[j], d[j], m2, d2);
+      sz[j] += s2;
+      zy[j] += y2;
+    }
   }
-  // Then the two waves that share columns (wm = 0, 1).
+  // Then the two waves that share tokens (wm = 0, 1).
   lds_f32x4* red = (lds_f32x4*)L.a[0];
-  if (wm == 1 && lane < 32) {
+  if (wm == 1 && lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wn * kWaveTile + 32 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
+    for (int j = 0; j < 8; ++j) red[wn * kWaveTile + 16 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < 16) {
     f32x4* part = (f32x4*)a.partials;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 o = red[wn * kWaveTile + 32 * j + lane];
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 o = red[wn * kWaveTile + 16 * j + lane];
       merge_md(m[j], d[j], o[0], o[1]);
-      const int n = n0 + wn * kWaveTile + 32 * j + lane;
+      const int n = n0 + wn * kWaveTile + 16 * j + lane;
       if (n < a.N) part[(int64_t)ph * a.N + n] = f32x4{m[j], d[j], sz[j] + o[2], zy[j] + o[3]};
     }
   }
@@ -295,94 +280,71 @@ __global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
   a.yv[n] = valid ? (int)t : -1;
 }
 
-// Sum 16 per-lane values over the 32 lanes of each wave half, halving the
-// values held per lane at every step (masks 16, 8, 4, 2), then adding the
-// neighbour (mask 1).  Afterwards lanes l and l ^ 1 hold the total of value
-// e = (l % 32) / 2 (bits 1..4 of the lane index).
-template <int HALF>
-__device__ __forceinline__ void xreduce_step(float (&v)[16], int lane) {
-  constexpr int mask = HALF;   // lane bit that selects the kept half
-  const bool up = (lane & mask) != 0;
+// Sum each of 32 per-lane values over the 16 lanes of its lane group
+// (lane / 16), halving the values a lane holds at every step (masks 8, 4, 2,
+// 1).  Afterwards v[t] (t = 0, 1) of lane l holds the group total of value
+// 2 (l % 16) + t.
+template <int COUNT, int MASK>
+__device__ __forceinline__ void xreduce_step(float (&v)[32], int lane) {
+  const bool up = (lane & MASK) != 0;
 #pragma unroll
-  for (int k = 0; k < HALF / 2; ++k) {
-    const float keep = up ? v[HALF / 2 + k] : v[k];
-    const float send = up ? v[k] : v[HALF / 2 + k];
-    v[k] = keep + __shfl_xor(send, mask);
+  for (int k = 0; k < COUNT / 2; ++k) {
+    const float keep = up ? v[COUNT / 2 + k] : v[k];
+    const float send = up ? v[k] : v[COUNT / 2 + k];
+    v[k] = keep + __shfl_xor(send, MASK);
   }
 }
 
-__device__ __forceinline__ float row_sum16(float (&v)[16], int lane) {
-  xreduce_step<16>(v, lane);
-  xreduce_step<8>(v, lane);
-  xreduce_step<4>(v, lane);
-  xreduce_step<2>(v, lane);
-  return v[0] + __shfl_xor(v[0], 1);
+__device__ __forceinline__ void group_sums16(float (&v)[32], int lane) {
+  xreduce_step<32, 8>(v, lane);
+  xreduce_step<16, 4>(v, lane);
+  xreduce_step<8, 2>(v, lane);
+  xreduce_step<4, 1>(v, lane);
 }
 
-// Store one 32 x 32 block of dlogits (a lane's column n = lane % 32 and rows
-// 8 q + 4 (lane / 32) + r) into the slab, whose rows are tokens with the
-// vocabulary contiguous.  Written directly, every lane would store 8 bytes
-// into a different token row; instead the block goes through a 2 KB LDS
-// buffer of this wave ([token][64 bytes], 16-byte chunk c of row n at
-// c ^ (n & 3)) and comes back as 16 contiguous bytes per lane, four lanes
-// per 64-byte row segment.  Rows nrow + row at or past nlimit are not
-// stored.  Two buffer stores per block, issued by every lane whatever the
-// rows.  The buffer is private to the wave, whose LDS operations complete in
-// order, so no barrier is needed.
-__device__ __forceinline__ void store_block_bf16(lds_t* sb, const float (&dz)[16], __amdgpu_buffer_rsrc_t rslab,
-                                                 int64_t ldS, int nrow, int nlimit, int vcol, int lane) {
-  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-  const int n = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *(lds_u32x2*)(sb + n * 64 + 16 * (q ^ (n & 3)) + 8 * g) =
-        u32x2{pack_bf16x2(dz[4 * q], dz[4 * q + 1]), pack_bf16x2(dz[4 * q + 2], dz[4 * q + 3])};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int row = 16 * k + (lane >> 2), c = lane & 3;
-    const u32x4 v = lds_load16(sb + row * 64 + 16 * (c ^ (row & 3)));
-    const uint32_t off = nrow + row < nlimit ? (uint32_t)(((int64_t)(nrow + row) * ldS + vcol + 8 * c) * 2) : kOOB;
-    __builtin_amdgcn_raw_buffer_store_b128(v, rslab, off, 0, 0);
+// Per-token data of a tile's 256 tokens: thread t fetches token n0 + t
+// before the mainloop (two loads; tokens past N get c = 0 and an infinite
+// log-sum-exp so their dlogits are 0) and publishes it to LDS after it.
+struct TokenTile {
+  f32x4 cf;   // {c (1 + 2 s lse), c eps / V, c (1 - eps), lse log2 e}
+  int y;      // target, -1 if ignored
+  __device__ __forceinline__ void fetch(const BwdLaunch& a, int n0, int tid) {
+    const bool ok = n0 + tid < a.N;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const f32x4*)a.coef + n0);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.yv + n0);
+    const f32x4 c = __builtin_bit_cast(f32x4, buf_load16(rc, ok ? (uint32_t)tid * 16u : kOOB));
+    const int t = (int)__builtin_amdgcn_raw_buffer_load_b32(ry, ok ? (uint32_t)tid * 4u : kOOB, 0, 0);
+    cf = ok ? c : f32x4{0.f, 0.f, 0.f, INFINITY};
+    y = ok ? t : -1;
   }
-}
+  __device__ __forceinline__ void publish(lds_f32x4* lc, __attribute__((address_space(3))) int* ly, int tid) const {
+    lc[tid] = cf;
+    ly[tid] = y;
+  }
+};
 
 // One tile of the recompute kernel.  EXTRA: the vector-memory instructions
 // every wave has issued since this tile's copies started (see
 // gemm_tile_bf16_run).
 template <class T, bool BIAS, bool DB, int EXTRA>
 __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
-                                        const Lds& L, lds_f32* red, lds_t* stage, int tid) {
+                                        const Lds& L, lds_f32* red, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
+                                        lds_t* stage, int tid) {
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
-  const int g = lane >> 5;
+  const int g = lane >> 4;
   const int rloc = wm * kWaveTile + 4 * g;
-  const f32x4* coef = (const f32x4*)a.coef;
   int tm, tn;
   tile_coords(t, G, TM, a.NT, tm, tn);
   const int v0 = vs + tm * kTile, n0 = tn * kTile;
   const int rb = v0 + rloc;
   const bool full = v0 + kTile <= a.V;
-  // Per-token coefficients and targets are fetched before the mainloop,
-  // through descriptors that start at token n0 (rows past N read zero).
-  const __amdgpu_buffer_rsrc_t rcoef = make_rsrc(coef + n0);
-  const __amdgpu_buffer_rsrc_t ryv = make_rsrc(a.yv + n0);
-  f32x4 cf[4];
-  int tcol[4];
-  T* rowp[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nl = wn * kWaveTile + 32 * j + (lane & 31);
-    const bool ok = n0 + nl < a.N;
-    const f32x4 c = __builtin_bit_cast(f32x4, buf_load16(rcoef, ok ? (uint32_t)nl * 16u : kOOB));
-    const int y = (int)__builtin_amdgcn_raw_buffer_load_b32(ryv, ok ? (uint32_t)nl * 4u : kOOB, 0, 0);
-    cf[j] = ok ? c : f32x4{0.f, 0.f, 0.f, INFINITY};
-    tcol[j] = (ok ? y : -1) - rb;
-    rowp[j] = ok ? (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs) + wm * kWaveTile + 4 * g : nullptr;
-  }
-  f32x16 acc[4][4];
+  TokenTile tt;
+  tt.fetch(a, n0, tid);
   BiasTile<T> bt;
   if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
+  Acc acc;
   if constexpr (sizeof(T) == 2) {
     gemm_tile_bf16_run<true, true, EXTRA>(acc, A, B, a.H, L, tid, tc);
     const int tnext = t + gridDim.x;
@@ -394,78 +356,98 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   } else {
     gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
   }
-  if (BIAS) {
-    bt.publish(L.bias, tid);
-    lds_barrier();
-  }
+  tt.publish(ltok, lyv, tid);
+  if (BIAS) bt.publish(L.bias, tid);
+  lds_barrier();
   acc_drain();
   // Slab rows of this tile's tokens, from token n0 on.
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
-  float dbsum[4];
+  float rs[32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float bv[16];
-    if (BIAS) {
-      read_bias16(bv, L.bias, rloc, i);
-    } else {
+  for (int e = 0; e < 32; ++e) rs[e] = 0.f;
+  // 32 x 32 regions (blocks 2I, 2I+1 x 2J, 2J+1): dlogits, db row sums, and
+  // the slab store through this wave's LDS staging buffer ([token][64 bytes],
+  // 16-byte chunk c of row n at c ^ (n & 3)), read back as 16 contiguous
+  // bytes per lane, four lanes per 64-byte row segment.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) bv[e] = 0.f;
-    }
-    float rs[16];
+  for (int J = 0; J < 4; ++J) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+    for (int I = 0; I < 4; ++I) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float z[16];
-      read_acc16(z, acc[i][j]);
-      float dz[16];
+      for (int bj = 0; bj < 2; ++bj) {
+        const int j = 2 * J + bj;
+        const int nl = wn * kWaveTile + 16 * j + (lane & 15);   // token within the tile
+        const f32x4 cf = ltok[nl];
+        const int tcol = lyv[nl] - rb;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(fmaf(z[e] + bv[e], kLog2e, -cf[j][3]));
-        dz[e] = fmaf(cf[j][0], p, -cf[j][1]);
-        if (!full && rb + row_off(i, e) >= a.V) dz[e] = 0.f;
-      }
-      const int tb = tcol[j] - 32 * i;
-      const bool own = (tb >= 0) && (tb < 32) && ((tb & 4) == 0);
-      if (__ballot(own)) {
+        for (int bi = 0; bi < 2; ++bi) {
+          const int i = 2 * I + bi;
+          const f32x4 z = acc_read4(acc[i][j]);
+          const f32x4 bias = BIAS ? read_bias4(L.bias, rloc + 16 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+          float dz[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (own && tb == row_off(0, e)) dz[e] -= cf[j][2];
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(z[r] + bias[r], kLog2e, -cf[3]));
+            dz[r] = fmaf(cf[0], p, -cf[1]);
+            if (!full && rb + 16 * i + r >= a.V) dz[r] = 0.f;
+          }
+          const int tb = tcol - 16 * i;
+          if (__ballot(tb >= 0 && tb < 4)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (tb == r) dz[r] -= cf[2];
+          }
+          if (DB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs[4 * i + r] += dz[r];
+          }
+          if constexpr (sizeof(T) == 2) {
+            typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+            const int n = 16 * bj + (lane & 15);
+            const int c = 2 * bi + (g >> 1);
+            *(lds_u32x2*)(stage + n * 64 + 16 * (c ^ (n & 3)) + 8 * (g & 1)) =
+                u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
+          } else {
+            const int n = n0 + nl;
+            const int v = (v0 - vs) + wm * kWaveTile + 16 * i + 4 * g;
+            if (n < a.N) store4<T>((T*)a.slab + (int64_t)n * a.ldS + v, dz[0], dz[1], dz[2], dz[3]);
+          }
+        }
       }
       if constexpr (sizeof(T) == 2) {
-        store_block_bf16(stage, dz, rslab, a.ldS, wn * kWaveTile + 32 * j, a.N - n0,
-                         (v0 - vs) + wm * kWaveTile + 32 * i, lane);
-      } else if (rowp[j] != nullptr) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          store4<T>(rowp[j] + 32 * i + 8 * q, dz[4 * q], dz[4 * q + 1], dz[4 * q + 2], dz[4 * q + 3]);
-      }
-      if (DB) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rs[e] += dz[e];
+        for (int k = 0; k < 2; ++k) {
+          const int row = 16 * k + (lane >> 2), c = lane & 3;
+          const u32x4 v = lds_load16(stage + row * 64 + 16 * (c ^ (row & 3)));
+          const int nl = wn * kWaveTile + 32 * J + row;
+          const uint32_t off = n0 + nl < a.N
+                                   ? (uint32_t)(((int64_t)nl * a.ldS + (v0 - vs) + wm * kWaveTile + 32 * I + 8 * c) * 2)
+                                   : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rslab, off, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (DB) dbsum[i] = row_sum16(rs, lane);
   }
 
   if (DB) {
-    // Lane l (even) holds the column sums of row e = (l % 32) / 2 of each row
-    // block i; add the two waves that share rows (wn = 0, 1).  The next
-    // tile's mainloop barriers keep this tile's reads of red ahead of the
-    // next tile's writes.
-    const int e = (lane & 31) >> 1;
-    if (wn == 1 && (lane & 1) == 0) {
+    // Rows of this lane group summed over its 16 lanes, then the two waves
+    // that share rows (wn = 0, 1).  The next tile's mainloop barriers keep
+    // this tile's reads of red ahead of the next tile's writes.
+    group_sums16(rs, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wm * kWaveTile + row_off(i, e) + 4 * g] = dbsum[i];
+    for (int tt2 = 0; tt2 < 2; ++tt2) {
+      const int idx = 2 * (lane & 15) + tt2;
+      const int row = wm * kWaveTile + 16 * (idx >> 2) + 4 * g + (idx & 3);
+      if (wn == 1) red[row] = rs[tt2];
     }
     lds_barrier();
-    if (wn == 0 && (lane & 1) == 0) {
+    if (wn == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rl = row_off(i, e) + 4 * g;
-        const int row = v0 + wm * kWaveTile + rl;
-        if (row < a.V) a.dbp[(int64_t)tn * a.ldS + (row - vs)] = dbsum[i] + red[wm * kWaveTile + rl];
+      for (int tt2 = 0; tt2 < 2; ++tt2) {
+        const int idx = 2 * (lane & 15) + tt2;
+        const int rl = wm * kWaveTile + 16 * (idx >> 2) + 4 * g + (idx & 3);
+        if (v0 + rl < a.V) a.dbp[(int64_t)tn * a.ldS + (v0 - vs) + rl] = rs[tt2] + red[rl];
       }
     }
   }
@@ -480,8 +462,10 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
 template <class T, bool BIAS, bool DB>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
   FLCE_LDS(L, T);
-  __shared__ __attribute__((aligned(16))) float red_s[kTile];   // db: the two waves sharing rows
-  __shared__ __attribute__((aligned(16))) char stage_s[4][2048];  // bf16 store staging, one 32 x 32 block per wave
+  __shared__ __attribute__((aligned(16))) float red_s[kTile];       // db: the two waves sharing rows
+  __shared__ __attribute__((aligned(16))) f32x4 tok_s[kTile];       // per-token coefficients
+  __shared__ __attribute__((aligned(16))) int yv_s[kTile];          // per-token targets
+  __shared__ __attribute__((aligned(16))) char stage_s[4][2048];    // bf16 store staging, one per wave
   lds_f32* red = (lds_f32*)red_s;
   const int tid = threadIdx.x, wave = tid >> 6;
   lds_t* stage = (lds_t*)stage_s[wave];
@@ -496,13 +480,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
     tc.start(A, vs + tm * kTile, B, tn * kTile, L, tid);
   }
   // Vector-memory instructions every wave issues between starting a tile's
-  // copies and its mainloop: the per-token loads (8) and the bias fetch, plus,
+  // copies and its mainloop: the per-token loads (2) and the bias fetch, plus,
   // after the first tile, the previous tile's slab stores (32).
-  constexpr int kLoadsVm = 8 + (BIAS ? 1 : 0);
+  constexpr int kLoadsVm = 2 + (BIAS ? 1 : 0);
   constexpr int kStoresVm = 32;
-  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, stage, tid);
+  lds_f32x4* ltok = (lds_f32x4*)tok_s;
+  __attribute__((address_space(3))) int* lyv = (__attribute__((address_space(3))) int*)yv_s;
+  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, stage, tid);
   for (t += gridDim.x; t < G; t += gridDim.x)
-    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, stage, tid);
+    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, stage, tid);
 }
 
 // db[vs + c] = sum over token tiles of the slab's db partials (fixed order),
@@ -529,23 +515,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
   if (a.db != nullptr && tm == 0) slab_db<T>(a, vs, width, v0 + tid);
   const Opnd<T> A{(const T*)a.x, a.H, a.H, a.N};
   const Opnd<T> B{(const T*)a.slab, a.ldS, wpad, a.N};
-  f32x16 acc[4][4];
+  Acc acc;
   gemm_tile<T, false, false>(acc, A, h0, B, v0, a.N, L, tid);
+  acc_drain();
   T* dW = (T*)a.dW;
-  const int g = lane >> 5;
+  const int g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int v = v0 + wn * kWaveTile + 32 * j + (lane & 31);
-    if (v >= width) continue;
+  for (int j = 0; j < 8; ++j) {
+    const int v = v0 + wn * kWaveTile + 16 * j + (lane & 15);
     T* rowp = dW + (int64_t)(vs + v) * a.H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
-        if (h < a.H)
-          store4<T>(rowp + h, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 z = acc_read4(acc[i][j]);
+      const int h = h0 + wm * kWaveTile + 16 * i + 4 * g;
+      if (v < width && h < a.H) store4<T>(rowp + h, z[0], z[1], z[2], z[3]);
+    }
   }
 }
 
@@ -553,8 +537,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
 // whether the fp32 accumulator is written (first slab), read and written
 // (middle slabs), read with dx written in its dtype (last slab), or skipped
 // (a single slab).  The epilogue is branch-free (buffer accesses with
-// out-of-range offsets for rows past N or columns past H) and reads each
-// accumulator block one block ahead of adding and storing it, so the
+// out-of-range offsets for rows past N or columns past H) and reads the
+// accumulator kAhead blocks ahead of adding and storing it, so the
 // read-modify-write does not wait once per 16 bytes.
 template <class T>
 __device__ __forceinline__ void store4_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
@@ -574,7 +558,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   const int h0 = tm * kTile, n0 = tn * kTile;
   const Opnd<T> A{(const T*)a.W + (int64_t)vs * a.H, a.H, a.H, width};
   const Opnd<T> B{(const T*)a.slab, a.ldS, a.N, wpad};
-  f32x16 acc[4][4];
+  Acc acc;
   gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, L, tid);
 
   constexpr bool kRead = MODE == kDxAccum || MODE == kDxLast;
@@ -582,46 +566,35 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   // Descriptors start at token row n0, so offsets stay below 256 * H * 4 bytes.
   const __amdgpu_buffer_rsrc_t racc = make_rsrc(a.dx_acc + (int64_t)n0 * a.H);
   const __amdgpu_buffer_rsrc_t rdx = make_rsrc((const T*)a.dx + (int64_t)n0 * a.H);
-  const int g = lane >> 5;
-  // Byte offset of block (i, j), group q (row n = n0 + nl, column h) for
-  // elements of es bytes; kOOB past N or H.
-  auto boff = [&](int i, int j, int q, uint32_t es) -> uint32_t {
-    const int nl = wn * kWaveTile + 32 * j + (lane & 31);
-    const int h = h0 + wm * kWaveTile + 32 * i + 8 * q + 4 * g;
+  const int g = lane >> 4;
+  // Byte offset of block b = 8 j + i (row n = n0 + nl, columns h .. h + 3)
+  // for elements of es bytes; kOOB past N or H.
+  auto boff = [&](int b, uint32_t es) -> uint32_t {
+    const int i = b & 7, j = b >> 3;
+    const int nl = wn * kWaveTile + 16 * j + (lane & 15);
+    const int h = h0 + wm * kWaveTile + 16 * i + 4 * g;
     return (n0 + nl < a.N && h < a.H) ? (uint32_t)(nl * a.H + h) * es : kOOB;
   };
   acc_drain();
   // Loads run kAhead blocks ahead (12 x 1 KB in flight per wave), about what
   // one CU's share of HBM bandwidth needs while every CU makes its
   // read-modify-write at the same moment.
-  constexpr int kAhead = 3;
-  f32x4 old[kAhead + 1][4];
+  constexpr int kAhead = 12;
+  f32x4 old[kAhead + 1];
   if (kRead) {
 #pragma unroll
-    for (int b = 0; b < kAhead; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) old[b][q] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b & 3, b >> 2, q, 4u)));
+    for (int b = 0; b < kAhead; ++b) old[b] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b, 4u)));
   }
 #pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    const int i = b & 3, j = b >> 2;
+  for (int b = 0; b < 64; ++b) {
     const int bn = b + kAhead;
-    if (kRead && bn < 16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        old[bn % (kAhead + 1)][q] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn & 3, bn >> 2, q, 4u)));
-    }
-    float z[16];
-    read_acc16(z, acc[i][j]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v = {z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
-      if (kRead) v += old[b % (kAhead + 1)][q];
-      if (kAcc) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(i, j, q, 4u), 0, 0);
-      } else {
-        store4_buf<T>(rdx, boff(i, j, q, (uint32_t)sizeof(T)), v);
-      }
+    if (kRead && bn < 64) old[bn % (kAhead + 1)] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn, 4u)));
+    f32x4 v = acc_read4(acc[b & 7][b >> 3]);
+    if (kRead) v += old[b % (kAhead + 1)];
+    if (kAcc) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(b, 4u), 0, 0);
+    } else {
+      store4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)), v);
     }
   }
 }
