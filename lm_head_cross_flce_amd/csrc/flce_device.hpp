@@ -610,7 +610,11 @@ __device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t
   // even) or Y (s odd).
   const int KT = (K + kStageK - 1) / kStageK;
   const int KTp = KT <= 4 ? 4 : (KT + 3) & ~3;
-  const int KF = K / kStageK;   // stages wholly inside K
+  // Stages wholly inside both operands' valid K: their copies skip the
+  // bounds check.  An operand's valid K can be shorter than the loop's K (the
+  // input-gradient product runs K to a whole tile past the last vocabulary
+  // row); stages past it take the checked path, which reads zeros.
+  const int KF = min(K, min(A.kext, B.kext)) / kStageK;
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<W0>());
   __builtin_amdgcn_s_barrier();
   Frag X, Y;

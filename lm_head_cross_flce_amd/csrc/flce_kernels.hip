@@ -280,26 +280,31 @@ __global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
   a.yv[n] = valid ? (int)t : -1;
 }
 
-// Sum each of 32 per-lane values over the 16 lanes of its lane group
-// (lane / 16), halving the values a lane holds at every step (masks 8, 4, 2,
-// 1).  Afterwards v[t] (t = 0, 1) of lane l holds the group total of value
-// 2 (l % 16) + t.
-template <int COUNT, int MASK>
-__device__ __forceinline__ void xreduce_step(float (&v)[32], int lane) {
+// Sums over the 16 lanes of a lane group (lane / 16).  A step halves the
+// values a lane holds: DPP control CTRL pairs every lane with one whose
+// lane-id bit MASK differs and whose higher bits agree (row mirror for bit 3,
+// half-row mirror for bit 2, quad permutations for bits 1 and 0), and the
+// lane with the bit set keeps the upper half.
+template <int COUNT, int MASK, int CTRL>
+__device__ __forceinline__ void xreduce_step(float (&v)[8], int lane) {
   const bool up = (lane & MASK) != 0;
 #pragma unroll
   for (int k = 0; k < COUNT / 2; ++k) {
     const float keep = up ? v[COUNT / 2 + k] : v[k];
     const float send = up ? v[k] : v[COUNT / 2 + k];
-    v[k] = keep + __shfl_xor(send, MASK);
+    v[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), CTRL,
+                                                                       0xf, 0xf, false));
   }
 }
 
-__device__ __forceinline__ void group_sums16(float (&v)[32], int lane) {
-  xreduce_step<32, 8>(v, lane);
-  xreduce_step<16, 4>(v, lane);
-  xreduce_step<8, 2>(v, lane);
-  xreduce_step<4, 1>(v, lane);
+// Group total of value q = (lane % 16) / 2 of 8 per-lane values, returned to
+// lanes 2q and 2q + 1 of every group.
+__device__ __forceinline__ float group_sum8(float (&v)[8], int lane) {
+  xreduce_step<8, 8, 0x140>(v, lane);   // row_mirror: l <-> 15 - l
+  xreduce_step<4, 4, 0x141>(v, lane);   // row_half_mirror: l <-> l ^ 7
+  xreduce_step<2, 2, 0x4e>(v, lane);    // quad_perm [2, 3, 0, 1]: l <-> l ^ 2
+  return v[0] + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[0]), 0xb1, 0xf,
+                                                                      0xf, false));   // l <-> l ^ 1
 }
 
 // Per-token data of a tile's 256 tokens: thread t fetches token n0 + t
@@ -339,7 +344,6 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   tile_coords(t, G, TM, a.NT, tm, tn);
   const int v0 = vs + tm * kTile, n0 = tn * kTile;
   const int rb = v0 + rloc;
-  const bool full = v0 + kTile <= a.V;
   TokenTile tt;
   tt.fetch(a, n0, tid);
   BiasTile<T> bt;
@@ -360,19 +364,25 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   if (BIAS) bt.publish(L.bias, tid);
   lds_barrier();
   acc_drain();
+  // Vocabulary rows past V read W and b as zeros, so their dlogits are finite
+  // and are stored unmasked: the weight-gradient and bias kernels drop those
+  // columns and the input-gradient kernel multiplies them by zero rows of W.
   // Slab rows of this tile's tokens, from token n0 on.
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
-  float rs[32];
+  // 32-row bands I of the wave's rows, one 32 x 32 region (blocks 2I, 2I+1 x
+  // 2J, 2J+1) at a time: dlogits, the band's db row sums, and the slab store
+  // through this wave's LDS staging buffer ([token][64 bytes], 16-byte chunk c
+  // of row n at c ^ (n & 3)), read back as 16 contiguous bytes per lane, four
+  // lanes per 64-byte row segment.  A band's row sums are reduced over the
+  // lane group as soon as the band is done, so few stay live.
+  float dbs[4];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) rs[e] = 0.f;
-  // 32 x 32 regions (blocks 2I, 2I+1 x 2J, 2J+1): dlogits, db row sums, and
-  // the slab store through this wave's LDS staging buffer ([token][64 bytes],
-  // 16-byte chunk c of row n at c ^ (n & 3)), read back as 16 contiguous
-  // bytes per lane, four lanes per 64-byte row segment.
+  for (int I = 0; I < 4; ++I) {
+    float rs[8];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+    for (int e = 0; e < 8; ++e) rs[e] = 0.f;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int J = 0; J < 4; ++J) {
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj) {
         const int j = 2 * J + bj;
@@ -389,7 +399,6 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(z[r] + bias[r], kLog2e, -cf[3]));
             dz[r] = fmaf(cf[0], p, -cf[1]);
-            if (!full && rb + 16 * i + r >= a.V) dz[r] = 0.f;
           }
           const int tb = tcol - 16 * i;
           if (__ballot(tb >= 0 && tb < 4)) {
@@ -399,7 +408,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
           }
           if (DB) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rs[4 * i + r] += dz[r];
+            for (int r = 0; r < 4; ++r) rs[4 * bi + r] += dz[r];
           }
           if constexpr (sizeof(T) == 2) {
             typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
@@ -428,26 +437,27 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (DB) dbs[I] = group_sum8(rs, lane);
   }
 
   if (DB) {
-    // Rows of this lane group summed over its 16 lanes, then the two waves
-    // that share rows (wn = 0, 1).  The next tile's mainloop barriers keep
-    // this tile's reads of red ahead of the next tile's writes.
-    group_sums16(rs, lane);
+    // Lanes 2q, 2q + 1 of group g hold band I's total of value q = 4 bi + r,
+    // wave row 32 I + 16 bi + 4 g + r.  The two waves that share rows (wn = 0,
+    // 1) add through LDS; the next tile's mainloop barriers keep this tile's
+    // reads of red ahead of the next tile's writes.
+    const int q = (lane & 15) >> 1;
+    const bool lead = (lane & 1) == 0;
 #pragma unroll
-    for (int tt2 = 0; tt2 < 2; ++tt2) {
-      const int idx = 2 * (lane & 15) + tt2;
-      const int row = wm * kWaveTile + 16 * (idx >> 2) + 4 * g + (idx & 3);
-      if (wn == 1) red[row] = rs[tt2];
+    for (int I = 0; I < 4; ++I) {
+      const int row = wm * kWaveTile + 32 * I + 16 * (q >> 2) + 4 * g + (q & 3);
+      if (wn == 1 && lead) red[row] = dbs[I];
     }
     lds_barrier();
-    if (wn == 0) {
+    if (wn == 0 && lead) {
 #pragma unroll
-      for (int tt2 = 0; tt2 < 2; ++tt2) {
-        const int idx = 2 * (lane & 15) + tt2;
-        const int rl = wm * kWaveTile + 16 * (idx >> 2) + 4 * g + (idx & 3);
-        if (v0 + rl < a.V) a.dbp[(int64_t)tn * a.ldS + (v0 - vs) + rl] = rs[tt2] + red[rl];
+      for (int I = 0; I < 4; ++I) {
+        const int rl = wm * kWaveTile + 32 * I + 16 * (q >> 2) + 4 * g + (q & 3);
+        if (v0 + rl < a.V) a.dbp[(int64_t)tn * a.ldS + (v0 - vs) + rl] = dbs[I] + red[rl];
       }
     }
   }

@@ -194,3 +194,41 @@ def test_module_frozen_weight_and_none_reduction():
     assert rel(loss.detach().cpu().numpy().astype(np.float64), f.loss) <= LOSS_RTOL
     assert rel(to_f64(x.grad), bw.dx) <= GRAD_RTOL["bf16"]
     assert W.grad is None
+
+
+def _nan_guarded(a, extra_rows):
+    """``a`` copied to the front of a buffer whose remaining ``extra_rows`` rows are NaN."""
+    flat = a.reshape(-1)
+    row = a.shape[1] if a.dim() == 2 else 1
+    buf = torch.full((flat.numel() + extra_rows * row,), float("nan"), dtype=a.dtype, device=a.device)
+    buf[: flat.numel()] = flat
+    return buf[: flat.numel()].view(a.shape)
+
+
+@pytest.mark.parametrize("name", ["sum_bias", "c3_small", "f32_none", "bf16_v_lt_tile"])
+def test_no_reads_past_operands_or_of_unwritten_memory(name):
+    # x, W and b end where NaN rows begin; the workspaces and the gradient
+    # outputs start as NaN bytes.  A read past an operand's last row, or of
+    # workspace or output memory that the library did not write first, would
+    # carry NaN into the results.
+    inp = inputs(name)
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    x, W = _nan_guarded(x, 300), _nan_guarded(W, 300)
+    b = _nan_guarded(b, 300) if b is not None else None
+    fb, bb = F.flce_workspace_size(w.N, w.H, w.V, x.dtype, b is not None, w.reduction)
+    wsf = torch.full((max(fb, 1),), 0xFF, dtype=torch.uint8, device=x.device)
+    wsb = torch.full((max(bb, 1),), 0xFF, dtype=torch.uint8, device=x.device)
+    out = (torch.full_like(x, float("nan")), torch.full_like(W, float("nan")),
+           torch.full_like(b, float("nan")) if b is not None else None)
+    print(f"[gpu] NaN-guarded operands {name}", flush=True)
+    loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                                   workspace=wsf)
+    dx, dW, db = F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                 w.reduction, workspace=wsb, out=out)
+    torch.cuda.synchronize()
+    got = {"loss": loss.cpu().numpy().astype(np.float64), "lse": lse.cpu().numpy().astype(np.float64),
+           "n_valid": int(nv.cpu().item()), "dx": to_f64(dx), "dW": to_f64(dW),
+           "db": None if db is None else to_f64(db)}
+    f, bw = oracle(name)
+    check(name, got, f, bw)
