@@ -36,6 +36,8 @@ constexpr int kTile = 256;                  // BM = BN
 constexpr int kWaveTile = 128;
 constexpr int kRowBytes = 144;              // fp32 LDS rows: 128 B of K + 16 B pad (bank spread)
 constexpr int kBufBytes = kTile * kRowBytes;
+constexpr int kStageK = 32;                 // bf16: K per MFMA stage
+constexpr int kBlockK = 64;                 // bf16: K per copy block (two stages)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
@@ -69,36 +71,29 @@ __device__ __forceinline__ u32x4 lds_load16(const lds_t* p) { return *(const lds
 
 __device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
 
-// Operand buffers: bf16 tiles use a ring of four 16 KB stages per operand; fp32
-// tiles use two 36 KB stages per operand (a[0..1], b[0..1]).  Each buffer is its
-// own __shared__ object (declared by FLCE_LDS in every kernel) so the compiler
-// can tell that reads of one buffer never overlap a copy into another and need
+// Operand buffers: two per operand, 32 KB for bf16 (one 64-deep K block) and
+// 36 KB for fp32 (one padded 32-deep stage).  Each buffer is its own
+// __shared__ object (declared by FLCE_LDS in every kernel) so the compiler can
+// tell that reads of one buffer never overlap a copy into another and need
 // not wait for it.
 typedef __attribute__((address_space(3))) float lds_f32;
 
 struct Lds {
-  lds_t* a[4];
-  lds_t* b[4];
+  lds_t* a[2];
+  lds_t* b[2];
   lds_f32* bias;   // 256 fp32: the bias of the current tile's rows
 };
 template <class T> struct LdsSize {
-  static constexpr int kBig = sizeof(T) == 2 ? 16384 : kBufBytes;  // stages 0, 1
-  static constexpr int kSmall = sizeof(T) == 2 ? 16384 : 16;       // stages 2, 3 (bf16 only)
+  static constexpr int kBuf = sizeof(T) == 2 ? kTile * kBlockK * 2 : kBufBytes;
 };
 #define FLCE_LDS(name, T)                                                                          \
-  __shared__ __attribute__((aligned(16))) char name##_a0[LdsSize<T>::kBig];                        \
-  __shared__ __attribute__((aligned(16))) char name##_a1[LdsSize<T>::kBig];                        \
-  __shared__ __attribute__((aligned(16))) char name##_a2[LdsSize<T>::kSmall];                      \
-  __shared__ __attribute__((aligned(16))) char name##_a3[LdsSize<T>::kSmall];                      \
-  __shared__ __attribute__((aligned(16))) char name##_b0[LdsSize<T>::kBig];                        \
-  __shared__ __attribute__((aligned(16))) char name##_b1[LdsSize<T>::kBig];                        \
-  __shared__ __attribute__((aligned(16))) char name##_b2[LdsSize<T>::kSmall];                      \
-  __shared__ __attribute__((aligned(16))) char name##_b3[LdsSize<T>::kSmall];                      \
+  __shared__ __attribute__((aligned(16))) char name##_a0[LdsSize<T>::kBuf];                        \
+  __shared__ __attribute__((aligned(16))) char name##_a1[LdsSize<T>::kBuf];                        \
+  __shared__ __attribute__((aligned(16))) char name##_b0[LdsSize<T>::kBuf];                        \
+  __shared__ __attribute__((aligned(16))) char name##_b1[LdsSize<T>::kBuf];                        \
   __shared__ __attribute__((aligned(16))) float name##_bias[kTile];                                \
   const Lds name {                                                                                 \
-    {(lds_t*)name##_a0, (lds_t*)name##_a1, (lds_t*)name##_a2, (lds_t*)name##_a3},                  \
-    {(lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3},                  \
-    (lds_f32*)name##_bias                                                                          \
+    {(lds_t*)name##_a0, (lds_t*)name##_a1}, {(lds_t*)name##_b0, (lds_t*)name##_b1}, (lds_f32*)name##_bias \
   }
 
 // Workgroup barrier that waits only for this wave's LDS operations, not for
@@ -339,28 +334,31 @@ __device__ __forceinline__ void gemm_tile_f32(Acc& acc, const Opnd<float>& A, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 mainloop.  K advances in stages of 32 through a ring of four LDS
-// buffers per operand; each stage is copied three stages ahead by the buffer
-// unit (buffer_load ... lds, 16 bytes per lane, each wave instruction filling
-// 1 KB of LDS contiguously), so no registers or LDS-write instructions carry
-// operands.
+// bf16 mainloop.  The MFMAs consume K in stages of 32; the buffer unit copies
+// K in blocks of 64 (two stages) into two LDS buffers per operand
+// (buffer_load ... lds, 16 bytes per lane, each wave instruction filling 1 KB
+// of LDS contiguously), so no registers or LDS-write instructions carry
+// operands.  Block b + 1 is copied while block b is computed, and one wait
+// plus one barrier per block (after its second stage) both publishes block
+// b + 1 and frees block b's buffer for block b + 2.
 //
-// K-contiguous operand, one stage = 256 rows x 32 k: LDS rows of 64 bytes;
-// 16-byte chunk p of row r holds logical K chunk p ^ ((r >> 1) & 3).  A
-// fragment (16 rows, lane l: row l % 16, K chunk l / 16) is one 16-byte read
-// per lane, free of bank conflicts on gfx950's 64 banks (measured).
+// K-contiguous operand, one block = 256 rows x 64 k: LDS rows of 128 bytes,
+// so every copy instruction fetches whole 128-byte lines (8 rows x 8 chunks);
+// 16-byte chunk p of row r holds logical K chunk p ^ (r & 7).  A fragment (16
+// rows, lane l: row l % 16, K chunk 4 h + l / 16 in stage half h) is one
+// 16-byte read per lane, and every 8 consecutive lanes cover the 8 chunk
+// positions of a 128-byte bank cycle, so the reads are free of bank conflicts.
 //
-// M-contiguous operand, one stage = 32 k x 256 m in its global layout: LDS
+// M-contiguous operand, one block = 64 k x 256 m in its global layout: LDS
 // rows (one per k) of 512 bytes; chunk p of row k holds logical chunk
 // p ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16, which within
 // each 16-lane group hands lane l element l % 4 of the 8-byte pieces
 // addressed by lanes 4 e + l / 4 (e = 0..3): lane j of group G addresses row
-// k = 8 G + 4 h + j / 4 at columns m0 + 4 (j % 4) .. + 3, so lane l receives
-// column m0 + l % 16 at k = 8 G + 4 h + e, the K order of a 16-byte read of
-// a K-contiguous row; two reads (h = 0, 1) give the lane its 8 values.
+// k = 8 G + 4 h + j / 4 (plus 32 in a block's second stage) at columns
+// m0 + 4 (j % 4) .. + 3, so lane l receives column m0 + l % 16 at
+// k = 8 G + 4 h + e, the K order of a 16-byte read of a K-contiguous row; two
+// reads (h = 0, 1) give the lane its 8 values.
 // ---------------------------------------------------------------------------
-
-constexpr int kStageK = 32;
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -371,42 +369,41 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint
 // outstanding and all LDS operations are done.
 template <int N> constexpr int waitcnt_vm_lgkm0() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
 
-// Copies of one operand: 16 wave instructions per stage, 4 per wave
-// (q = 0..3, instruction index 4 q + wave).  issue(q) fills them one at a
-// time so a stage body can spread them between MFMAs; TAIL masks K chunks
-// past K (stages that are not wholly inside K).
+// Copies of one operand: 32 wave instructions per block, 8 per wave (q =
+// 0..7, instruction index 4 q + wave).  issue(q) fills them one at a time so
+// a stage body can spread them between MFMAs; TAIL masks K chunks past the
+// operand's valid K (blocks that are not wholly inside it).
 template <bool KCONTIG> struct Dma;
 
-// K-contiguous: instruction idx fills rows 16 idx .. 16 idx + 15.
+// K-contiguous: instruction idx fills rows 8 idx .. 8 idx + 7; lane l takes
+// row 8 idx + l / 8 and LDS chunk l % 8, which holds global chunk
+// (l % 8) ^ (l / 8).
 template <> struct Dma<true> {
-  uint32_t off[4];
+  uint32_t off[8];
   const uint16_t* base;
-  int64_t ld;
   int wave;
   __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = o.p + (int64_t)m0 * o.ld;
-    ld = o.ld;
+    const int c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 16 * (4 * q + wave) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 1) & 3);
+    for (int q = 0; q < 8; ++q) {
+      const int row = 8 * (4 * q + wave) + (lane >> 3);
       off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int k0) const { return make_rsrc(base + k0); }
   template <bool TAIL>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kleft, lds_t* buf, int lane, int q) const {
-    const int row = 16 * (4 * q + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int c = (lane & 7) ^ (lane >> 3);
     dma16(rs, buf + (4 * q + wave) * 1024, (!TAIL || 8 * c < kleft) ? off[q] : kOOB);
   }
 };
 
 // M-contiguous: instruction idx fills k rows 2 idx and 2 idx + 1.
 template <> struct Dma<false> {
-  uint32_t off[4];
+  uint32_t off[8];
   const uint16_t* base;
   int64_t ld;
   int wave;
@@ -416,7 +413,7 @@ template <> struct Dma<false> {
     base = o.p + m0;
     ld = o.ld;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       const int row = 2 * (4 * q + wave) + (lane >> 5);
       const int c = (lane & 31) ^ (4 * (row & 3));
       off[q] = (m0 + 8 * c < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
@@ -430,25 +427,27 @@ template <> struct Dma<false> {
   }
 };
 
-// Per-lane LDS addresses of one operand's fragments.
+// Per-lane LDS addresses of one operand's fragments; PAR is the stage's half
+// of its K block.
 template <bool KCONTIG> struct FragAddr;
 
 template <> struct FragAddr<true> {
   static constexpr int kReads = 1;   // LDS read instructions per 16-row block
-  int base;                          // block i adds 16 * 64 * i
+  int base[2];                       // per block half; block i adds 16 * 128 * i
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int rl = lane & 15, c = lane >> 4;
-    base = (wbase + rl) * 64 + 16 * (c ^ ((rl >> 1) & 3));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) base[h] = (wbase + rl) * 128 + 16 * ((4 * h + c) ^ (rl & 7));
   }
-  template <int H>
+  template <int PAR, int H>
   __device__ __forceinline__ void read(u32x4& f, const lds_t* buf, int i) const {
-    f = lds_load16(buf + base + 1024 * i);
+    f = lds_load16(buf + base[PAR] + 2048 * i);
   }
 };
 
 template <> struct FragAddr<false> {
   static constexpr int kReads = 2;
-  int a[2][8];   // per half h and block i
+  int a[2][8];   // per read h and block i, for the block's first stage
   __device__ __forceinline__ void init(int wbase, int lane) {
     const int j = lane & 15, G = lane >> 4;
 #pragma unroll
@@ -460,11 +459,13 @@ template <> struct FragAddr<false> {
         a[h][i] = k * 512 + 16 * ((m >> 3) ^ (4 * (k & 3))) + 2 * (m & 7);
       }
   }
-  // Half H of block i: elements 2H, 2H + 1 of the fragment's dwords.
-  template <int H>
+  // Read H of block i: elements 2H, 2H + 1 of the fragment's dwords.  The
+  // block's second stage lies 32 rows (16 KB) further; k & 3 is unchanged.
+  template <int PAR, int H>
   __device__ __forceinline__ void read(u32x4& f, const lds_t* buf, int i) const {
     typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + a[H][i])));
+    const u32x2 v = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + 16384 * PAR + a[H][i])));
     f[2 * H] = v[0];
     f[2 * H + 1] = v[1];
   }
@@ -477,73 +478,89 @@ struct Frag {
 
 // One read instruction of a stage's fragments, by index: A blocks 0..3 come
 // first (kReads each), then B blocks 0..7, then A blocks 4..7.
-template <bool AK, bool BK>
+template <bool AK, bool BK, int PAR>
 __device__ __forceinline__ void frag_read(Frag& f, const FragAddr<AK>& fa, const FragAddr<BK>& fb, const lds_t* bA,
                                           const lds_t* bB, int idx) {
   constexpr int RA = FragAddr<AK>::kReads, RB = FragAddr<BK>::kReads;
   if (idx < 4 * RA) {
     const int i = idx / RA;
-    if (RA == 1 || (idx % RA) == 0) fa.template read<0>(f.a[i], bA, i);
-    else fa.template read<1>(f.a[i], bA, i);
+    if (RA == 1 || (idx % RA) == 0) fa.template read<PAR, 0>(f.a[i], bA, i);
+    else fa.template read<PAR, 1>(f.a[i], bA, i);
   } else if (idx < 4 * RA + 8 * RB) {
     const int t = idx - 4 * RA, j = t / RB;
-    if (RB == 1 || (t % RB) == 0) fb.template read<0>(f.b[j], bB, j);
-    else fb.template read<1>(f.b[j], bB, j);
+    if (RB == 1 || (t % RB) == 0) fb.template read<PAR, 0>(f.b[j], bB, j);
+    else fb.template read<PAR, 1>(f.b[j], bB, j);
   } else {
     const int t = idx - 4 * RA - 8 * RB, i = 4 + t / RA;
-    if (RA == 1 || (t % RA) == 0) fa.template read<0>(f.a[i], bA, i);
-    else fa.template read<1>(f.a[i], bA, i);
+    if (RA == 1 || (t % RA) == 0) fa.template read<PAR, 0>(f.a[i], bA, i);
+    else fa.template read<PAR, 1>(f.a[i], bA, i);
   }
 }
 
-// One stage body, for the stage held in ring slot CUR.  Its 64 MFMAs per wave
-// are split by A block: the first 32 slots run the previous stage's blocks
-// i = 4..7 (fragments P) while this stage's A 0..3 and B 0..7 fragments are
-// read and the stage three ahead is copied (one instruction per MFMA slot);
-// the next 32 run this stage's blocks i = 0..3 while A 4..7 are read.  Then
-// one wait (copies of the next stage done; VMW newer memory operations may
-// stay in flight) and one barrier.  FIRST: the tile's first stage (no previous
-// MFMAs; blocks 0..3 start from zero); SECOND: blocks 4..7 start from zero.
-// Every instruction slot ends in a scheduling barrier, which pins this order.
-template <int CUR, bool FIRST, bool SECOND, bool AK, bool BK, int VMW, bool TAIL>
+// Instruction plan of one stage body: 32 + 32 MFMA slots per wave.  The first
+// 32 run the previous stage's blocks i = 4..7 while this stage's A 0..3 and
+// B 0..7 fragments are read (kR1 reads); the next 32 run this stage's blocks
+// i = 0..3 while A 4..7 are read (kR2 reads).  A block's first stage (PAR 0)
+// also issues the 16 copies of the next block, as early as it can: copies
+// and first reads alternate from slot 0, and copies that do not fit in the
+// first half follow the second half's reads.  Slot kinds: 0 none, 1 read,
+// 2 copy; idx*() gives the read or copy index.
+template <int RA, int RB, int PAR> struct StagePlan {
+  static constexpr int kR1 = 4 * RA + 8 * RB, kR2 = 4 * RA;
+  static constexpr int kC = PAR == 0 ? 16 : 0;
+  static constexpr int kC1 = kC < 32 - kR1 ? kC : 32 - kR1;   // copies in the first half
+  static constexpr int kMix = kC1 < kR1 ? kC1 : kR1;          // alternating copy/read pairs
+  static_assert(kR1 <= 32 && kR2 + (kC - kC1) <= 32, "at most one read or copy per MFMA slot");
+  static constexpr int kind1(int k) {
+    return k < 2 * kMix ? ((k & 1) ? 1 : 2)
+                        : (kR1 > kMix ? (k - 2 * kMix < kR1 - kMix ? 1 : 0) : (k - 2 * kMix < kC1 - kMix ? 2 : 0));
+  }
+  static constexpr int idx1(int k) { return k < 2 * kMix ? (k >> 1) : kMix + (k - 2 * kMix); }
+  static constexpr int kind2(int k) { return k < kR2 ? 1 : (k - kR2 < kC - kC1 ? 2 : 0); }
+  static constexpr int idx2(int k) { return k < kR2 ? kR1 + k : kC1 + (k - kR2); }
+};
+
+// One stage body: half PAR of the K block in buffer BUF.  A PAR 0 stage
+// copies the block at k_copy into the other buffer; a PAR 1 stage ends with
+// the block's wait (the next block's copies done; VMW newer memory
+// operations may stay in flight) and barrier.  FIRST: the tile's first stage
+// (no previous MFMAs; blocks 0..3 start from zero); SECOND: blocks 4..7
+// start from zero.  Every instruction slot ends in a scheduling barrier,
+// which pins this order.
+template <int PAR, int BUF, bool FIRST, bool SECOND, bool AK, bool BK, int VMW, bool TAIL>
 __device__ __forceinline__ void stage_bf16(Acc& acc, Frag& P, Frag& C, const FragAddr<AK>& fa,
                                            const FragAddr<BK>& fb, const Lds& L, int lane, const Opnd<uint16_t>& A,
                                            const Opnd<uint16_t>& B, const Dma<AK>& da, const Dma<BK>& db,
                                            int k_copy) {
-  constexpr int NXT = (CUR + 3) & 3;
-  constexpr int RA = FragAddr<AK>::kReads, RB = FragAddr<BK>::kReads;
-  constexpr int kReads1 = 4 * RA + 8 * RB;          // reads in the first half
-  constexpr int kSlots1 = kReads1 + 8;              // plus 8 copy instructions
-  static_assert(kSlots1 <= 32, "first half holds at most one read or copy per MFMA");
-  const lds_t* bA = L.a[CUR];
-  const lds_t* bB = L.b[CUR];
+  typedef StagePlan<FragAddr<AK>::kReads, FragAddr<BK>::kReads, PAR> Plan;
+  const lds_t* bA = L.a[BUF];
+  const lds_t* bB = L.b[BUF];
   const __amdgpu_buffer_rsrc_t rsa = da.rsrc(k_copy);
   const __amdgpu_buffer_rsrc_t rsb = db.rsrc(k_copy);
   const int kla = A.kext - k_copy, klb = B.kext - k_copy;
+  auto copy = [&](int q) {
+    if (q < 8) da.template issue<TAIL>(rsa, kla, L.a[BUF ^ 1], lane, q);
+    else db.template issue<TAIL>(rsb, klb, L.b[BUF ^ 1], lane, q - 8);
+  };
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     if (!FIRST) mfma16<SECOND>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
-    // reads fill the slots before the copies; copies take every other slot
-    // after that while there is room, else the next free slots
-    constexpr int kGap = (32 - kReads1) >= 16 ? 2 : 1;
-    if (k < kReads1) {
-      frag_read<AK, BK>(C, fa, fb, bA, bB, k);
-    } else if ((k - kReads1) % kGap == 0 && (k - kReads1) / kGap < 8) {
-      const int q = (k - kReads1) / kGap;
-      if (q < 4) da.template issue<TAIL>(rsa, kla, L.a[NXT], lane, q);
-      else db.template issue<TAIL>(rsb, klb, L.b[NXT], lane, q - 4);
-    }
+    if (Plan::kind1(k) == 1) frag_read<AK, BK, PAR>(C, fa, fb, bA, bB, Plan::idx1(k));
+    else if (Plan::kind1(k) == 2) copy(Plan::idx1(k));
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     mfma16<FIRST>(acc[k / 8][k % 8], C.a[k / 8], C.b[k % 8]);
-    if (k < 4 * RA) frag_read<AK, BK>(C, fa, fb, bA, bB, kReads1 + k);
+    if (Plan::kind2(k) == 1) frag_read<AK, BK, PAR>(C, fa, fb, bA, bB, Plan::idx2(k));
+    else if (Plan::kind2(k) == 2) copy(Plan::idx2(k));
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VMW>());
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PAR == 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VMW>());
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // The upper half (blocks 4..7) of a tile's last stage.
@@ -556,10 +573,11 @@ __device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
   }
 }
 
-// Copy state of one bf16 tile.  start() issues the copies of the first three
-// stages; it may run while the previous tile's epilogue is still working, as
-// long as every wave has finished that tile's mainloop (whose last barrier
-// follows the last fragment read of every slot).
+// Copy state of one bf16 tile.  start() issues the copies of the first K
+// block into buffer 0; it may run while the previous tile's epilogue is still
+// working, as long as every wave has finished that tile's mainloop (whose
+// last barrier follows its last fragment read and the completion of its
+// copies).
 template <bool AK, bool BK> struct TileCopy {
   Dma<AK> da;
   Dma<BK> db;
@@ -569,32 +587,27 @@ template <bool AK, bool BK> struct TileCopy {
     db.init(B, n0, tid);
     const int lane = tid & 63;
     // Copies past K read zeros (out-of-range offsets), so the stage bodies
-    // need no branches; the ones still in flight are drained at the end.
+    // need no branches.
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
-      const int k0 = st * kStageK;
+    for (int q = 0; q < 8; ++q) da.template issue<true>(da.rsrc(0), A.kext, L.a[0], lane, q);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) da.template issue<true>(da.rsrc(k0), A.kext - k0, L.a[st], lane, q);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) db.template issue<true>(db.rsrc(k0), B.kext - k0, L.b[st], lane, q);
-    }
+    for (int q = 0; q < 8; ++q) db.template issue<true>(db.rsrc(0), B.kext, L.b[0], lane, q);
   }
 };
 
-// Mainloop of a tile whose copies TileCopy::start has issued.  EXTRA is a
-// lower bound on the vector-memory instructions each wave issued after
+// Mainloop of a tile whose first block TileCopy::start has issued.  EXTRA is
+// a lower bound on the vector-memory instructions each wave issued after
 // start() and before this call (an epilogue's stores and loads): vmcnt counts
-// stores too, in issue order, so the waits for stages 0-2, whose copies are
-// older than those instructions, allow EXTRA more to stay in flight instead
-// of draining the epilogue's stores.  Counting too few only costs a stall;
-// every counted instruction must be issued unconditionally by every wave.
-// Returns with all copies complete; the accumulators need acc_drain() before
-// they are read.
+// stores too, in issue order, so the wait for the first block, whose copies
+// are older than those instructions, allows EXTRA more to stay in flight
+// instead of draining the epilogue's stores.  Counting too few only costs a
+// stall; every counted instruction must be issued unconditionally by every
+// wave.  Returns with all copies complete; the accumulators need acc_drain()
+// before they are read.
 template <bool AK, bool BK, int EXTRA = 0>
 __device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, int K,
                                                    const Lds& L, int tid, const TileCopy<AK, BK>& tc) {
-  static_assert(EXTRA >= 0 && 16 + EXTRA <= 63, "vmcnt holds at most 63");
-  constexpr int W0 = 16 + EXTRA;
+  static_assert(EXTRA >= 0 && EXTRA <= 63, "vmcnt holds at most 63");
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Dma<AK>& da = tc.da;
   const Dma<BK>& db = tc.db;
@@ -602,45 +615,43 @@ __device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t
   FragAddr<BK> fb;
   fa.init(wm * 128, lane);
   fb.init(wn * 128, lane);
-  // Stages run in groups of four (one per ring slot); the count is rounded
-  // up to a multiple of four, the extra stages reading zeros (their copies
-  // lie past K).  The loops then hold whole groups and no stage body is
-  // conditional: the register allocator keeps the tied accumulators in place
-  // only along straight-line paths.  Stage s keeps its fragments in X (s
-  // even) or Y (s odd).
+  // Stages run in groups of four (two blocks, one per buffer); the count is
+  // rounded up to a multiple of four, the extra stages reading zeros (their
+  // copies lie past K).  The loops then hold whole groups and no stage body
+  // is conditional: the register allocator keeps the tied accumulators in
+  // place only along straight-line paths.  Stage s keeps its fragments in X
+  // (s even) or Y (s odd).
   const int KT = (K + kStageK - 1) / kStageK;
   const int KTp = KT <= 4 ? 4 : (KT + 3) & ~3;
-  // Stages wholly inside both operands' valid K: their copies skip the
+  // Blocks wholly inside both operands' valid K: their copies skip the
   // bounds check.  An operand's valid K can be shorter than the loop's K (the
   // input-gradient product runs K to a whole tile past the last vocabulary
-  // row); stages past it take the checked path, which reads zeros.
-  const int KF = min(K, min(A.kext, B.kext)) / kStageK;
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<W0>());
+  // row); blocks past it take the checked path, which reads zeros.
+  const int KBF = min(K, min(A.kext, B.kext)) / kBlockK;
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<EXTRA>());
   __builtin_amdgcn_s_barrier();
   Frag X, Y;
-  // Stages 0 and 1 end by waiting for the copies of stages 1 and 2, which
-  // start() issued (EXTRA newer instructions may be in flight); from stage 2
-  // on, the waited-for copies are the body's own.
-  stage_bf16<0, true, false, AK, BK, W0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 3 * kStageK);
-  stage_bf16<1, false, true, AK, BK, W0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 4 * kStageK);
-  stage_bf16<2, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 5 * kStageK);
-  stage_bf16<3, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 6 * kStageK);
+  stage_bf16<0, 0, true, false, AK, BK, 0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 1 * kBlockK);
+  stage_bf16<1, 0, false, true, AK, BK, 0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
+  stage_bf16<0, 1, false, false, AK, BK, 0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, 2 * kBlockK);
+  stage_bf16<1, 1, false, false, AK, BK, 0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
   int kt = 4;
-  // copies of stages kt + 3 .. kt + 6 wholly inside K: no masking
-  for (; kt + 7 <= KF; kt += 4) {
-    stage_bf16<0, false, false, AK, BK, 16, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 3) * kStageK);
-    stage_bf16<1, false, false, AK, BK, 16, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 4) * kStageK);
-    stage_bf16<2, false, false, AK, BK, 16, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 5) * kStageK);
-    stage_bf16<3, false, false, AK, BK, 16, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 6) * kStageK);
+  // copies of blocks kt / 2 + 1 and kt / 2 + 2 wholly inside K: no masking
+  for (; kt + 6 <= 2 * KBF; kt += 4) {
+    stage_bf16<0, 0, false, false, AK, BK, 0, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db,
+                                                      (kt / 2 + 1) * kBlockK);
+    stage_bf16<1, 0, false, false, AK, BK, 0, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
+    stage_bf16<0, 1, false, false, AK, BK, 0, false>(acc, Y, X, fa, fb, L, lane, A, B, da, db,
+                                                      (kt / 2 + 2) * kBlockK);
+    stage_bf16<1, 1, false, false, AK, BK, 0, false>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
   }
   for (; kt < KTp; kt += 4) {
-    stage_bf16<0, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 3) * kStageK);
-    stage_bf16<1, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 4) * kStageK);
-    stage_bf16<2, false, false, AK, BK, 16, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt + 5) * kStageK);
-    stage_bf16<3, false, false, AK, BK, 16, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, (kt + 6) * kStageK);
+    stage_bf16<0, 0, false, false, AK, BK, 0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt / 2 + 1) * kBlockK);
+    stage_bf16<1, 0, false, false, AK, BK, 0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
+    stage_bf16<0, 1, false, false, AK, BK, 0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt / 2 + 2) * kBlockK);
+    stage_bf16<1, 1, false, false, AK, BK, 0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
   }
   stage_last_half<false>(acc, Y);   // upper half of stage KTp - 1 (odd)
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
 }
 
 template <bool AK, bool BK>
