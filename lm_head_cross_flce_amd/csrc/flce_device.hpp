@@ -375,21 +375,31 @@ template <int N> constexpr int waitcnt_vm_lgkm0() { return (N & 15) | ((N >> 4) 
 // operand's valid K (blocks that are not wholly inside it).
 template <bool KCONTIG> struct Dma;
 
+// Tile row t of an operand copied with permuted rows holds global row
+// m0 + tile_row_perm(t): bits 3..2 of t move to bits 4..3 and bit 4 to bit 2.
+// An accumulator lane then owns, in blocks 2s and 2s + 1 of a wave, the eight
+// consecutive rows 32 s + 8 (l / 16) .. + 7 of its 128 (instead of two runs
+// of four 16 rows apart), so it can store them as one 16-byte piece.
+__device__ __forceinline__ constexpr int tile_row_perm(int t) {
+  return (t & 0xE3) | ((t & 0x0C) << 1) | ((t & 0x10) >> 2);
+}
+
 // K-contiguous: instruction idx fills rows 8 idx .. 8 idx + 7; lane l takes
 // row 8 idx + l / 8 and LDS chunk l % 8, which holds global chunk
-// (l % 8) ^ (l / 8).
+// (l % 8) ^ (l / 8).  PERM: tile rows hold permuted global rows.
 template <> struct Dma<true> {
   uint32_t off[8];
   const uint16_t* base;
   int wave;
-  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
+  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid, bool perm = false) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = o.p + (int64_t)m0 * o.ld;
     const int c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int row = 8 * (4 * q + wave) + (lane >> 3);
+      const int t = 8 * (4 * q + wave) + (lane >> 3);
+      const int row = perm ? tile_row_perm(t) : t;
       off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
@@ -407,7 +417,7 @@ template <> struct Dma<false> {
   const uint16_t* base;
   int64_t ld;
   int wave;
-  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid) {
+  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid, bool = false) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = o.p + m0;
@@ -577,13 +587,14 @@ __device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
 // block into buffer 0; it may run while the previous tile's epilogue is still
 // working, as long as every wave has finished that tile's mainloop (whose
 // last barrier follows its last fragment read and the completion of its
-// copies).
+// copies).  perm_a: A's tile rows hold permuted rows (tile_row_perm; A must
+// be K-contiguous).
 template <bool AK, bool BK> struct TileCopy {
   Dma<AK> da;
   Dma<BK> db;
   __device__ __forceinline__ void start(const Opnd<uint16_t>& A, int m0, const Opnd<uint16_t>& B, int n0,
-                                        const Lds& L, int tid) {
-    da.init(A, m0, tid);
+                                        const Lds& L, int tid, bool perm_a = false) {
+    da.init(A, m0, tid, perm_a);
     db.init(B, n0, tid);
     const int lane = tid & 63;
     // Copies past K read zeros (out-of-range offsets), so the stage bodies

@@ -330,20 +330,26 @@ struct TokenTile {
 
 // One tile of the recompute kernel.  EXTRA: the vector-memory instructions
 // every wave has issued since this tile's copies started (see
-// gemm_tile_bf16_run).
+// gemm_tile_bf16_run).  bf16 tiles copy W with permuted rows
+// (tile_row_perm), so a lane's values in blocks 2s and 2s + 1 of a token
+// column are eight consecutive vocabulary rows; fp32 tiles keep the MFMA row
+// order (two runs of four rows, 16 apart).
+template <class T>
+__device__ __forceinline__ constexpr int dz_row(int i, int g) {
+  return sizeof(T) == 2 ? 32 * (i >> 1) + 8 * g + 4 * (i & 1) : 16 * i + 4 * g;
+}
+
 template <class T, bool BIAS, bool DB, int EXTRA>
 __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
                                         const Lds& L, lds_f32* red, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
-                                        lds_t* stage, int tid) {
+                                        int tid) {
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
   const int g = lane >> 4;
-  const int rloc = wm * kWaveTile + 4 * g;
   int tm, tn;
   tile_coords(t, G, TM, a.NT, tm, tn);
   const int v0 = vs + tm * kTile, n0 = tn * kTile;
-  const int rb = v0 + rloc;
   TokenTile tt;
   tt.fetch(a, n0, tid);
   BiasTile<T> bt;
@@ -355,7 +361,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
     if (tnext < G) {
       int tm2, tn2;
       tile_coords(tnext, G, TM, a.NT, tm2, tn2);
-      tc.start(A, vs + tm2 * kTile, B, tn2 * kTile, L, tid);
+      tc.start(A, vs + tm2 * kTile, B, tn2 * kTile, L, tid, true);
     }
   } else {
     gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
@@ -369,95 +375,83 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // columns and the input-gradient kernel multiplies them by zero rows of W.
   // Slab rows of this tile's tokens, from token n0 on.
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
-  // 32-row bands I of the wave's rows, one 32 x 32 region (blocks 2I, 2I+1 x
-  // 2J, 2J+1) at a time: dlogits, the band's db row sums, and the slab store
-  // through this wave's LDS staging buffer ([token][64 bytes], 16-byte chunk c
-  // of row n at c ^ (n & 3)), read back as 16 contiguous bytes per lane, four
-  // lanes per 64-byte row segment.  A band's row sums are reduced over the
-  // lane group as soon as the band is done, so few stay live.
+  // Bands s of 32 wave rows (blocks 2s, 2s + 1), token blocks j within them:
+  // dlogits of the lane's token (16 j + l % 16) at its rows r0 .. r0 + 3 and
+  // r1 .. r1 + 3 (tile-relative), the band's db row sums, and the slab store.
+  // A band's row sums are reduced over the lane group as soon as the band is
+  // done, so few stay live.
   float dbs[4];
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
+  for (int s = 0; s < 4; ++s) {
+    const int r0 = wm * kWaveTile + dz_row<T>(2 * s, g), r1 = wm * kWaveTile + dz_row<T>(2 * s + 1, g);
+    const f32x4 bias0 = BIAS ? read_bias4(L.bias, r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 bias1 = BIAS ? read_bias4(L.bias, r1) : f32x4{0.f, 0.f, 0.f, 0.f};
     float rs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) rs[e] = 0.f;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int j = 0; j < 8; ++j) {
+      const int nl = wn * kWaveTile + 16 * j + (lane & 15);   // token within the tile
+      const f32x4 cf = ltok[nl];
+      const int y = lyv[nl];
+      const f32x4 z0 = acc_read4(acc[2 * s][j]);
+      const f32x4 z1 = acc_read4(acc[2 * s + 1][j]);
+      float dz[8];
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj) {
-        const int j = 2 * J + bj;
-        const int nl = wn * kWaveTile + 16 * j + (lane & 15);   // token within the tile
-        const f32x4 cf = ltok[nl];
-        const int tcol = lyv[nl] - rb;
+      for (int r = 0; r < 4; ++r) {
+        dz[r] = fmaf(cf[0], fast_exp2(fmaf(z0[r] + bias0[r], kLog2e, -cf[3])), -cf[1]);
+        dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(z1[r] + bias1[r], kLog2e, -cf[3])), -cf[1]);
+      }
+      const int t0 = y - (v0 + r0), t1 = y - (v0 + r1);
+      if (__ballot((t0 >= 0 && t0 < 4) || (t1 >= 0 && t1 < 4))) {
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-          const int i = 2 * I + bi;
-          const f32x4 z = acc_read4(acc[i][j]);
-          const f32x4 bias = BIAS ? read_bias4(L.bias, rloc + 16 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
-          float dz[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(z[r] + bias[r], kLog2e, -cf[3]));
-            dz[r] = fmaf(cf[0], p, -cf[1]);
-          }
-          const int tb = tcol - 16 * i;
-          if (__ballot(tb >= 0 && tb < 4)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (tb == r) dz[r] -= cf[2];
-          }
-          if (DB) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rs[4 * bi + r] += dz[r];
-          }
-          if constexpr (sizeof(T) == 2) {
-            typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-            const int n = 16 * bj + (lane & 15);
-            const int c = 2 * bi + (g >> 1);
-            *(lds_u32x2*)(stage + n * 64 + 16 * (c ^ (n & 3)) + 8 * (g & 1)) =
-                u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
-          } else {
-            const int n = n0 + nl;
-            const int v = (v0 - vs) + wm * kWaveTile + 16 * i + 4 * g;
-            if (n < a.N) store4<T>((T*)a.slab + (int64_t)n * a.ldS + v, dz[0], dz[1], dz[2], dz[3]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          if (t0 == r) dz[r] -= cf[2];
+          if (t1 == r) dz[4 + r] -= cf[2];
         }
+      }
+      if (DB) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rs[e] += dz[e];
       }
       if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int row = 16 * k + (lane >> 2), c = lane & 3;
-          const u32x4 v = lds_load16(stage + row * 64 + 16 * (c ^ (row & 3)));
-          const int nl = wn * kWaveTile + 32 * J + row;
-          const uint32_t off = n0 + nl < a.N
-                                   ? (uint32_t)(((int64_t)nl * a.ldS + (v0 - vs) + wm * kWaveTile + 32 * I + 8 * c) * 2)
-                                   : kOOB;
-          __builtin_amdgcn_raw_buffer_store_b128(v, rslab, off, 0, 0);
+        // r1 = r0 + 4: sixteen contiguous bytes; a wave instruction writes 16
+        // tokens x 64 bytes.
+        const uint32_t off =
+            n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.ldS + (v0 - vs) + r0) * 2) : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3]), pack_bf16x2(dz[4], dz[5]),
+                  pack_bf16x2(dz[6], dz[7])},
+            rslab, off, 0, 0);
+      } else {
+        if (n0 + nl < a.N) {
+          T* row = (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs);
+          store4<T>(row + r0, dz[0], dz[1], dz[2], dz[3]);
+          store4<T>(row + r1, dz[4], dz[5], dz[6], dz[7]);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if (DB) dbs[I] = group_sum8(rs, lane);
+    if (DB) dbs[s] = group_sum8(rs, lane);
   }
 
   if (DB) {
-    // Lanes 2q, 2q + 1 of group g hold band I's total of value q = 4 bi + r,
-    // wave row 32 I + 16 bi + 4 g + r.  The two waves that share rows (wn = 0,
-    // 1) add through LDS; the next tile's mainloop barriers keep this tile's
+    // Lanes 2q, 2q + 1 of group g hold band s's total of value q: tile row
+    // r0 + q (q < 4) or r1 + q - 4.  The two waves that share rows (wn = 0, 1)
+    // add through LDS; the next tile's mainloop barriers keep this tile's
     // reads of red ahead of the next tile's writes.
     const int q = (lane & 15) >> 1;
     const bool lead = (lane & 1) == 0;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const int row = wm * kWaveTile + 32 * I + 16 * (q >> 2) + 4 * g + (q & 3);
-      if (wn == 1 && lead) red[row] = dbs[I];
+    for (int s = 0; s < 4; ++s) {
+      const int row = wm * kWaveTile + dz_row<T>(2 * s + (q >> 2), g) + (q & 3);
+      if (wn == 1 && lead) red[row] = dbs[s];
     }
     lds_barrier();
     if (wn == 0 && lead) {
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const int rl = wm * kWaveTile + 32 * I + 16 * (q >> 2) + 4 * g + (q & 3);
-        if (v0 + rl < a.V) a.dbp[(int64_t)tn * a.ldS + (v0 - vs) + rl] = dbs[I] + red[rl];
+      for (int s = 0; s < 4; ++s) {
+        const int rl = wm * kWaveTile + dz_row<T>(2 * s + (q >> 2), g) + (q & 3);
+        if (v0 + rl < a.V) a.dbp[(int64_t)tn * a.ldS + (v0 - vs) + rl] = dbs[s] + red[rl];
       }
     }
   }
@@ -475,10 +469,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   __shared__ __attribute__((aligned(16))) float red_s[kTile];       // db: the two waves sharing rows
   __shared__ __attribute__((aligned(16))) f32x4 tok_s[kTile];       // per-token coefficients
   __shared__ __attribute__((aligned(16))) int yv_s[kTile];          // per-token targets
-  __shared__ __attribute__((aligned(16))) char stage_s[4][2048];    // bf16 store staging, one per wave
   lds_f32* red = (lds_f32*)red_s;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  lds_t* stage = (lds_t*)stage_s[wave];
+  const int tid = threadIdx.x;
   const int G = TM * a.NT;
   TileCopy<true, true> tc;
   int t = blockIdx.x;
@@ -487,7 +479,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
     const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
     int tm, tn;
     tile_coords(t, G, TM, a.NT, tm, tn);
-    tc.start(A, vs + tm * kTile, B, tn * kTile, L, tid);
+    tc.start(A, vs + tm * kTile, B, tn * kTile, L, tid, true);
   }
   // Vector-memory instructions every wave issues between starting a tile's
   // copies and its mainloop: the per-token loads (2) and the bias fetch, plus,
@@ -496,9 +488,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   constexpr int kStoresVm = 32;
   lds_f32x4* ltok = (lds_f32x4*)tok_s;
   __attribute__((address_space(3))) int* lyv = (__attribute__((address_space(3))) int*)yv_s;
-  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, stage, tid);
+  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
   for (t += gridDim.x; t < G; t += gridDim.x)
-    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, stage, tid);
+    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
 }
 
 // db[vs + c] = sum over token tiles of the slab's db partials (fixed order),
