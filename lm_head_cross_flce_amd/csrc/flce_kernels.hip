@@ -624,8 +624,6 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   if (bias && want_db) hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
   else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
   else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
-  if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
-  else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
   if (a.dx) {
     const dim3 gdx(TH * a.NT);
     if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst>), gdx, blk, 0, st, a, vs, width, wpad, TH);
@@ -633,6 +631,8 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
     else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast>), gdx, blk, 0, st, a, vs, width, wpad, TH);
     else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly>), gdx, blk, 0, st, a, vs, width, wpad, TH);
   }
+  if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
   return hipGetLastError();
 }
 
