@@ -48,12 +48,25 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources; a traffic figure is valid only for this hash."""
+def _code_only(text):
+    """C++/HIP source with comments removed and whitespace collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(sources=None):
+    """Hash of the HIP sources' code (comments and whitespace ignored); a traffic
+    figure is valid only for this hash.  ``sources``: {file name: text}, default
+    the files under csrc/."""
+    if sources is None:
+        sources = {}
+        for f in glob.glob(os.path.join(ROOT, "lm_head_cross_flce_amd", "csrc", "*")):
+            with open(f, encoding="utf-8") as fh:
+                sources[os.path.basename(f)] = fh.read()
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "lm_head_cross_flce_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+    for name in sorted(sources):
+        h.update(name.encode() + _code_only(sources[name]).encode())
     return h.hexdigest()[:16]
 
 

@@ -2,20 +2,20 @@
 //
 // Every contraction of the method is computed by one tile routine: a 256 x 256
 // output tile per 256-thread workgroup (4 waves in a 2 x 2 grid, 128 x 128 per
-// wave as 4 x 4 blocks of 32 x 32 MFMA accumulators).
+// wave as 8 x 8 blocks of 16 x 16 MFMA accumulators).
 //
 //   C[m, n] = sum_k A[m, k] * B[n, k]
 //
 // Each operand is read from global memory either "K-contiguous" (element
 // (m, k) at p[m * ld + k]) or "M-contiguous" (element (m, k) at p[k * ld + m]).
-// bf16 operands are copied global -> LDS by the buffer unit in their global
-// layout (32-wide K stages, a ring of four LDS slots per operand) and read with
-// 16-byte LDS loads (K-contiguous) or transposing 8-byte loads (M-contiguous).
-// fp32 operands go through registers into two padded LDS buffers.
+// bf16 operands are copied global -> LDS by the buffer unit in 64-deep K
+// blocks (two LDS buffers per operand) and read with 16-byte LDS loads
+// (K-contiguous) or transposing 8-byte loads (M-contiguous).  fp32 operands go
+// through registers into two padded LDS buffers.
 //
-// MFMA output layout (32 x 32 blocks): accumulator element r of lane l holds
-// row 8 * (r / 4) + 4 * (l / 32) + (r % 4) and column l % 32 of its block, so
-// one lane owns one column and 16 rows, four of them consecutive.
+// MFMA output layout (16 x 16 blocks): accumulator element r of lane l holds
+// row 4 * (l / 16) + r and column l % 16 of its block, so one lane owns one
+// column and four consecutive rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
