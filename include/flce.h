@@ -119,6 +119,66 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
                           void* dx, void* dW, void* db,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Vocabulary shards.  DeepSpeed PR 8792 ("What"; "Memory and time") splits W's
+ * rows across ranks: each rank reduces its rows to per-token statistics in
+ * forward, the statistics are merged across ranks (a max and sums), and in
+ * backward each rank recomputes its own logits against the global lse and
+ * produces dW and db for its rows and an fp32 partial of dx, summed across
+ * ranks and cast once at the end (the PR's fp32 hidden-gradient review).  A
+ * shard is W's rows [vocab_start, vocab_start + V_shard) of a head with
+ * V_total rows; W_shard points at row vocab_start (and b_shard at
+ * b[vocab_start]); targets stay global indices.  On one GPU the shards can
+ * simply run one after another.
+ *
+ * flce_shard_workspace_size: workspace bytes for flce_shard_forward
+ * (*fwd_bytes), flce_shard_merge (*merge_bytes) and flce_shard_backward
+ * (*bwd_bytes); pure host arithmetic; outputs may be NULL.
+ */
+flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int dtype, int has_bias,
+                                      size_t* fwd_bytes, size_t* merge_bytes, size_t* bwd_bytes);
+
+/*
+ * Shard forward: writes stats, float32 [N][4]: per token, over the shard's
+ * rows only, {m = max_j z, d = sum_j exp(z - m), sum_j z (0 unless eps > 0),
+ * z[y_n] if y_n lies in the shard, else 0}.  Every token gets statistics,
+ * ignored ones included (the merge drops them).  eps = label_smoothing only
+ * decides whether sum_j z is formed.
+ */
+flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
+                               int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
+                               int dtype, float label_smoothing, int64_t ignore_index, float* stats,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge of num_shards shards' statistics, stacked as float32
+ * [num_shards][N][4] (any order of shards), into loss, lse and n_valid exactly
+ * as flce_forward writes them for the whole head (eps / V_total in the loss).
+ * On several GPUs the stack is what an all-gather of the statistics gives; a
+ * max all-reduce of m followed by sum all-reduces of the rescaled d, sum z and
+ * z_y is the same merge.
+ */
+flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64_t* targets, int64_t N,
+                             int64_t V_total, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                             int reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Shard backward: with the merged lse and n_valid, overwrites
+ *   dW_shard [V_shard, H]  (may be NULL)   and   db_shard [V_shard] (may be NULL)
+ * in the input dtype, and writes the shard's contribution to dx, float32
+ * [N, H], into dx_partial (may be NULL): overwritten, or added to what it
+ * holds when accumulate_dx != 0 (so shards run in sequence can sum into one
+ * buffer).  dx itself is the sum over all shards, cast once to the input
+ * dtype by the caller.
+ */
+flce_status flce_shard_backward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
+                                int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
+                                int dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                int reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
+                                float* dx_partial, int accumulate_dx, void* dW_shard, void* db_shard,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* flce_status_string(int status);
 

@@ -25,7 +25,8 @@ REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 
 # Every symbol the public header declares.
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_status_string",
-           "flce_backward_slab_cols")
+           "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
+           "flce_shard_backward")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +63,17 @@ def load() -> ctypes.CDLL:
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
         lib.flce_backward_slab_cols.restype = i64
+        lib.flce_shard_workspace_size.argtypes = [i64, i64, i64, c_int, c_int, ctypes.POINTER(sz),
+                                                  ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        lib.flce_shard_workspace_size.restype = c_int
+        lib.flce_shard_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, c_int, f32, i64, vp,
+                                           vp, sz, vp]
+        lib.flce_shard_forward.restype = c_int
+        lib.flce_shard_merge.argtypes = [vp, i64, vp, i64, i64, f32, f32, i64, c_int, vp, vp, vp, vp, sz, vp]
+        lib.flce_shard_merge.restype = c_int
+        lib.flce_shard_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, c_int, f32, f32, i64,
+                                            c_int, vp, vp, vp, vp, c_int, vp, vp, vp, sz, vp]
+        lib.flce_shard_backward.restype = c_int
         _lib = lib
         return lib
 
@@ -102,3 +114,39 @@ def flce_backward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scal
     _check(load().flce_backward(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
                                 ignore_index, reduction, lse, n_valid, grad_loss, dx or None, dW or None,
                                 db or None, workspace, workspace_bytes, stream or None), "flce_backward")
+
+
+def flce_shard_workspace_size(N: int, H: int, V_shard: int, dtype: int, has_bias: bool):
+    """(forward_bytes, merge_bytes, backward_bytes) for one vocabulary shard."""
+    f, m, b = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().flce_shard_workspace_size(N, H, V_shard, dtype, int(bool(has_bias)), ctypes.byref(f),
+                                            ctypes.byref(m), ctypes.byref(b)), "flce_shard_workspace_size")
+    return f.value, m.value, b.value
+
+
+def flce_shard_forward(x, W_shard, b_shard, targets, N, H, V_shard, vocab_start, V_total, dtype,
+                       label_smoothing, ignore_index, stats, workspace, workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_shard_forward(x, W_shard, b_shard or None, targets, N, H, V_shard, vocab_start, V_total,
+                                     dtype, label_smoothing, ignore_index, stats, workspace, workspace_bytes,
+                                     stream or None), "flce_shard_forward")
+
+
+def flce_shard_merge(stats, num_shards, targets, N, V_total, label_smoothing, z_loss_scale, ignore_index,
+                     reduction, loss, lse, n_valid, workspace, workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_shard_merge(stats, num_shards, targets, N, V_total, label_smoothing, z_loss_scale,
+                                   ignore_index, reduction, loss, lse, n_valid, workspace, workspace_bytes,
+                                   stream or None), "flce_shard_merge")
+
+
+def flce_shard_backward(x, W_shard, b_shard, targets, N, H, V_shard, vocab_start, V_total, dtype,
+                        label_smoothing, z_loss_scale, ignore_index, reduction, lse, n_valid, grad_loss,
+                        dx_partial, accumulate_dx, dW_shard, db_shard, workspace, workspace_bytes,
+                        stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_shard_backward(x, W_shard, b_shard or None, targets, N, H, V_shard, vocab_start, V_total,
+                                      dtype, label_smoothing, z_loss_scale, ignore_index, reduction, lse, n_valid,
+                                      grad_loss, dx_partial or None, int(bool(accumulate_dx)), dW_shard or None,
+                                      db_shard or None, workspace, workspace_bytes, stream or None),
+           "flce_shard_backward")

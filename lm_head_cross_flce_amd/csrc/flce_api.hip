@@ -63,7 +63,9 @@ int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   return c < vmax ? c : vmax;
 }
 
-Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias) {
+// with_dx_acc: the backward keeps its own fp32 dx accumulator (the shard
+// backward accumulates into the caller's buffer instead).
+Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true) {
   Geometry g{};
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   g.NT = (int)cdiv(N, kTile);
@@ -84,7 +86,7 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias) {
   g.off_slab = off;
   off = align_up(off + (size_t)N * g.slab_cols * es);
   g.off_dxacc = off;
-  off = align_up(off + (size_t)N * H * 4);
+  if (with_dx_acc) off = align_up(off + (size_t)N * H * 4);
   g.off_dbp = off;
   if (has_bias) off = align_up(off + (size_t)g.NT * g.slab_cols * 4);
   g.off_coef = off;
@@ -105,10 +107,44 @@ flce_status check_options(float eps, float s, int reduction) {
   return FLCE_OK;
 }
 
+flce_status check_shard(int64_t V_shard, int64_t vocab_start, int64_t V_total) {
+  if (vocab_start < 0 || V_total < 1 || V_total > (int64_t(1) << 30)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (vocab_start + V_shard > V_total) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
 flce_status check_inputs(const void* x, const void* W, const void* b, const int64_t* targets, int dtype) {
   if (!x || !W || !targets) return FLCE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(targets, 8)) return FLCE_ERR_INVALID_ARGUMENT;
   if (b && !aligned(b, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+// Backward launch sequence shared by the full and the shard entry points:
+// per-token coefficients, then per slab the recompute, dx and dW (+ db)
+// launches.  dx_out_fp32: dx is the fp32 accumulator itself (a.dx_acc),
+// never cast; accumulate: it already holds a partial sum to add to.
+flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int dtype, bool want_db,
+                         bool dx_out_fp32, bool accumulate, hipStream_t s) {
+  (void)hipGetLastError();
+  if (flce::launch_bwd_prepare(a, s) != hipSuccess) return FLCE_ERR_HIP;
+  const int64_t cols = g.slab_cols;
+  const int64_t nslab = cdiv(V, cols);
+  for (int64_t k = 0; k < nslab; ++k) {
+    const int64_t vs = k * cols;
+    const int64_t width = (V - vs) < cols ? (V - vs) : cols;
+    int mode = flce::kDxAccum;
+    if (dx_out_fp32) {
+      if (k == 0 && !accumulate) mode = flce::kDxFirst;
+    } else if (nslab == 1) {
+      mode = flce::kDxOnly;
+    } else if (k == 0) {
+      mode = flce::kDxFirst;
+    } else if (k == nslab - 1) {
+      mode = flce::kDxLast;
+    }
+    if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
+  }
   return FLCE_OK;
 }
 
@@ -214,21 +250,121 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
   a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
   a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
 
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (flce::launch_bwd_prepare(a, s) != hipSuccess) return FLCE_ERR_HIP;
-  const int64_t cols = g.slab_cols;
-  const int64_t nslab = cdiv(V, cols);
-  for (int64_t k = 0; k < nslab; ++k) {
-    const int64_t vs = k * cols;
-    const int64_t width = (V - vs) < cols ? (V - vs) : cols;
-    int mode = flce::kDxAccum;
-    if (nslab == 1) mode = flce::kDxOnly;
-    else if (k == 0) mode = flce::kDxFirst;
-    else if (k == nslab - 1) mode = flce::kDxLast;
-    if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
-  }
+  return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream);
+}
+
+flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int dtype, int has_bias,
+                                      size_t* fwd_bytes, size_t* merge_bytes, size_t* bwd_bytes) {
+  flce_status st = check_shape(N, H, V_shard, dtype);
+  if (st != FLCE_OK) return st;
+  const Geometry g = geometry(N, H, V_shard, dtype, has_bias, false);
+  if (fwd_bytes) *fwd_bytes = g.fwd_total;
+  if (merge_bytes) *merge_bytes = align_up((size_t)N * 4);
+  if (bwd_bytes) *bwd_bytes = g.bwd_total;
   return FLCE_OK;
+}
+
+flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
+                               int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
+                               int dtype, float label_smoothing, int64_t ignore_index, float* stats,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status st = check_shape(N, H, V_shard, dtype);
+  if (st != FLCE_OK) return st;
+  if ((st = check_shard(V_shard, vocab_start, V_total)) != FLCE_OK) return st;
+  if ((st = check_options(label_smoothing, 0.f, FLCE_REDUCTION_MEAN)) != FLCE_OK) return st;
+  if ((st = check_inputs(x, W_shard, b_shard, targets, dtype)) != FLCE_OK) return st;
+  if (!stats || !aligned(stats, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Geometry g = geometry(N, H, V_shard, dtype, b_shard != nullptr, false);
+  if (workspace_bytes < g.fwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+
+  char* ws = (char*)workspace;
+  flce::FwdLaunch a{};
+  a.x = x; a.W = W_shard; a.b = b_shard; a.targets = targets;
+  a.N = (int)N; a.H = (int)H; a.V = (int)V_shard;
+  a.NT = g.NT; a.P = g.P; a.VT = g.VT;
+  a.vocab_start = vocab_start;
+  a.ignore_index = ignore_index;
+  a.eps = label_smoothing;
+  a.partials = ws + g.off_partials;
+  a.stats = stats;
+  (void)hipGetLastError();
+  if (flce::launch_shard_forward(a, dtype, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
+flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64_t* targets, int64_t N,
+                             int64_t V_total, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                             int reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (N < 1 || N > (int64_t(1) << 30) || V_total < 1 || V_total > (int64_t(1) << 30)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (num_shards < 1 || num_shards > (int64_t(1) << 20)) return FLCE_ERR_INVALID_ARGUMENT;
+  flce_status st = check_options(label_smoothing, z_loss_scale, reduction);
+  if (st != FLCE_OK) return st;
+  if (!stats || !aligned(stats, 16) || !targets || !aligned(targets, 8)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!loss || !lse || !n_valid || !aligned(loss, 4) || !aligned(lse, 4) || !aligned(n_valid, 8))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < align_up((size_t)N * 4)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+
+  flce::FwdLaunch a{};
+  a.targets = targets;
+  a.N = (int)N;
+  a.P = (int)num_shards;
+  a.ignore_index = ignore_index;
+  a.eps = label_smoothing;
+  a.eps_over_v = (float)((double)label_smoothing / (double)V_total);
+  a.s = z_loss_scale;
+  a.reduction = reduction;
+  a.partials = const_cast<float*>(stats);
+  a.rowloss = (float*)workspace;
+  a.loss = loss; a.lse = lse; a.n_valid = n_valid;
+  (void)hipGetLastError();
+  if (flce::launch_merge(a, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
+flce_status flce_shard_backward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
+                                int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
+                                int dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                int reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
+                                float* dx_partial, int accumulate_dx, void* dW_shard, void* db_shard,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status st = check_shape(N, H, V_shard, dtype);
+  if (st != FLCE_OK) return st;
+  if ((st = check_shard(V_shard, vocab_start, V_total)) != FLCE_OK) return st;
+  if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
+  if ((st = check_inputs(x, W_shard, b_shard, targets, dtype)) != FLCE_OK) return st;
+  if (!lse || !n_valid || !grad_loss) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!aligned(lse, 4) || !aligned(n_valid, 8) || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((dx_partial && !aligned(dx_partial, 16)) || (dW_shard && !aligned(dW_shard, 16))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (db_shard && !aligned(db_shard, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Geometry g = geometry(N, H, V_shard, dtype, b_shard != nullptr, false);
+  if (workspace_bytes < g.bwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  const bool want_db = b_shard != nullptr && db_shard != nullptr;
+  if (!dx_partial && !dW_shard && !want_db) return FLCE_OK;
+
+  char* ws = (char*)workspace;
+  flce::BwdLaunch a{};
+  a.x = x; a.W = W_shard; a.b = b_shard; a.targets = targets;
+  a.N = (int)N; a.H = (int)H; a.V = (int)V_shard;
+  a.NT = g.NT;
+  a.vocab_start = vocab_start;
+  a.ignore_index = ignore_index;
+  a.eps = label_smoothing;
+  a.eps_over_v = (float)((double)label_smoothing / (double)V_total);
+  a.s = z_loss_scale;
+  a.reduction = reduction;
+  a.lse = lse; a.n_valid = n_valid; a.grad = grad_loss;
+  a.coef = ws + g.off_coef;
+  a.yv = (int*)(ws + g.off_yv);
+  a.slab = ws + g.off_slab;
+  a.ldS = g.slab_cols;
+  a.dx_acc = dx_partial;
+  a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
+  a.dx = dx_partial; a.dW = dW_shard; a.db = want_db ? db_shard : nullptr;
+  return run_backward(a, g, V_shard, dtype, want_db, true, accumulate_dx != 0, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -121,7 +121,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   for (int j = 0; j < 8; ++j) {
     const int n = n0 + wn * kWaveTile + 16 * j + (lane & 15);
     const int64_t t = n < a.N ? a.targets[n] : a.ignore_index;
-    ycol[j] = (t == a.ignore_index) ? -1 : (int)t;
+    const int64_t lt = t - a.vocab_start;   // row of W holding the target, if any
+    ycol[j] = (t == a.ignore_index || lt < 0 || lt >= a.V) ? -1 : (int)lt;
     m[j] = -INFINITY;
     d[j] = 0.f;
     sz[j] = 0.f;
@@ -217,6 +218,23 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdLaunch a) {
   if (a.reduction == kNone) a.loss[n] = l;
 }
 
+// Shard forward: the phases' partials of each token merged into one
+// {m, d, sum z, z_y} over the shard's rows (z_y is 0 unless the target lies in
+// the shard).
+__global__ void __launch_bounds__(256) fwd_stats_kernel(FwdLaunch a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const f32x4* part = (const f32x4*)a.partials;
+  float m = -INFINITY, d = 0.f, sz = 0.f, zy = 0.f;
+  for (int p = 0; p < a.P; ++p) {
+    const f32x4 q = part[(int64_t)p * a.N + n];
+    merge_md(m, d, q[0], q[1]);
+    sz += q[2];
+    zy += q[3];
+  }
+  ((f32x4*)a.stats)[n] = f32x4{m, d, sz, zy};
+}
+
 __global__ void __launch_bounds__(1024) fwd_finalize_kernel(FwdLaunch a) {
   __shared__ double ssum[1024];
   __shared__ long long scnt[1024];
@@ -261,6 +279,28 @@ hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
   return dtype == 1 ? launch_forward_t<uint16_t>(a, st) : launch_forward_t<float>(a, st);
 }
 
+template <class T>
+static hipError_t launch_shard_forward_t(const FwdLaunch& a, hipStream_t st) {
+  const int G = a.NT * a.P;
+  const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
+  if (bias && smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, true, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) hipLaunchKernelGGL((fwd_lse_kernel<T, true, false>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, false, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((fwd_lse_kernel<T, false, false>), dim3(G), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(fwd_stats_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
+  return dtype == 1 ? launch_shard_forward_t<uint16_t>(a, st) : launch_shard_forward_t<float>(a, st);
+}
+
+hipError_t launch_merge(const FwdLaunch& a, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
@@ -277,7 +317,8 @@ __global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
   if (!valid) c = 0.f;
   const float lse = a.lse[n];
   ((f32x4*)a.coef)[n] = f32x4{c * (1.f + 2.f * a.s * lse), c * a.eps_over_v, c * (1.f - a.eps), lse * kLog2e};
-  a.yv[n] = valid ? (int)t : -1;
+  const int64_t lt = t - a.vocab_start;   // row of W holding the target, if any
+  a.yv[n] = (valid && lt >= 0 && lt < a.V) ? (int)lt : -1;
 }
 
 // Sums over the 16 lanes of a lane group (lane / 16).  A step halves the

@@ -11,8 +11,9 @@ enum DxMode { kDxFirst = 0, kDxAccum = 1, kDxLast = 2, kDxOnly = 3 };
 
 struct FwdLaunch {
   const void* x; const void* W; const void* b; const int64_t* targets;
-  int N, H, V;
+  int N, H, V;            // V: rows of W (a shard's rows for the shard forward)
   int NT, P, VT;          // token tiles, vocabulary phases, vocabulary tiles
+  int64_t vocab_start;    // global index of W's row 0; targets are global indices
   int64_t ignore_index;
   float eps, eps_over_v, s;
   int reduction;
@@ -21,12 +22,14 @@ struct FwdLaunch {
   float* loss;            // [1] or [N]
   float* lse;             // [N]
   int64_t* n_valid;       // [1]
+  float* stats;           // shard forward: float4 [N] {m, d, sum z, z_y} over the shard's rows
 };
 
 struct BwdLaunch {
   const void* x; const void* W; const void* b; const int64_t* targets;
-  int N, H, V;
+  int N, H, V;            // V: rows of W (a shard's rows for the shard backward)
   int NT;
+  int64_t vocab_start;    // global index of W's row 0; targets are global indices
   int64_t ignore_index;
   float eps, eps_over_v, s;
   int reduction;
@@ -41,6 +44,10 @@ struct BwdLaunch {
 
 // dtype: 0 = fp32, 1 = bf16.  Each returns the launch error code.
 hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st);
+// Shard forward: logits statistics of W's rows only, merged over phases into a.stats.
+hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st);
+// Merge of a.P shards' statistics (a.partials = float4 [P][N]) into lse, loss and the count.
+hipError_t launch_merge(const FwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
                            hipStream_t st);

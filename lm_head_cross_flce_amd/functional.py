@@ -112,6 +112,97 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
     return dx, dW, db
 
 
+def flce_shard_workspace_size(N: int, H: int, V_shard: int, dtype: torch.dtype,
+                              has_bias: bool) -> Tuple[int, int, int]:
+    """(forward, merge, backward) workspace bytes of one vocabulary shard."""
+    return _lib.flce_shard_workspace_size(N, H, V_shard, _DTYPES[dtype], has_bias)
+
+
+def flce_shard_forward(x: torch.Tensor, W_shard: torch.Tensor, b_shard: Optional[torch.Tensor],
+                       targets: torch.Tensor, vocab_start: int, V_total: int, label_smoothing: float = 0.0,
+                       ignore_index: int = -100, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-token statistics float32 [N, 4] = (m, d, sum z, z_y) over the shard's rows
+    W[vocab_start : vocab_start + V_shard] (W_shard); targets are global indices."""
+    x, W_shard, b_shard, targets = _prep(x, W_shard, b_shard, targets)
+    N, H = x.shape
+    V_shard = W_shard.shape[0]
+    dt, dev = _dtype_code(x), x.device
+    fwd_bytes, _, _ = _lib.flce_shard_workspace_size(N, H, V_shard, dt, b_shard is not None)
+    if workspace is None or workspace.numel() < fwd_bytes:
+        workspace = torch.empty(max(fwd_bytes, 1), dtype=torch.uint8, device=dev)
+    stats = torch.empty(N, 4, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_shard_forward(x.data_ptr(), W_shard.data_ptr(), _ptr(b_shard), targets.data_ptr(), N, H, V_shard,
+                                int(vocab_start), int(V_total), dt, float(label_smoothing), int(ignore_index),
+                                stats.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    return stats
+
+
+def flce_shard_merge(stats: torch.Tensor, targets: torch.Tensor, V_total: int, label_smoothing: float = 0.0,
+                     z_loss_scale: float = 0.0, ignore_index: int = -100, reduction: str = "mean",
+                     workspace: Optional[torch.Tensor] = None):
+    """Merge stacked shard statistics [num_shards, N, 4] into (loss, lse, n_valid), as
+    flce_forward returns them for the whole head."""
+    if stats.dim() != 3 or stats.shape[2] != 4 or stats.dtype != torch.float32:
+        raise ValueError("stats must be float32 [num_shards, N, 4]")
+    stats = stats.contiguous()
+    num_shards, N = stats.shape[0], stats.shape[1]
+    dev = stats.device
+    targets = targets.reshape(-1).to(torch.int64).contiguous()
+    _, merge_bytes, _ = _lib.flce_shard_workspace_size(N, 8, 1, _lib.FLCE_F32, False)
+    if workspace is None or workspace.numel() < merge_bytes:
+        workspace = torch.empty(max(merge_bytes, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(N if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_shard_merge(stats.data_ptr(), num_shards, targets.data_ptr(), N, int(V_total),
+                              float(label_smoothing), float(z_loss_scale), int(ignore_index),
+                              _reduction_code(reduction), loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), stream)
+    return loss, lse, n_valid
+
+
+def flce_shard_backward(x: torch.Tensor, W_shard: torch.Tensor, b_shard: Optional[torch.Tensor],
+                        targets: torch.Tensor, vocab_start: int, V_total: int, lse: torch.Tensor,
+                        n_valid: torch.Tensor, grad_loss: torch.Tensor, label_smoothing: float = 0.0,
+                        z_loss_scale: float = 0.0, ignore_index: int = -100, reduction: str = "mean",
+                        dx_partial: Optional[torch.Tensor] = None, accumulate_dx: bool = False,
+                        need_dx: bool = True, need_dW: bool = True, need_db: bool = True,
+                        workspace: Optional[torch.Tensor] = None):
+    """Returns (dx_partial float32 [N, H], dW_shard, db_shard) (None where not requested).
+    dx_partial: the buffer to write (or, with accumulate_dx, to add to); allocated if None."""
+    x, W_shard, b_shard, targets = _prep(x, W_shard, b_shard, targets)
+    N, H = x.shape
+    V_shard = W_shard.shape[0]
+    dt, red, dev = _dtype_code(x), _reduction_code(reduction), x.device
+    g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
+    if g.numel() != (N if reduction == "none" else 1):
+        raise ValueError("grad_loss must have N entries for none and one otherwise")
+    if dx_partial is not None:
+        if dx_partial.shape != (N, H) or dx_partial.dtype != torch.float32 or not dx_partial.is_contiguous():
+            raise ValueError("dx_partial must be a contiguous float32 [N, H] tensor")
+    elif need_dx:
+        if accumulate_dx:
+            raise ValueError("accumulate_dx needs dx_partial")
+        dx_partial = torch.empty(N, H, dtype=torch.float32, device=dev)
+    _, _, bwd_bytes = _lib.flce_shard_workspace_size(N, H, V_shard, dt, b_shard is not None)
+    if workspace is None or workspace.numel() < bwd_bytes:
+        workspace = torch.empty(max(bwd_bytes, 1), dtype=torch.uint8, device=dev)
+    dW = torch.empty_like(W_shard) if need_dW else None
+    db = torch.empty_like(b_shard) if (need_db and b_shard is not None) else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_shard_backward(x.data_ptr(), W_shard.data_ptr(), _ptr(b_shard), targets.data_ptr(), N, H,
+                                 V_shard, int(vocab_start), int(V_total), dt, float(label_smoothing),
+                                 float(z_loss_scale), int(ignore_index), red, lse.data_ptr(), n_valid.data_ptr(),
+                                 g.data_ptr(), _ptr(dx_partial), bool(accumulate_dx), _ptr(dW), _ptr(db),
+                                 workspace.data_ptr(), workspace.numel(), stream)
+    return dx_partial, dW, db
+
+
 class FusedLinearCrossEntropyFunction(torch.autograd.Function):
     """loss = FLCE(x, target, weight, bias); saves only lse and the count."""
 

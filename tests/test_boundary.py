@@ -154,3 +154,67 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def _sfwd(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, Vs=400, vs0=300, Vt=1000, dtype=0, eps=0.0, ign=-100,
+                stats=P2, ws=P2, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.flce_shard_forward(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"],
+                                  args["Vs"], args["vs0"], args["Vt"], args["dtype"], args["eps"], args["ign"],
+                                  args["stats"], args["ws"], args["wsb"], args["stream"])
+
+
+def _smerge(lib, **over):
+    args = dict(stats=P2, p=3, targets=P, N=64, Vt=1000, eps=0.0, s=0.0, ign=-100, red=2, loss=P2, lse=P2,
+                nv=P2, ws=P2, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.flce_shard_merge(args["stats"], args["p"], args["targets"], args["N"], args["Vt"], args["eps"],
+                                args["s"], args["ign"], args["red"], args["loss"], args["lse"], args["nv"],
+                                args["ws"], args["wsb"], args["stream"])
+
+
+def _sbwd(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, Vs=400, vs0=300, Vt=1000, dtype=0, eps=0.0, s=0.0,
+                ign=-100, red=2, lse=P2, nv=P2, g=P2, dx=P2, acc=0, dW=P2, db=None, ws=P2, wsb=1 << 30,
+                stream=None)
+    args.update(over)
+    return lib.flce_shard_backward(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"],
+                                   args["Vs"], args["vs0"], args["Vt"], args["dtype"], args["eps"], args["s"],
+                                   args["ign"], args["red"], args["lse"], args["nv"], args["g"], args["dx"],
+                                   args["acc"], args["dW"], args["db"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Vs=0), 1), (dict(vs0=-1), 1), (dict(vs0=700), 1), (dict(Vt=0), 1), (dict(Vt=(1 << 30) + 1), 1),
+    (dict(H=12), 2), (dict(eps=1.5), 1), (dict(stats=None), 1), (dict(stats=P2 + 4), 1), (dict(W=P + 2), 1),
+    (dict(wsb=16), 3), (dict(ws=None), 1),
+])
+def test_shard_forward_validation(lib, over, code):
+    assert _sfwd(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(p=0), 1), (dict(N=0), 1), (dict(Vt=0), 1), (dict(eps=-1.0), 1), (dict(red=5), 1),
+    (dict(stats=None), 1), (dict(stats=P2 + 8), 1), (dict(targets=None), 1), (dict(loss=None), 1),
+    (dict(wsb=64), 3), (dict(ws=None), 1),
+])
+def test_shard_merge_validation(lib, over, code):
+    assert _smerge(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Vs=0), 1), (dict(vs0=601), 1), (dict(Vt=500), 1), (dict(s=-1.0), 1), (dict(lse=None), 1),
+    (dict(g=None), 1), (dict(dx=P2 + 4), 1), (dict(dW=P2 + 8), 1), (dict(wsb=100), 3),
+])
+def test_shard_backward_validation(lib, over, code):
+    assert _sbwd(lib, **over) == code
+
+
+def test_shard_workspace_sizes(lib):
+    f, m, b = _lib.flce_shard_workspace_size(8192, 4096, 16032, _lib.FLCE_BF16, True)
+    ff, bb = _lib.flce_workspace_size(8192, 4096, 16032, _lib.FLCE_BF16, True, 2)
+    assert f == ff                                   # same forward partials
+    assert m >= 8192 * 4                             # per-row losses of the merge
+    assert b == bb - 8192 * 4096 * 4                 # no dx accumulator: the caller's fp32 buffer
+    assert _sbwd(lib, dx=None, dW=None, db=None) == 0   # nothing requested: no launch, OK
