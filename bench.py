@@ -4,6 +4,7 @@
     python bench.py --copy-probe BYTES          # one plain device copy of BYTES (counter calibration)
     python bench.py --summarize-trace DIR       # markdown table from a rocprofv3 --kernel-trace run
     python bench.py --summarize-pmc DIR         # markdown table from a rocprofv3 --pmc run
+    python bench.py --shards P                  # the vocabulary-shard path: P shards in sequence
 
 A step is one pass of the whole hot path over one batch: flce_forward (logits
 GEMM with the online log-sum-exp epilogue, combine, reduction) then
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     p.add_argument("--summarize-trace", default=None, metavar="DIR")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR")
+    p.add_argument("--shards", type=int, default=0, metavar="P",
+                   help="time the vocabulary-shard entry points: W split into P shards run one after another")
     return p.parse_args()
 
 
@@ -160,6 +163,55 @@ def cpu_baseline(inp, rows):
                       f"(logits computed twice), {dt:.2f} s"}
 
 
+def shard_bench(args, w, x, W, b, tg, g, name):
+    """A step of the shard path: P shard forwards, the merge, P shard backwards
+    summing the fp32 dx partials into one buffer (the cross-GPU sum and the final
+    cast of dx are the caller's and are not timed)."""
+    import torch
+    from lm_head_cross_flce_amd import functional as F
+
+    N, H, V, P = w.N, w.H, w.V, args.shards
+    cuts = [k * V // P for k in range(P + 1)]
+    dev = x.device
+    shards = [(a, e, W[a:e], b[a:e] if b is not None else None) for a, e in zip(cuts[:-1], cuts[1:])]
+    sizes = [F.flce_shard_workspace_size(N, H, e - a, x.dtype, b is not None) for a, e, _, _ in shards]
+    ws_f = torch.empty(max(s[0] for s in sizes), dtype=torch.uint8, device=dev)
+    ws_m = torch.empty(max(s[1] for s in sizes), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(s[2] for s in sizes), dtype=torch.uint8, device=dev)
+    dx = torch.empty(N, H, dtype=torch.float32, device=dev)
+
+    def step():
+        stats = torch.stack([F.flce_shard_forward(x, Ws, bs, tg, a, V, w.label_smoothing, w.ignore_index,
+                                                  workspace=ws_f) for a, e, Ws, bs in shards])
+        loss, lse, nv = F.flce_shard_merge(stats, tg, V, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                           w.reduction, workspace=ws_m)
+        for k, (a, e, Ws, bs) in enumerate(shards):
+            F.flce_shard_backward(x, Ws, bs, tg, a, V, lse, nv, g, w.label_smoothing, w.z_loss_scale,
+                                  w.ignore_index, w.reduction, dx_partial=dx, accumulate_dx=k > 0,
+                                  workspace=ws_b)
+        return loss
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    tflops = 8.0 * N * H * V / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": f"FLCE fwd+bwd tokens/s, vocabulary split into {P} shards run in sequence on one GPU",
+        "value": N * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64 draws, random-init weights)",
+        "config": {"workload": name, "N": N, "H": H, "V": V, "shards": P, "shard_rows": cuts[1] - cuts[0]},
+        "tflops_8nhv": tflops, "mfma_frac_8nhv": tflops / PEAK_BF16_TFLOPS, "loss": loss.item(),
+        "workspace_mb": (ws_f.numel() + ws_m.numel() + ws_b.numel()) / 1e6,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -212,6 +264,10 @@ def main():
     dx, dW = torch.empty_like(x), torch.empty_like(W)
     db = torch.empty_like(b) if b is not None else None
     stream = torch.cuda.current_stream(dev)
+
+    if args.shards > 0:
+        shard_bench(args, w, x, W, b, tg, g, name)
+        return
 
     def step(ev=None):
         if ev is not None:

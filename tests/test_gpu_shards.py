@@ -96,3 +96,56 @@ def test_merge_is_independent_of_shard_order():
     _, b = run_shards(inp, order=list(reversed(range(len(sh)))))
     assert a["n_valid"] == b["n_valid"]
     assert rel(b["lse"], a["lse"]) <= 1e-6 and rel(b["loss"], a["loss"]) <= 1e-6
+
+
+@pytest.mark.timeout(900)
+def test_full_size_eight_shards():
+    # The benchmarked Llama-3-sized head in 8 shards of 16032 rows (not tile
+    # aligned): lse, per-row losses and dx rows against the oracle on sampled
+    # rows; lse against the unsharded forward; dW and db bit-identical to the
+    # unsharded backward given the same lse (every dlogit is computed the same
+    # way and db's partials are summed in the same order).
+    name = "n8192_h4096_v128256"
+    inp = synth.make_inputs(synth.WORKLOADS[name])
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    P = 8
+    cuts = [k * w.V // P for k in range(P + 1)]
+    print(f"[gpu] full size {name}: {P} shards", flush=True)
+    stats = torch.stack([F.flce_shard_forward(x, W[a:e], b[a:e], t, a, w.V, w.label_smoothing, w.ignore_index)
+                         for a, e in zip(cuts[:-1], cuts[1:])])
+    loss, lse, nv = F.flce_shard_merge(stats, t, w.V, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                       w.reduction)
+    loss_none, _, _ = F.flce_shard_merge(stats, t, w.V, w.label_smoothing, w.z_loss_scale, w.ignore_index, "none")
+    dx = torch.empty(w.N, w.H, dtype=torch.float32, device=x.device)
+    dWs, dbs = [], []
+    for k, (a, e) in enumerate(zip(cuts[:-1], cuts[1:])):
+        _, dW, db = F.flce_shard_backward(x, W[a:e], b[a:e], t, a, w.V, lse, nv, g, w.label_smoothing,
+                                          w.z_loss_scale, w.ignore_index, w.reduction, dx_partial=dx,
+                                          accumulate_dx=k > 0)
+        dWs.append(dW)
+        dbs.append(db)
+    dW = torch.cat(dWs)
+    db = torch.cat(dbs)
+    del dWs, dbs, stats
+    torch.cuda.synchronize()
+    T = O.count_valid(inp.targets, w.ignore_index)
+    assert int(nv.item()) == T
+    np.testing.assert_allclose(loss.item(), loss_none.double().sum().item() / T, rtol=1e-5)
+    print(f"[gpu] full size {name}: unsharded run", flush=True)
+    _, ref_lse, _ = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    assert rel(lse.double().cpu().numpy(), ref_lse.double().cpu().numpy()) <= 1e-6
+    # the unsharded backward given the shards' merged lse: identical dlogits
+    ref_dx, ref_dW, ref_db = F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale,
+                                             w.ignore_index, w.reduction)
+    assert torch.equal(dW, ref_dW) and torch.equal(db, ref_db)
+    assert rel(to_f64(dx.to(torch.bfloat16)), to_f64(ref_dx)) <= 1e-2
+    del ref_dx, ref_dW, ref_db
+    torch.cuda.empty_cache()
+    rows = O.sample_rows(w.N, 12, seed=w.seed)
+    print(f"[gpu] full size {name}: oracle on {rows.size} rows", flush=True)
+    r = O.rows(synth.bf16_bits_to_f64(inp.x[rows]), inp.as_f64("W"), inp.as_f64("b"), inp.targets[rows], T,
+               inp.grad, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    assert rel(lse.cpu().numpy().astype(np.float64)[rows], r["lse"]) <= LSE_RTOL
+    assert rel(loss_none.cpu().numpy().astype(np.float64)[rows], r["row_loss"]) <= LOSS_RTOL
+    assert rel(dx[torch.from_numpy(rows).to(dx.device)].cpu().numpy().astype(np.float64), r["dx"]) <= GRAD_RTOL["bf16"]
