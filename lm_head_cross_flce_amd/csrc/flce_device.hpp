@@ -518,16 +518,26 @@ __device__ __forceinline__ void frag_read(Frag& f, const FragAddr<AK>& fa, const
 template <int RA, int RB, int PAR> struct StagePlan {
   static constexpr int kR1 = 4 * RA + 8 * RB, kR2 = 4 * RA;
   static constexpr int kC = PAR == 0 ? 16 : 0;
-  static constexpr int kC1 = kC < 32 - kR1 ? kC : 32 - kR1;   // copies in the first half
-  static constexpr int kMix = kC1 < kR1 ? kC1 : kR1;          // alternating copy/read pairs
-  static_assert(kR1 <= 32 && kR2 + (kC - kC1) <= 32, "at most one read or copy per MFMA slot");
-  static constexpr int kind1(int k) {
-    return k < 2 * kMix ? ((k & 1) ? 1 : 2)
-                        : (kR1 > kMix ? (k - 2 * kMix < kR1 - kMix ? 1 : 0) : (k - 2 * kMix < kC1 - kMix ? 2 : 0));
+  // copies every fourth slot of both halves; reads in the other slots, in order
+  static constexpr bool copy_slot(int k) { return kC > 0 && (k & 3) == 0; }
+  static constexpr int nonc_before(int k) { return kC > 0 ? k - (k + 3) / 4 : k; }   // non-copy slots before k
+  static constexpr int kind1(int k) { return copy_slot(k) ? 2 : (nonc_before(k) < kR1 ? 1 : 0); }
+  static constexpr int idx1(int k) { return copy_slot(k) ? k / 4 : nonc_before(k); }
+  static constexpr int kind2(int k) { return copy_slot(k) ? 2 : (nonc_before(k) < kR2 ? 1 : 0); }
+  static constexpr int idx2(int k) { return copy_slot(k) ? 8 + k / 4 : kR1 + nonc_before(k); }
+  // Every read and every copy is placed exactly once.
+  static constexpr bool complete() {
+    int reads = 0, copies = 0, rsum = 0, csum = 0;
+    for (int k = 0; k < 32; ++k) {
+      if (kind1(k) == 1) { ++reads; rsum += idx1(k); }
+      if (kind1(k) == 2) { ++copies; csum += idx1(k); }
+      if (kind2(k) == 1) { ++reads; rsum += idx2(k); }
+      if (kind2(k) == 2) { ++copies; csum += idx2(k); }
+    }
+    const int nr = kR1 + kR2;
+    return reads == nr && copies == kC && rsum == nr * (nr - 1) / 2 && csum == kC * (kC - 1) / 2;
   }
-  static constexpr int idx1(int k) { return k < 2 * kMix ? (k >> 1) : kMix + (k - 2 * kMix); }
-  static constexpr int kind2(int k) { return k < kR2 ? 1 : (k - kR2 < kC - kC1 ? 2 : 0); }
-  static constexpr int idx2(int k) { return k < kR2 ? kR1 + k : kC1 + (k - kR2); }
+  static_assert(complete(), "stage plan must place every read and copy once");
 };
 
 // One stage body: half PAR of the K block in buffer BUF.  A PAR 0 stage
