@@ -18,8 +18,10 @@ from __future__ import annotations
 import math
 
 
-def run(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100, reduction="mean"):
-    """Returns (loss, lse, row_loss, dx, dW, db) as nested Python lists."""
+def run(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100, reduction="mean", logit_scale=1.0):
+    """Returns (loss, lse, row_loss, dx, dW, db) as nested Python lists.  logit_scale
+    multiplies every logit (bias included) and the gradient of the raw logits (fla
+    cross_entropy_kernel)."""
     N = len(x)
     H = len(x[0])
     V = len(W)
@@ -31,7 +33,7 @@ def run(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100, reduction="me
             acc = math.fsum(float(x[n][h]) * float(W[j][h]) for h in range(H))
             if b is not None:
                 acc += float(b[j])
-            z.append(acc)
+            z.append(logit_scale * acc)
         m = max(z)
         d = math.fsum(math.exp(zj - m) for zj in z)
         lse = m + math.log(d)
@@ -57,7 +59,7 @@ def run(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100, reduction="me
             g = (1.0 + 2.0 * s * lse) * p - eps / V
             if j == y:
                 g -= 1.0 - eps
-            row.append(c * g)
+            row.append(c * logit_scale * g)
         dz_all.append(row)
     if reduction == "none":
         loss = list(row_loss)

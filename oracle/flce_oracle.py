@@ -34,6 +34,16 @@ definition, so this oracle is that definition written out in fp64:
   gradients       dx = dz W,  dW = dz^T x,  db_j = sum_n dz[n, j]
                   (fla forward driver: torch.mm(c_logits, weight),
                   c_logits.t() @ c_x, c_logits.sum(0))
+  logit scale     with logit_scale a, every formula above applies to the
+                  scaled logits a z (bias included), and the gradient of the
+                  raw logits is a times the dlogits of the scaled ones
+                  (fla forward driver: logsumexp_fwd(c_logits,
+                  scale=logit_scale); cross_entropy_kernel: the loaded logits
+                  and the target logit multiplied by logit_scale, and the
+                  gradient (exp(z - lse) - eps) * logit_scale with the target
+                  term (label_smoothing - 1) * logit_scale)
+  z-loss term     s lse^2 of a row, reported alone as well (0 for ignored
+                  rows), reduced like the loss
 
 Readings where the pages are silent or garbled (each is also listed in the
 design notes): all rows ignored gives loss 0 and zero gradients (the fla kernel
@@ -65,6 +75,8 @@ class ForwardResult:
     lse: np.ndarray         # [N]
     row_loss: np.ndarray    # [N], zero for ignored rows
     n_valid: int
+    z_loss: np.ndarray = None      # the z-loss term alone, reduced like loss
+    row_z_loss: np.ndarray = None  # [N]
 
 
 @dataclass
@@ -97,10 +109,12 @@ def _check(x, W, b, targets, eps, s, ignore_index, reduction):
     return N, H, V, t.astype(np.int64), valid
 
 
-def _logits(x64, W64, b64):
+def _logits(x64, W64, b64, scale=1.0):
     z = x64 @ W64.T
     if b64 is not None:
         z += b64[None, :]
+    if scale != 1.0:
+        z *= scale
     return z
 
 
@@ -129,14 +143,23 @@ def _coeff(t_valid, grad, reduction, T, rows):
     return np.where(t_valid, c, 0.0)
 
 
-def _dlogits(z, lse, t, valid, c, eps, s, V):
+def _dlogits(z, lse, t, valid, c, eps, s, V, scale=1.0):
+    """Gradient of the raw logits (before the logit scale), from the scaled z."""
     p = np.exp(z - lse[:, None])
     dz = (1.0 + 2.0 * s * lse)[:, None] * p - eps / V
     rows = np.arange(z.shape[0])
     tv = np.where(valid, t, 0)
     dz[rows, tv] -= np.where(valid, 1.0 - eps, 0.0)
-    dz *= c[:, None]
+    dz *= (c * scale)[:, None]
     return dz
+
+
+def _reduce(rows_v, reduction, T):
+    if reduction == "none":
+        return rows_v.copy()
+    if reduction == "sum":
+        return np.array([np.sum(rows_v)])
+    return np.array([np.sum(rows_v) / T if T > 0 else 0.0])
 
 
 def _f64(a):
@@ -156,8 +179,8 @@ def _pool():
 
 
 def forward(x, W, b, targets, eps=0.0, s=0.0, ignore_index=-100, reduction="mean",
-            rows_per_chunk=256) -> ForwardResult:
-    """Loss, per-row lse and the non-ignored count."""
+            rows_per_chunk=256, logit_scale=1.0) -> ForwardResult:
+    """Loss, per-row lse and the non-ignored count (and the z-loss term alone)."""
     N, H, V, t, valid = _check(x, W, b, targets, eps, s, ignore_index, reduction)
     W64, b64 = _f64(W), _f64(b)
     lse = np.empty(N)
@@ -165,24 +188,19 @@ def forward(x, W, b, targets, eps=0.0, s=0.0, ignore_index=-100, reduction="mean
 
     def work(c):
         lo, hi = c
-        z = _logits(_f64(x[lo:hi]), W64, b64)
+        z = _logits(_f64(x[lo:hi]), W64, b64, logit_scale)
         lse[lo:hi] = _lse(z)
         rl[lo:hi] = _row_loss(z, lse[lo:hi], t[lo:hi], valid[lo:hi], eps, s, V)
 
     with _pool() as ex:
         list(ex.map(work, _chunks(N, rows_per_chunk)))
     T = int(np.sum(valid))
-    if reduction == "none":
-        loss = rl.copy()
-    elif reduction == "sum":
-        loss = np.array([np.sum(rl)])
-    else:
-        loss = np.array([np.sum(rl) / T if T > 0 else 0.0])
-    return ForwardResult(loss, lse, rl, T)
+    rzl = np.where(valid, s * lse * lse, 0.0)
+    return ForwardResult(_reduce(rl, reduction, T), lse, rl, T, _reduce(rzl, reduction, T), rzl)
 
 
 def backward(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
-             reduction="mean", rows_per_chunk=256) -> BackwardResult:
+             reduction="mean", rows_per_chunk=256, logit_scale=1.0) -> BackwardResult:
     """dx, dW and db of the reduced loss, scaled by the upstream gradient."""
     N, H, V, t, valid = _check(x, W, b, targets, eps, s, ignore_index, reduction)
     W64, b64 = _f64(W), _f64(b)
@@ -194,10 +212,10 @@ def backward(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
     def work(k):
         lo, hi = chunks[k]
         x64 = _f64(x[lo:hi])
-        z = _logits(x64, W64, b64)
+        z = _logits(x64, W64, b64, logit_scale)
         lse = _lse(z)
         c = _coeff(valid[lo:hi], grad, reduction, T, np.arange(lo, hi))
-        dz = _dlogits(z, lse, t[lo:hi], valid[lo:hi], c, eps, s, V)
+        dz = _dlogits(z, lse, t[lo:hi], valid[lo:hi], c, eps, s, V, logit_scale)
         dx[lo:hi] = dz @ W64
         parts[k] = (dz.T @ x64, dz.sum(axis=0))
 
@@ -219,7 +237,7 @@ def backward(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
 
 
 def rows(x_rows, W, b, targets_rows, T, grad_rows, eps=0.0, s=0.0, ignore_index=-100,
-         reduction="mean"):
+         reduction="mean", logit_scale=1.0):
     """Per-row outputs for a subset of rows, computed one row block at a time.
 
     ``T`` is the non-ignored count of the whole batch (it fixes the mean's
@@ -235,7 +253,7 @@ def rows(x_rows, W, b, targets_rows, T, grad_rows, eps=0.0, s=0.0, ignore_index=
     valid = t != ignore_index
     if np.any(valid & ((t < 0) | (t >= V))):
         raise ValueError("a non-ignored target lies outside [0, V)")
-    z = _logits(x64, W64, b64)
+    z = _logits(x64, W64, b64, logit_scale)
     lse = _lse(z)
     rl = _row_loss(z, lse, t, valid, eps, s, V)
     g = np.asarray(grad_rows, dtype=np.float64).reshape(-1)
@@ -245,7 +263,7 @@ def rows(x_rows, W, b, targets_rows, T, grad_rows, eps=0.0, s=0.0, ignore_index=
         c = np.where(valid, g[0], 0.0)
     else:
         c = np.where(valid, g[0] / T if T > 0 else 0.0, 0.0)
-    dz = _dlogits(z, lse, t, valid, c, eps, s, V)
+    dz = _dlogits(z, lse, t, valid, c, eps, s, V, logit_scale)
     return {"lse": lse, "row_loss": rl, "dz": dz, "dx": dz @ W64}
 
 
@@ -254,10 +272,10 @@ def count_valid(targets, ignore_index=-100) -> int:
 
 
 def loss_and_grads(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
-                   reduction="mean", rows_per_chunk=256):
+                   reduction="mean", rows_per_chunk=256, logit_scale=1.0):
     """Forward and backward in one pass over row chunks (the oracle timing leg)."""
-    f = forward(x, W, b, targets, eps, s, ignore_index, reduction, rows_per_chunk)
-    g = backward(x, W, b, targets, grad, eps, s, ignore_index, reduction, rows_per_chunk)
+    f = forward(x, W, b, targets, eps, s, ignore_index, reduction, rows_per_chunk, logit_scale)
+    g = backward(x, W, b, targets, grad, eps, s, ignore_index, reduction, rows_per_chunk, logit_scale)
     return f, g
 
 

@@ -331,15 +331,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
     good_dlogits, good_row_loss, good_lse = O._dlogits, O._row_loss, O._lse
 
     # 1. sign of the eps/V term flipped (the garbled inline form on the PR page)
-    def bad_sign(z, lse, t, valid, c, eps, s, V):
-        return good_dlogits(z, lse, t, valid, c, eps, s, V) + 2 * c[:, None] * eps / V
+    def bad_sign(z, lse, t, valid, c, eps, s, V, scale=1.0):
+        return good_dlogits(z, lse, t, valid, c, eps, s, V, scale) + 2 * scale * c[:, None] * eps / V
     monkeypatch.setattr(O, "_dlogits", bad_sign)
     assert _fd_error() > 1e-3
     monkeypatch.setattr(O, "_dlogits", good_dlogits)
 
     # 2. z-loss term dropped from the gradient
-    def no_zloss_grad(z, lse, t, valid, c, eps, s, V):
-        return good_dlogits(z, lse, t, valid, c, eps, 0.0, V)
+    def no_zloss_grad(z, lse, t, valid, c, eps, s, V, scale=1.0):
+        return good_dlogits(z, lse, t, valid, c, eps, 0.0, V, scale)
     monkeypatch.setattr(O, "_dlogits", no_zloss_grad)
     assert _fd_error() > 1e-3
     monkeypatch.setattr(O, "_dlogits", good_dlogits)
@@ -361,3 +361,123 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "_row_loss", bad_loss)
     assert _fd_error() > 1e-3
     monkeypatch.setattr(O, "_row_loss", good_row_loss)
+
+
+# --- logit_scale (fla cross_entropy_kernel; forward driver's scaled lse) -------
+
+@pytest.mark.parametrize("alpha", [0.5, 2.5, -1.3])
+@pytest.mark.parametrize("red", RED)
+def test_logit_scale_equals_scaled_weights_chain_rule(alpha, red):
+    # a (x W^T + b) = x (a W)^T + a b: the same loss; by the chain rule dx is
+    # the same and the weight and bias gradients are a times those of (aW, ab).
+    rng = np.random.default_rng(31)
+    x, W, b, t = _rand_problem(rng, 9, 6, 14, n_ign=2)
+    g = _grad(rng, red, 9)
+    kw = dict(eps=0.1, s=1e-2, reduction=red)
+    f1 = O.forward(x, W, b, t, logit_scale=alpha, **kw)
+    f2 = O.forward(x, alpha * W, alpha * b, t, **kw)
+    np.testing.assert_allclose(f1.loss, f2.loss, rtol=1e-12)
+    np.testing.assert_allclose(f1.lse, f2.lse, rtol=1e-12)
+    np.testing.assert_allclose(f1.z_loss, f2.z_loss, rtol=1e-12)
+    b1 = O.backward(x, W, b, t, g, logit_scale=alpha, **kw)
+    b2 = O.backward(x, alpha * W, alpha * b, t, g, **kw)
+    np.testing.assert_allclose(b1.dx, b2.dx, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(b1.dW, alpha * b2.dW, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(b1.db, alpha * b2.db, rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("alpha,eps,red", [(0.7, 0.0, "mean"), (3.0, 0.2, "sum"), (-0.4, 0.05, "none")])
+def test_logit_scale_matches_torch_cross_entropy(alpha, eps, red):
+    # PyTorch fp64 cross entropy of the scaled logits, with autograd gradients
+    # (s = 0: torch has no z-loss).
+    rng = np.random.default_rng(32)
+    x, W, b, t = _rand_problem(rng, 8, 5, 11, n_ign=1)
+    g = _grad(rng, red, 8)
+    xt = torch.tensor(x, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    z = alpha * (xt @ Wt.T + bt)
+    loss = torch.nn.functional.cross_entropy(z, torch.tensor(t), ignore_index=-100, label_smoothing=eps,
+                                             reduction=red)
+    (loss * torch.tensor(g if red == "none" else g[0])).sum().backward()
+    f = O.forward(x, W, b, t, eps=eps, reduction=red, logit_scale=alpha)
+    bw = O.backward(x, W, b, t, g, eps=eps, reduction=red, logit_scale=alpha)
+    np.testing.assert_allclose(f.loss, np.atleast_1d(loss.detach().numpy()), rtol=1e-12)
+    np.testing.assert_allclose(bw.dx, xt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(bw.dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(bw.db, bt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def _fd_error_scaled(alpha=1.7):
+    rng = np.random.default_rng(33)
+    N, H, V = 4, 3, 6
+    x, W, b, t = _rand_problem(rng, N, H, V, n_ign=1, scale=2.0)
+    g = np.array([0.9])
+    kw = dict(eps=0.1, s=1e-2, reduction="mean", logit_scale=alpha)
+    bw = O.backward(x, W, b, t, g, **kw)
+    h = 1e-5
+    num_W = np.zeros_like(W)
+    for idx in np.ndindex(W.shape):
+        old = W[idx]
+        W[idx] = old + h
+        fp = O.forward(x, W, b, t, **kw).loss[0] * g[0]
+        W[idx] = old - h
+        fm = O.forward(x, W, b, t, **kw).loss[0] * g[0]
+        W[idx] = old
+        num_W[idx] = (fp - fm) / (2 * h)
+    num_b = np.zeros_like(b)
+    for j in range(V):
+        old = b[j]
+        b[j] = old + h
+        fp = O.forward(x, W, b, t, **kw).loss[0] * g[0]
+        b[j] = old - h
+        fm = O.forward(x, W, b, t, **kw).loss[0] * g[0]
+        b[j] = old
+        num_b[j] = (fp - fm) / (2 * h)
+    return max(np.max(np.abs(num_W - bw.dW)) / np.max(np.abs(num_W)),
+               np.max(np.abs(num_b - bw.db)) / np.max(np.abs(num_b)))
+
+
+def test_logit_scale_finite_differences():
+    assert _fd_error_scaled() < 1e-6
+
+
+def test_logit_scale_planted_mistake_is_caught(monkeypatch):
+    good = O._dlogits
+
+    def unscaled(z, lse, t, valid, c, eps, s, V, scale=1.0):   # forgets the scale on the gradient
+        return good(z, lse, t, valid, c, eps, s, V, 1.0)
+    monkeypatch.setattr(O, "_dlogits", unscaled)
+    assert _fd_error_scaled() > 1e-3
+
+
+def test_logit_scale_brute_force_agrees():
+    rng = np.random.default_rng(34)
+    x, W, b, t = _rand_problem(rng, 5, 4, 7, n_ign=1)
+    g = np.array([1.3])
+    loss, lse, rl, dx, dW, db = brute.run(x.tolist(), W.tolist(), b.tolist(), t.tolist(), g.tolist(), eps=0.1,
+                                          s=1e-2, reduction="mean", logit_scale=-2.2)
+    f = O.forward(x, W, b, t, eps=0.1, s=1e-2, reduction="mean", logit_scale=-2.2)
+    bw = O.backward(x, W, b, t, g, eps=0.1, s=1e-2, reduction="mean", logit_scale=-2.2)
+    np.testing.assert_allclose(f.loss, loss, rtol=1e-12)
+    np.testing.assert_allclose(bw.dx, dx, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(bw.dW, dW, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(bw.db, db, rtol=1e-11, atol=1e-14)
+
+
+# --- z-loss term reported alone (PR 239: L_total = L_ce + s lse^2) -------------
+
+@pytest.mark.parametrize("red", RED)
+def test_z_loss_term_alone(red):
+    rng = np.random.default_rng(35)
+    x, W, b, t = _rand_problem(rng, 10, 6, 13, n_ign=3)
+    s = 3e-2
+    f = O.forward(x, W, b, t, eps=0.1, s=s, reduction=red)
+    f0 = O.forward(x, W, b, t, eps=0.1, s=0.0, reduction=red)
+    # the CE part is unchanged: loss(s) - z_loss(s) = loss(s = 0)
+    np.testing.assert_allclose(f.loss - f.z_loss, f0.loss, rtol=1e-12, atol=1e-14)
+    lse = torch.logsumexp(torch.tensor(x @ W.T + b), dim=1).numpy()
+    valid = t != -100
+    rows = np.where(valid, s * lse * lse, 0.0)
+    expect = {"none": rows, "sum": [rows.sum()], "mean": [rows.sum() / valid.sum()]}[red]
+    np.testing.assert_allclose(f.z_loss, expect, rtol=1e-12)
