@@ -85,6 +85,7 @@ typedef enum {
  */
 flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias,
                                 int reduction, size_t* fwd_bytes, size_t* bwd_bytes);
+/* (The figures also cover the _ex entry points.) */
 
 /*
  * Forward: writes
@@ -118,6 +119,44 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
                           const float* grad_loss,
                           void* dx, void* dW, void* db,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Options of the _ex entry points (a NULL options pointer means the
+ * defaults, which make them equal to flce_forward / flce_backward):
+ *  logit_scale  the logits are logit_scale * (x W^T + b), as fla's
+ *               fused_linear_cross_entropy_loss scales them (its
+ *               cross_entropy_kernel multiplies the loaded logits by
+ *               logit_scale before the softmax and the gradient of the raw
+ *               logits by logit_scale); lse, the loss and the z-loss are those
+ *               of the scaled logits.  Any finite value; default 1.
+ *  accumulate   backward: add dx, dW and db to what those buffers hold
+ *               (summed in fp32, rounded once to the input dtype) instead of
+ *               overwriting them, as Liger-Kernel commit 95b01e9 adds each
+ *               chunk's weight gradient into grad_weight.  Default 0.
+ *  z_loss       forward: if non-NULL, also receives the z-loss term
+ *               s * lse^2 alone, float32 [1] (sum/mean, reduced like loss) or
+ *               [N] (none; 0 for ignored rows).  Default NULL.
+ */
+typedef struct flce_options {
+  float logit_scale;
+  int accumulate;
+  float* z_loss;
+} flce_options;
+
+flce_status flce_forward_ex(const void* x, const void* W, const void* b, const int64_t* targets,
+                            int64_t N, int64_t H, int64_t V, int dtype,
+                            float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                            int reduction, const flce_options* opts,
+                            float* loss, float* lse, int64_t* n_valid,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+flce_status flce_backward_ex(const void* x, const void* W, const void* b, const int64_t* targets,
+                             int64_t N, int64_t H, int64_t V, int dtype,
+                             float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                             int reduction, const flce_options* opts,
+                             const float* lse, const int64_t* n_valid, const float* grad_loss,
+                             void* dx, void* dW, void* db,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Vocabulary shards.  DeepSpeed PR 8792 ("What"; "Memory and time") splits W's

@@ -24,9 +24,15 @@ FLCE_BF16 = 1
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 
 # Every symbol the public header declares.
-EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_status_string",
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex", "flce_backward_ex",
+           "flce_status_string",
            "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
            "flce_shard_backward")
+
+class FlceOptions(ctypes.Structure):
+    """struct flce_options of flce.h."""
+    _fields_ = [("logit_scale", ctypes.c_float), ("accumulate", ctypes.c_int), ("z_loss", ctypes.c_void_p)]
+
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +65,13 @@ def load() -> ctypes.CDLL:
         lib.flce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int,
                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flce_backward.restype = c_int
+        opt = ctypes.POINTER(FlceOptions)
+        lib.flce_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                        vp, vp, vp, vp, sz, vp]
+        lib.flce_forward_ex.restype = c_int
+        lib.flce_backward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flce_backward_ex.restype = c_int
         lib.flce_status_string.argtypes = [c_int]
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
@@ -150,3 +163,27 @@ def flce_shard_backward(x, W_shard, b_shard, targets, N, H, V_shard, vocab_start
                                       grad_loss, dx_partial or None, int(bool(accumulate_dx)), dW_shard or None,
                                       db_shard or None, workspace, workspace_bytes, stream or None),
            "flce_shard_backward")
+
+
+def options(logit_scale: float = 1.0, accumulate: bool = False, z_loss=None) -> FlceOptions:
+    """An flce_options value; z_loss is an integer device address or None."""
+    return FlceOptions(float(logit_scale), int(bool(accumulate)), z_loss or None)
+
+
+def flce_forward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                    reduction, opts, loss, lse, n_valid, workspace, workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_forward_ex(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                  ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
+                                  loss, lse, n_valid, workspace, workspace_bytes, stream or None),
+           "flce_forward_ex")
+
+
+def flce_backward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                     reduction, opts, lse, n_valid, grad_loss, dx, dW, db, workspace, workspace_bytes,
+                     stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_backward_ex(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                   ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
+                                   lse, n_valid, grad_loss, dx or None, dW or None, db or None, workspace,
+                                   workspace_bytes, stream or None), "flce_backward_ex")

@@ -23,7 +23,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Geometry {
   int NT, VT, P;
   int64_t slab_cols;
-  size_t off_partials, off_rowloss, fwd_total;
+  size_t off_partials, off_rowloss, off_rowzl, fwd_total;
   size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, bwd_total;
 };
 
@@ -78,6 +78,8 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   g.off_partials = off;
   off = align_up(off + (size_t)P * N * 16);
   g.off_rowloss = off;
+  off = align_up(off + (size_t)N * 4);
+  g.off_rowzl = off;
   off = align_up(off + (size_t)N * 4);
   g.fwd_total = off;
 
@@ -148,6 +150,14 @@ flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int d
   return FLCE_OK;
 }
 
+flce_options default_options() {
+  flce_options o{};
+  o.logit_scale = 1.f;
+  o.accumulate = 0;
+  o.z_loss = nullptr;
+  return o;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,6 +194,17 @@ flce_status flce_forward(const void* x, const void* W, const void* b, const int6
                          int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
                          int64_t ignore_index, int reduction, float* loss, float* lse, int64_t* n_valid,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return flce_forward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
+                         nullptr, loss, lse, n_valid, workspace, workspace_bytes, stream);
+}
+
+flce_status flce_forward_ex(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                            int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
+                            int64_t ignore_index, int reduction, const flce_options* opts, float* loss, float* lse,
+                            int64_t* n_valid, void* workspace, size_t workspace_bytes, void* stream) {
+  const flce_options o = opts ? *opts : default_options();
+  if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (o.z_loss && !aligned(o.z_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status st = check_shape(N, H, V, dtype);
   if (st != FLCE_OK) return st;
   if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
@@ -204,8 +225,11 @@ flce_status flce_forward(const void* x, const void* W, const void* b, const int6
   a.eps_over_v = (float)((double)label_smoothing / (double)V);
   a.s = z_loss_scale;
   a.reduction = reduction;
+  a.logit_scale = o.logit_scale;
   a.partials = ws + g.off_partials;
   a.rowloss = (float*)(ws + g.off_rowloss);
+  a.rowzl = (float*)(ws + g.off_rowzl);
+  a.zloss = o.z_loss;
   a.loss = loss; a.lse = lse; a.n_valid = n_valid;
   (void)hipGetLastError();
   if (flce::launch_forward(a, dtype, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
@@ -217,6 +241,17 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
                           int64_t ignore_index, int reduction, const float* lse, const int64_t* n_valid,
                           const float* grad_loss, void* dx, void* dW, void* db, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  return flce_backward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
+                          nullptr, lse, n_valid, grad_loss, dx, dW, db, workspace, workspace_bytes, stream);
+}
+
+flce_status flce_backward_ex(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                             int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
+                             int64_t ignore_index, int reduction, const flce_options* opts, const float* lse,
+                             const int64_t* n_valid, const float* grad_loss, void* dx, void* dW, void* db,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const flce_options o = opts ? *opts : default_options();
+  if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status st = check_shape(N, H, V, dtype);
   if (st != FLCE_OK) return st;
   if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
@@ -240,7 +275,9 @@ flce_status flce_backward(const void* x, const void* W, const void* b, const int
   a.eps = label_smoothing;
   a.eps_over_v = (float)((double)label_smoothing / (double)V);
   a.s = z_loss_scale;
+  a.logit_scale = o.logit_scale;
   a.reduction = reduction;
+  a.accumulate = o.accumulate != 0;
   a.lse = lse; a.n_valid = n_valid; a.grad = grad_loss;
   a.coef = ws + g.off_coef;
   a.yv = (int*)(ws + g.off_yv);
@@ -286,6 +323,7 @@ flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b
   a.vocab_start = vocab_start;
   a.ignore_index = ignore_index;
   a.eps = label_smoothing;
+  a.logit_scale = 1.f;
   a.partials = ws + g.off_partials;
   a.stats = stats;
   (void)hipGetLastError();
@@ -315,6 +353,7 @@ flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64
   a.eps = label_smoothing;
   a.eps_over_v = (float)((double)label_smoothing / (double)V_total);
   a.s = z_loss_scale;
+  a.logit_scale = 1.f;
   a.reduction = reduction;
   a.partials = const_cast<float*>(stats);
   a.rowloss = (float*)workspace;
@@ -355,6 +394,7 @@ flce_status flce_shard_backward(const void* x, const void* W_shard, const void* 
   a.eps = label_smoothing;
   a.eps_over_v = (float)((double)label_smoothing / (double)V_total);
   a.s = z_loss_scale;
+  a.logit_scale = 1.f;
   a.reduction = reduction;
   a.lse = lse; a.n_valid = n_valid; a.grad = grad_loss;
   a.coef = ws + g.off_coef;

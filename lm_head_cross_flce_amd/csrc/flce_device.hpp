@@ -131,7 +131,7 @@ template <class T> struct BiasTile {
       v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)tid * 4u, 0, 0));
     }
   }
-  __device__ __forceinline__ void publish(lds_f32* dst, int tid) const { dst[tid] = v; }
+  __device__ __forceinline__ void publish(lds_f32* dst, int tid, float scale = 1.f) const { dst[tid] = v * scale; }
 };
 
 // Bias of tile rows row .. row + 3 (row a multiple of 4).

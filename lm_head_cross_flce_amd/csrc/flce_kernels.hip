@@ -43,11 +43,12 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 
 // Fold column j of a tile (this lane's 32 rows of one token) into the running
 // (m, d) of that token, the running sum of logits, and the target logit.
+// Logits are scale * acc + bias, the bias already multiplied by scale.
 // rb: tile row index of the lane's row 0 (v0 + wave row offset + 4 g); t: the
 // token's target minus rb (negative if ignored or elsewhere).
 template <bool SMOOTH, bool RAGGED>
-__device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&bias)[8], float& m, float& d,
-                                           float& sz, float& zy, int t, int rb, int V) {
+__device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&bias)[8], float scale, float& m,
+                                           float& d, float& sz, float& zy, int t, int rb, int V) {
   float z[32];
   float bmax = -INFINITY, zs = 0.f;
 #pragma unroll
@@ -55,7 +56,7 @@ __device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&
     const f32x4 v = acc_read4(acc[i][j]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float x = v[r] + bias[i][r];
+      float x = fmaf(v[r], scale, bias[i][r]);
       if (RAGGED) {
         const bool ok = rb + 16 * i + r < V;
         if (SMOOTH) zs += ok ? x : 0.f;
@@ -148,7 +149,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     }
     f32x4 bias[8];
     if (BIAS) {
-      bt.publish(L.bias, tid);
+      bt.publish(L.bias, tid, a.logit_scale);
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < 8; ++i) bias[i] = read_bias4(L.bias, rloc + 16 * i);
@@ -161,8 +162,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     acc_drain();
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (full) lse_column<SMOOTH, false>(acc, j, bias, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
-      else lse_column<SMOOTH, true>(acc, j, bias, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      if (full) lse_column<SMOOTH, false>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      else lse_column<SMOOTH, true>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
       // One column at a time keeps the live logits to 32 registers.
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -212,10 +213,15 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdLaunch a) {
   }
   const float lse = m + logf(d);
   const bool valid = a.targets[n] != a.ignore_index;
-  const float l = valid ? (lse - (1.f - a.eps) * zy - a.eps_over_v * sz + a.s * lse * lse) : 0.f;
+  const float zl = valid ? a.s * lse * lse : 0.f;
+  const float l = valid ? (lse - (1.f - a.eps) * zy - a.eps_over_v * sz) + zl : 0.f;
   a.lse[n] = lse;
   a.rowloss[n] = l;
   if (a.reduction == kNone) a.loss[n] = l;
+  if (a.zloss) {
+    a.rowzl[n] = zl;
+    if (a.reduction == kNone) a.zloss[n] = zl;
+  }
 }
 
 // Shard forward: the phases' partials of each token merged into one
@@ -237,28 +243,35 @@ __global__ void __launch_bounds__(256) fwd_stats_kernel(FwdLaunch a) {
 
 __global__ void __launch_bounds__(1024) fwd_finalize_kernel(FwdLaunch a) {
   __shared__ double ssum[1024];
+  __shared__ double zsum[1024];
   __shared__ long long scnt[1024];
   const int tid = threadIdx.x;
-  double s = 0.0;
+  double s = 0.0, z = 0.0;
   long long c = 0;
   for (int n = tid; n < a.N; n += 1024) {
     s += (double)a.rowloss[n];
+    if (a.zloss) z += (double)a.rowzl[n];
     c += (a.targets[n] != a.ignore_index) ? 1 : 0;
   }
   ssum[tid] = s;
+  zsum[tid] = z;
   scnt[tid] = c;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
     if (tid < w) {
       ssum[tid] += ssum[tid + w];
+      zsum[tid] += zsum[tid + w];
       scnt[tid] += scnt[tid + w];
     }
     __syncthreads();
   }
   if (tid == 0) {
-    a.n_valid[0] = scnt[0];
+    const long long T = scnt[0];
+    a.n_valid[0] = T;
     if (a.reduction == kSum) a.loss[0] = (float)ssum[0];
-    if (a.reduction == kMean) a.loss[0] = scnt[0] > 0 ? (float)(ssum[0] / (double)scnt[0]) : 0.f;
+    if (a.reduction == kMean) a.loss[0] = T > 0 ? (float)(ssum[0] / (double)T) : 0.f;
+    if (a.zloss && a.reduction == kSum) a.zloss[0] = (float)zsum[0];
+    if (a.zloss && a.reduction == kMean) a.zloss[0] = T > 0 ? (float)(zsum[0] / (double)T) : 0.f;
   }
 }
 
@@ -316,6 +329,8 @@ __global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
   if (a.reduction == kMean) c = T > 0 ? g / (float)T : 0.f;
   if (!valid) c = 0.f;
   const float lse = a.lse[n];
+  // Gradients of the raw logits: the logits' scale multiplies every term.
+  c *= a.logit_scale;
   ((f32x4*)a.coef)[n] = f32x4{c * (1.f + 2.f * a.s * lse), c * a.eps_over_v, c * (1.f - a.eps), lse * kLog2e};
   const int64_t lt = t - a.vocab_start;   // row of W holding the target, if any
   a.yv[n] = (valid && lt >= 0 && lt < a.V) ? (int)lt : -1;
@@ -416,6 +431,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // columns and the input-gradient kernel multiplies them by zero rows of W.
   // Slab rows of this tile's tokens, from token n0 on.
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
+  const float sl2e = a.logit_scale * kLog2e;   // p = 2^((scale (z + b)) log2 e - lse log2 e)
   // Bands s of 32 wave rows (blocks 2s, 2s + 1), token blocks j within them:
   // dlogits of the lane's token (16 j + l % 16) at its rows r0 .. r0 + 3 and
   // r1 .. r1 + 3 (tile-relative), the band's db row sums, and the slab store.
@@ -440,8 +456,8 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
       float dz[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        dz[r] = fmaf(cf[0], fast_exp2(fmaf(z0[r] + bias0[r], kLog2e, -cf[3])), -cf[1]);
-        dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(z1[r] + bias1[r], kLog2e, -cf[3])), -cf[1]);
+        dz[r] = fmaf(cf[0], fast_exp2(fmaf(z0[r] + bias0[r], sl2e, -cf[3])), -cf[1]);
+        dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(z1[r] + bias1[r], sl2e, -cf[3])), -cf[1]);
       }
       const int t0 = y - (v0 + r0), t1 = y - (v0 + r1);
       if (__ballot((t0 >= 0 && t0 < 4) || (t1 >= 0 && t1 < 4))) {
@@ -541,12 +557,28 @@ __device__ __forceinline__ void slab_db(const BwdLaunch& a, int vs, int width, i
   if (c >= width) return;
   float s = 0.f;
   for (int t = 0; t < a.NT; ++t) s += a.dbp[(int64_t)t * a.ldS + c];
-  if constexpr (sizeof(T) == 4) ((float*)a.db)[vs + c] = s;
-  else ((uint16_t*)a.db)[vs + c] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
+  if constexpr (sizeof(T) == 4) {
+    float* p = (float*)a.db + vs + c;
+    *p = a.accumulate ? *p + s : s;
+  } else {
+    uint16_t* p = (uint16_t*)a.db + vs + c;
+    if (a.accumulate) s += bf16_bits_to_f32(*p);
+    *p = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
+  }
 }
 
-// dW[vs + v, h] for the slab: C[h][v] = sum_n x[n][h] dz[n][v].
-template <class T>
+// Four consecutive output values added to what p holds (accumulate mode).
+template <class T> __device__ __forceinline__ f32x4 load4(const T* p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) { return *(const f32x4*)p; }
+template <> __device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const u32x2 v = *(const u32x2*)p;
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+               __uint_as_float(v[1] & 0xffff0000u)};
+}
+
+// dW[vs + v, h] for the slab: C[h][v] = sum_n x[n][h] dz[n][v].  ACC: added
+// to what dW holds.
+template <class T, bool ACC>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int TN) {
   FLCE_LDS(L, T);
@@ -569,9 +601,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
     T* rowp = dW + (int64_t)(vs + v) * a.H;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const f32x4 z = acc_read4(acc[i][j]);
+      f32x4 z = acc_read4(acc[i][j]);
       const int h = h0 + wm * kWaveTile + 16 * i + 4 * g;
-      if (v < width && h < a.H) store4<T>(rowp + h, z[0], z[1], z[2], z[3]);
+      if (v < width && h < a.H) {
+        if (ACC) z += load4<T>(rowp + h);
+        store4<T>(rowp + h, z[0], z[1], z[2], z[3]);
+      }
     }
   }
 }
@@ -592,7 +627,20 @@ __device__ __forceinline__ void store4_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
   }
 }
 
-template <class T, int MODE>
+template <class T>
+__device__ __forceinline__ f32x4 load4_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(f32x4, buf_load16(r, off));
+  } else {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+                 __uint_as_float(v[1] & 0xffff0000u)};
+  }
+}
+
+// ACC (modes that write dx in its dtype): dx is added to what it holds; its
+// old values are loaded ahead with the accumulator's.
+template <class T, int MODE, bool ACC>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -623,17 +671,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   // one CU's share of HBM bandwidth needs while every CU makes its
   // read-modify-write at the same moment.
   constexpr int kAhead = 12;
-  f32x4 old[kAhead + 1];
-  if (kRead) {
+  constexpr bool kOld = ACC && !kAcc;   // read the dx being added to
+  f32x4 old[kAhead + 1], oldx[kAhead + 1];
 #pragma unroll
-    for (int b = 0; b < kAhead; ++b) old[b] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b, 4u)));
+  for (int b = 0; b < kAhead; ++b) {
+    if (kRead) old[b] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b, 4u)));
+    if (kOld) oldx[b] = load4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)));
   }
 #pragma unroll
   for (int b = 0; b < 64; ++b) {
     const int bn = b + kAhead;
     if (kRead && bn < 64) old[bn % (kAhead + 1)] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn, 4u)));
+    if (kOld && bn < 64) oldx[bn % (kAhead + 1)] = load4_buf<T>(rdx, boff(bn, (uint32_t)sizeof(T)));
     f32x4 v = acc_read4(acc[b & 7][b >> 3]);
     if (kRead) v += old[b % (kAhead + 1)];
+    if (kOld) v += oldx[b % (kAhead + 1)];
     if (kAcc) {
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(b, 4u), 0, 0);
     } else {
@@ -667,12 +719,16 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   if (a.dx) {
     const dim3 gdx(TH * a.NT);
-    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    const bool acc = a.accumulate != 0;
+    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (dx_mode == kDxLast && !acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else if (!acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH);
   }
-  if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  if (a.dW && a.accumulate) hipLaunchKernelGGL((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  else if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
   else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
   return hipGetLastError();
 }

@@ -16,6 +16,7 @@ struct FwdLaunch {
   int64_t vocab_start;    // global index of W's row 0; targets are global indices
   int64_t ignore_index;
   float eps, eps_over_v, s;
+  float logit_scale;      // logits are logit_scale * (x W^T + b)
   int reduction;
   void* partials;         // float4 [P][N]
   float* rowloss;         // [N]
@@ -23,6 +24,8 @@ struct FwdLaunch {
   float* lse;             // [N]
   int64_t* n_valid;       // [1]
   float* stats;           // shard forward: float4 [N] {m, d, sum z, z_y} over the shard's rows
+  float* zloss;           // optional: the z-loss term alone, [1] or [N] like loss; null if not wanted
+  float* rowzl;           // [N] per-row z-loss terms (workspace), used when zloss is set
 };
 
 struct BwdLaunch {
@@ -32,7 +35,9 @@ struct BwdLaunch {
   int64_t vocab_start;    // global index of W's row 0; targets are global indices
   int64_t ignore_index;
   float eps, eps_over_v, s;
+  float logit_scale;      // logits are logit_scale * (x W^T + b)
   int reduction;
+  int accumulate;         // add dx, dW, db to what the outputs hold
   const float* lse; const int64_t* n_valid; const float* grad;
   void* coef;             // float4 [N]
   int* yv;                // [N]

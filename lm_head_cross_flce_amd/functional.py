@@ -57,8 +57,11 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
                  label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
-                 reduction: str = "mean", workspace: Optional[torch.Tensor] = None):
-    """Returns (loss, lse, n_valid): loss float32 [1] (sum/mean) or [N] (none)."""
+                 reduction: str = "mean", workspace: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
+                 return_z_loss: bool = False):
+    """Returns (loss, lse, n_valid): loss float32 [1] (sum/mean) or [N] (none); with
+    return_z_loss, (loss, lse, n_valid, z_loss), z_loss the s * lse^2 term alone,
+    shaped like loss.  The logits are logit_scale * (x W^T + b)."""
     x, W, b, targets = _prep(x, W, b, targets)
     N, H = x.shape
     V = W.shape[0]
@@ -70,13 +73,20 @@ def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], ta
     loss = torch.empty(N if reduction == "none" else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    z_loss = torch.empty_like(loss) if return_z_loss else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        _lib.flce_forward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
-                          float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
-                          loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), workspace.data_ptr(),
-                          workspace.numel(), stream)
-    return loss, lse, n_valid
+        if logit_scale == 1.0 and not return_z_loss:
+            _lib.flce_forward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                              float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                              loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), workspace.data_ptr(),
+                              workspace.numel(), stream)
+        else:
+            _lib.flce_forward_ex(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                                 float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                                 _lib.options(logit_scale, False, _ptr(z_loss)), loss.data_ptr(), lse.data_ptr(),
+                                 n_valid.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    return (loss, lse, n_valid, z_loss) if return_z_loss else (loss, lse, n_valid)
 
 
 def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
@@ -84,8 +94,9 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
                   label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
                   reduction: str = "mean", need_dx: bool = True, need_dW: bool = True,
                   need_db: bool = True, workspace: Optional[torch.Tensor] = None,
-                  out: Optional[Tuple] = None):
-    """Returns (dx, dW, db) in the input dtype (None where not requested)."""
+                  out: Optional[Tuple] = None, logit_scale: float = 1.0, accumulate: bool = False):
+    """Returns (dx, dW, db) in the input dtype (None where not requested).  With
+    accumulate, the gradients are added to the ``out`` tensors' contents."""
     x, W, b, targets = _prep(x, W, b, targets)
     N, H = x.shape
     V = W.shape[0]
@@ -100,15 +111,24 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
     if out is not None:
         dx, dW, db = out
     else:
+        if accumulate:
+            raise ValueError("accumulate needs the out tensors to add to")
         dx = torch.empty_like(x) if need_dx else None
         dW = torch.empty_like(W) if need_dW else None
         db = torch.empty_like(b) if (need_db and b is not None) else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        _lib.flce_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
-                           float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
-                           lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db),
-                           workspace.data_ptr(), workspace.numel(), stream)
+        if logit_scale == 1.0 and not accumulate:
+            _lib.flce_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                               float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                               lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db),
+                               workspace.data_ptr(), workspace.numel(), stream)
+        else:
+            _lib.flce_backward_ex(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                                  float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                                  _lib.options(logit_scale, accumulate, None), lse.data_ptr(), n_valid.data_ptr(),
+                                  g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db), workspace.data_ptr(),
+                                  workspace.numel(), stream)
     return dx, dW, db
 
 
@@ -208,38 +228,39 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
-                z_loss_scale=0.0, reduction="mean"):
+                z_loss_scale=0.0, reduction="mean", logit_scale=1.0):
         loss, lse, n_valid = flce_forward(x, weight, bias, target, label_smoothing, z_loss_scale,
-                                          ignore_index, reduction)
+                                          ignore_index, reduction, logit_scale=logit_scale)
         ctx.save_for_backward(x, target, weight, bias, lse, n_valid)
-        ctx.opts = (ignore_index, label_smoothing, z_loss_scale, reduction)
+        ctx.opts = (ignore_index, label_smoothing, z_loss_scale, reduction, logit_scale)
         return loss if reduction == "none" else loss.reshape(())
 
     @staticmethod
     def backward(ctx, grad):
         x, target, weight, bias, lse, n_valid = ctx.saved_tensors
-        ignore_index, eps, s, reduction = ctx.opts
+        ignore_index, eps, s, reduction, logit_scale = ctx.opts
         dx, dW, db = flce_backward(x, weight, bias, target, lse, n_valid, grad, eps, s, ignore_index,
                                    reduction, need_dx=ctx.needs_input_grad[0],
                                    need_dW=ctx.needs_input_grad[2],
-                                   need_db=bias is not None and ctx.needs_input_grad[3])
-        return dx, None, dW, db, None, None, None, None
+                                   need_db=bias is not None and ctx.needs_input_grad[3], logit_scale=logit_scale)
+        return dx, None, dW, db, None, None, None, None, None
 
 
 def fused_linear_cross_entropy_loss(x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
-                                    z_loss_scale=0.0, reduction="mean"):
+                                    z_loss_scale=0.0, reduction="mean", logit_scale=1.0):
     """Functional form: x [N, H], target [N], weight [V, H], bias [V] or None."""
     return FusedLinearCrossEntropyFunction.apply(x, target, weight, bias, ignore_index, label_smoothing,
-                                                 z_loss_scale, reduction)
+                                                 z_loss_scale, reduction, logit_scale)
 
 
 class FusedLinearCrossEntropyLoss(torch.nn.Module):
     """Module form; x may be [..., H] and target [...]; they are flattened."""
 
     def __init__(self, ignore_index: int = -100, label_smoothing: float = 0.0, z_loss_scale: float = 0.0,
-                 reduction: str = "mean"):
+                 reduction: str = "mean", logit_scale: float = 1.0):
         super().__init__()
         _reduction_code(reduction)
+        self.logit_scale = logit_scale
         self.ignore_index = ignore_index
         self.label_smoothing = label_smoothing
         self.z_loss_scale = z_loss_scale
@@ -248,4 +269,4 @@ class FusedLinearCrossEntropyLoss(torch.nn.Module):
     def forward(self, x, target, weight, bias=None):
         return fused_linear_cross_entropy_loss(x.reshape(-1, x.shape[-1]), target.reshape(-1), weight, bias,
                                                self.ignore_index, self.label_smoothing, self.z_loss_scale,
-                                               self.reduction)
+                                               self.reduction, self.logit_scale)

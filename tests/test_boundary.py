@@ -218,3 +218,24 @@ def test_shard_workspace_sizes(lib):
     assert m >= 8192 * 4                             # per-row losses of the merge
     assert b == bb - 8192 * 4096 * 4                 # no dx accumulator: the caller's fp32 buffer
     assert _sbwd(lib, dx=None, dW=None, db=None) == 0   # nothing requested: no launch, OK
+
+
+def test_ex_entry_points_validate_options(lib):
+    import math as _m
+    bad = _lib.options(logit_scale=float("inf"))
+    assert lib.flce_forward_ex(P, P, None, P, 64, 128, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(bad), P2, P2, P2,
+                               P2, 1 << 30, None) == 1
+    assert lib.flce_backward_ex(P, P, None, P, 64, 128, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(bad), P2, P2, P2,
+                                P2, P2, None, P2, 1 << 30, None) == 1
+    nan = _lib.options(logit_scale=_m.nan)
+    assert lib.flce_forward_ex(P, P, None, P, 64, 128, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(nan), P2, P2, P2,
+                               P2, 1 << 30, None) == 1
+    misaligned = _lib.options(z_loss=P2 + 2)
+    assert lib.flce_forward_ex(P, P, None, P, 64, 128, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(misaligned), P2,
+                               P2, P2, P2, 1 << 30, None) == 1
+    # the usual argument checks still come first for the rest
+    ok = _lib.options(logit_scale=0.5)
+    assert lib.flce_forward_ex(P, P, None, P, 0, 128, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(ok), P2, P2, P2,
+                               P2, 1 << 30, None) == 1
+    assert lib.flce_backward_ex(P, P, None, P, 64, 12, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(ok), P2, P2, P2,
+                                P2, P2, None, P2, 1 << 30, None) == 2
