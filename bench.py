@@ -207,7 +207,8 @@ def shard_bench(args, w, x, W, b, tg, g, name):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 draws, random-init weights)",
         "config": {"workload": name, "N": N, "H": H, "V": V, "shards": P, "shard_rows": cuts[1] - cuts[0]},
-        "tflops_8nhv": tflops, "mfma_frac_8nhv": tflops / PEAK_BF16_TFLOPS, "loss": loss.item(),
+        "tflops_8nhv": tflops, "mfma_frac_8nhv": tflops / PEAK_BF16_TFLOPS,
+        "loss": loss.sum().item() if loss.numel() > 1 else loss.item(),
         "workspace_mb": (ws_f.numel() + ws_m.numel() + ws_b.numel()) / 1e6,
     }), flush=True)
 
@@ -302,7 +303,8 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = 2.0 * N * H * V / (fwd_avg * 1e-3) / 1e12
     extra = fwd_bytes + bwd_bytes + N * 4 + 8
-    print(f"[bench] loss {loss.item():.6f}; fwd {fwd_med:.3f} ms, bwd {bwd_med:.3f} ms (median)",
+    loss_v = loss.sum().item() if loss.numel() > 1 else loss.item()   # reduction none: report the sum
+    print(f"[bench] loss {loss_v:.6f}; fwd {fwd_med:.3f} ms, bwd {bwd_med:.3f} ms (median)",
           file=sys.stderr, flush=True)
 
     out = {
