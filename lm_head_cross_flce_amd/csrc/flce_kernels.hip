@@ -2,24 +2,32 @@
 //
 // Forward (statistics only; logits recomputed in backward, the schedule of
 // DeepSpeed PR 8792):
-//   fwd_lse_kernel     logits tiles z = W x^T (+ b) on MFMA; the epilogue folds
-//                      each tile into per-token online max / sum-exp (the
-//                      online softmax the fla kernel cites), the running sum of
-//                      logits (label smoothing) and the target logit.
+//   fwd_lse_kernel     logits tiles z = scale (W x^T + b) on MFMA; the
+//                      epilogue folds each tile into per-token online max /
+//                      sum-exp (the online softmax the fla kernel cites), the
+//                      running sum of logits (label smoothing) and the target
+//                      logit.  Persistent over (token tile, vocabulary phase).
 //   fwd_combine_kernel merges the per-phase partials: lse = m + log d and the
-//                      per-row loss of the label-smoothed CE plus z-loss.
-//   fwd_finalize       fixed-order sum and non-ignored count (no host sync).
+//                      per-row loss of the label-smoothed CE plus z-loss (and
+//                      the z-loss term alone when asked for).
+//   fwd_stats_kernel   vocabulary shards: merges the phases into per-token
+//                      statistics instead (the shard merge then runs
+//                      fwd_combine over the shards).
+//   fwd_finalize       fixed-order sums and non-ignored count (no host sync).
 // Backward, one vocabulary slab at a time:
-//   bwd_coef_kernel    per-token c_n (upstream grad, 1/T for mean) folded with
-//                      the z-loss factor (1 + 2 s lse) of Liger PR 239.
-//   bwd_dz_kernel      recomputes a logits tile and turns it into dlogits
-//                      dz = c [(1 + 2 s lse) p - eps/V - (1 - eps) [j = y]],
-//                      written to the slab; optional db partial sums (fp32).
-//   bwd_dw_kernel      dW[slab] = dz^T x with K = all tokens, fp32 in
-//                      registers, written once in W's dtype.
+//   bwd_coef_kernel    per-token c_n (upstream grad, 1/T for mean, the logit
+//                      scale) folded with the z-loss factor (1 + 2 s lse) of
+//                      Liger PR 239.
+//   bwd_dz_kernel      recomputes logits tiles (persistent) and turns them
+//                      into dlogits dz = c [(1 + 2 s lse) p - eps/V
+//                      - (1 - eps) [j = y]], written to the slab; optional db
+//                      partial sums (fp32).
 //   bwd_dx_kernel      dx += dz W[slab] into an fp32 accumulator; the last
-//                      slab writes dx in x's dtype.
-//   bwd_db_kernel      fixed-order sum of the db partials.
+//                      slab writes dx in x's dtype (optionally added to it).
+//   bwd_dw_kernel      dW[slab] = dz^T x with K = all tokens, fp32 in
+//                      registers, written once in W's dtype (optionally added);
+//                      its first H-tile workgroups also finish db.
+//   bwd_db_kernel      db alone, when dW is not requested.
 #include "flce_device.hpp"
 #include "flce_launch.hpp"
 
