@@ -81,7 +81,10 @@ typedef enum {
  * (*bwd_bytes) need for this problem.  Pure host arithmetic: no HIP call.
  * Either output pointer may be NULL.  The backward figure includes one
  * vocabulary slab of dlogits [N, slab] in the input dtype and an fp32 [N, H]
- * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch.
+ * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch.  When the dx
+ * product has too few 256 x 256 output tiles to fill the GPU (at most half
+ * of its 256 CUs), each slab's columns are split into P <= 8 parts, each with
+ * its own fp32 [N, H] accumulator (P x N x H x 4 bytes, at most about 64 MB).
  */
 flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias,
                                 int reduction, size_t* fwd_bytes, size_t* bwd_bytes);

@@ -23,6 +23,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Geometry {
   int NT, VT, P;
   int64_t slab_cols;
+  int dx_split;
   size_t off_partials, off_rowloss, off_rowzl, fwd_total;
   size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, bwd_total;
 };
@@ -63,6 +64,21 @@ int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   return c < vmax ? c : vmax;
 }
 
+// Input-gradient K split.  The dx product has cdiv(N, 256) x cdiv(H, 256)
+// output tiles, one workgroup each; when that is at most half the CUs, each
+// slab's columns are split into parts that run side by side, each adding into
+// its own fp32 accumulator, and the parts are summed once after the last slab.
+// At most 8 parts of at least 512 columns.  The Llama-3-sized head (512
+// tiles) never splits; N=4096, H=2048 (128 tiles) splits in two.
+int dx_split(int64_t N, int64_t H, int64_t slab_cols) {
+  const int64_t tiles = cdiv(N, kTile) * cdiv(H, kTile);
+  if (2 * tiles > kCUs) return 1;
+  int64_t p = kCUs / tiles;
+  if (p > slab_cols / 512) p = slab_cols / 512;
+  if (p > 8) p = 8;
+  return p < 2 ? 1 : (int)p;
+}
+
 // with_dx_acc: the backward keeps its own fp32 dx accumulator (the shard
 // backward accumulates into the caller's buffer instead).
 Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true) {
@@ -84,11 +100,12 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   g.fwd_total = off;
 
   g.slab_cols = slab_cols(N, H, V, dtype);
+  g.dx_split = with_dx_acc ? dx_split(N, H, g.slab_cols) : 1;
   off = 0;
   g.off_slab = off;
   off = align_up(off + (size_t)N * g.slab_cols * es);
   g.off_dxacc = off;
-  if (with_dx_acc) off = align_up(off + (size_t)N * H * 4);
+  if (with_dx_acc) off = align_up(off + (size_t)g.dx_split * N * H * 4);
   g.off_dbp = off;
   if (has_bias) off = align_up(off + (size_t)g.NT * g.slab_cols * 4);
   g.off_coef = off;
@@ -138,6 +155,8 @@ flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int d
     int mode = flce::kDxAccum;
     if (dx_out_fp32) {
       if (k == 0 && !accumulate) mode = flce::kDxFirst;
+    } else if (a.dx_split > 1) {
+      mode = k == 0 ? flce::kDxFirst : flce::kDxAccum;   // the parts' sum is written below
     } else if (nslab == 1) {
       mode = flce::kDxOnly;
     } else if (k == 0) {
@@ -147,6 +166,8 @@ flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int d
     }
     if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
   }
+  if (a.dx && !dx_out_fp32 && a.dx_split > 1 && flce::launch_bwd_dx_finalize(a, dtype, s) != hipSuccess)
+    return FLCE_ERR_HIP;
   return FLCE_OK;
 }
 
@@ -284,6 +305,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   a.slab = ws + g.off_slab;
   a.ldS = g.slab_cols;
   a.dx_acc = (float*)(ws + g.off_dxacc);
+  a.dx_split = g.dx_split;
   a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
   a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
 

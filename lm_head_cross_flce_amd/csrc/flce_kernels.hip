@@ -648,22 +648,35 @@ __device__ __forceinline__ f32x4 load4_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // ACC (modes that write dx in its dtype): dx is added to what it holds; its
 // old values are loaded ahead with the accumulator's.
+//
+// K split (a.dx_split parts, when the output has too few tiles to fill the
+// CUs): workgroup b computes tile b % G over the slab columns
+// [p kc, (p + 1) kc) of part p = b / G into accumulator p, in the First or
+// Accum mode; a part past the slab's columns reads only zeros (its operands'
+// valid K is 0), so it still writes or keeps its accumulator.
 template <class T, int MODE, bool ACC>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM) {
+__global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
+                                                             int kc) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int G = TM * a.NT;
+  const int part = blockIdx.x / G;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, TM, a.NT, tm, tn);
+  tile_coords(blockIdx.x - part * G, G, TM, a.NT, tm, tn);
   const int h0 = tm * kTile, n0 = tn * kTile;
-  const Opnd<T> A{(const T*)a.W + (int64_t)vs * a.H, a.H, a.H, width};
-  const Opnd<T> B{(const T*)a.slab, a.ldS, a.N, wpad};
+  const int k0 = part * kc;
+  const bool live = k0 < wpad;
+  const int kw = live ? min(width - k0, kc) : 0;     // valid W rows of this part (may be <= 0)
+  const int kp = live ? min(wpad - k0, kc) : 0;      // slab columns of this part
+  const Opnd<T> A{(const T*)a.W + (int64_t)(vs + (live ? k0 : 0)) * a.H, a.H, a.H, kw > 0 ? kw : 0};
+  const Opnd<T> B{(const T*)a.slab + (live ? k0 : 0), a.ldS, a.N, kp};
   Acc acc;
-  gemm_tile<T, false, true>(acc, A, h0, B, n0, wpad, L, tid);
+  gemm_tile<T, false, true>(acc, A, h0, B, n0, kp > 0 ? kp : 1, L, tid);   // K >= 1: an empty part sums zeros
 
   constexpr bool kRead = MODE == kDxAccum || MODE == kDxLast;
   constexpr bool kAcc = MODE == kDxFirst || MODE == kDxAccum;   // write the fp32 accumulator
   // Descriptors start at token row n0, so offsets stay below 256 * H * 4 bytes.
-  const __amdgpu_buffer_rsrc_t racc = make_rsrc(a.dx_acc + (int64_t)n0 * a.H);
+  const __amdgpu_buffer_rsrc_t racc = make_rsrc(a.dx_acc + (int64_t)part * a.N * a.H + (int64_t)n0 * a.H);
   const __amdgpu_buffer_rsrc_t rdx = make_rsrc((const T*)a.dx + (int64_t)n0 * a.H);
   const int g = lane >> 4;
   // Byte offset of block b = 8 j + i (row n = n0 + nl, columns h .. h + 3)
@@ -702,6 +715,36 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   }
 }
 
+// dx from the K-split accumulators: thread i sums four consecutive elements
+// of every part in part order (plus dx's old values when accumulating).
+template <class T, bool ACC>
+__global__ void __launch_bounds__(256) bwd_dx_finalize_kernel(BwdLaunch a) {
+  const int64_t n4 = (int64_t)a.N * a.H / 4;
+  const int64_t stride = (int64_t)a.N * a.H;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 v = ((const f32x4*)a.dx_acc)[i];
+    for (int p = 1; p < a.dx_split; ++p) v += ((const f32x4*)(a.dx_acc + p * stride))[i];
+    T* d = (T*)a.dx + 4 * i;
+    if (ACC) v += load4<T>(d);
+    store4<T>(d, v[0], v[1], v[2], v[3]);
+  }
+}
+
+hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st) {
+  const int64_t n4 = (int64_t)a.N * a.H / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4 * kPersistGrid) blocks = 4 * kPersistGrid;
+  const dim3 grid((unsigned)blocks), blk(256);
+  if (dtype == 1) {
+    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, false>), grid, blk, 0, st, a);
+  } else {
+    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, false>), grid, blk, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 // db of one slab when no dW launch does it (frozen weight).
 template <class T>
 __global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a, int vs, int width) {
@@ -726,14 +769,17 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
   else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   if (a.dx) {
-    const dim3 gdx(TH * a.NT);
+    // K split: each part takes kc slab columns (a multiple of the 64-deep copy block).
+    const int parts = a.dx_split > 1 ? a.dx_split : 1;
+    const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
+    const dim3 gdx(TH * a.NT * parts);
     const bool acc = a.accumulate != 0;
-    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (dx_mode == kDxLast && !acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else if (!acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH);
-    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH);
+    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxLast && !acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (!acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
   }
   if (a.dW && a.accumulate) hipLaunchKernelGGL((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
   else if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);

@@ -42,7 +42,8 @@ struct BwdLaunch {
   void* coef;             // float4 [N]
   int* yv;                // [N]
   void* slab; int64_t ldS;
-  float* dx_acc;          // [N][H]
+  float* dx_acc;          // [dx_split][N][H]
+  int dx_split;           // input-gradient K split: parts of each slab's columns, one accumulator each
   float* dbp;             // [NT][ldS]: per token tile db partials of the current slab; null if no db
   void* dx; void* dW; void* db;
 };
@@ -56,5 +57,8 @@ hipError_t launch_merge(const FwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
                            hipStream_t st);
+// dx = the sum of the a.dx_split fp32 accumulators (plus dx's old values when
+// a.accumulate), written in dx's dtype.
+hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st);
 
 }  // namespace flce

@@ -73,6 +73,22 @@ def test_workspace_size_arithmetic(lib):
     assert b - b_nobias >= NT * slab * 4
 
 
+def test_workspace_holds_one_dx_accumulator_per_k_part(lib):
+    # N=4096, H=2048: the dx product has 16 x 8 = 128 output tiles, half the
+    # 256 CUs, so each slab's columns are split in two parts with an fp32
+    # [N, H] accumulator each; the Llama-3-sized head (512 tiles) keeps one.
+    N, H, V = 4096, 2048, 32000
+    slab = _lib.flce_backward_slab_cols(N, H, V, _lib.FLCE_BF16)
+    _, b = _lib.flce_workspace_size(N, H, V, _lib.FLCE_BF16, False, 2)
+    need = N * slab * 2 + 2 * N * H * 4 + N * 20
+    assert need <= b <= need + 8 * 256
+    # no split below 512 columns per part: a 1000-column vocabulary splits in two at most
+    _, b1 = _lib.flce_workspace_size(64, 128, 1000, _lib.FLCE_F32, False, 2)
+    slab1 = _lib.flce_backward_slab_cols(64, 128, 1000, _lib.FLCE_F32)
+    need1 = 64 * slab1 * 4 + 2 * 64 * 128 * 4 + 64 * 20
+    assert need1 <= b1 <= need1 + 8 * 256
+
+
 def test_slab_width_heuristic(lib):
     # the wider of: one slab's dW tiles cover 256 CUs twice, or the widest
     # slab within 256 MiB whose dW tiles fill whole rounds of 256 CUs; capped

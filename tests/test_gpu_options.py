@@ -77,9 +77,11 @@ def test_z_loss_term_alone(red):
     assert rel(loss.cpu().numpy().astype(np.float64), f.loss) <= LOSS_RTOL
 
 
-@pytest.mark.parametrize("name,slab", [("c3_small", None), ("c3_small", "512"), ("f32_none", None)])
+@pytest.mark.parametrize("name,slab", [("c3_small", None), ("c3_small", "512"), ("c3_small", "1024"),
+                                       ("f32_none", None)])
 def test_accumulate_into_existing_gradients(monkeypatch, name, slab):
-    # one slab (dx written directly) and several (dx through the fp32 accumulator)
+    # one slab and several (dx through the fp32 accumulators; with no override
+    # and with 1024 columns these shapes split each slab's columns in K parts)
     if slab:
         monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", slab)
     inp = inputs(name)

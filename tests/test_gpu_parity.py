@@ -44,6 +44,8 @@ CASES = {
                             reduction="sum", grad="scalar_normal", seed=9),
     "n1_v1": _case("tiny_f32", "n1_v1", N=1, H=8, V=1, n_ignored=0, z_loss_scale=0.01, seed=10),
     "bf16_v_lt_tile": _case("n8192_h4096_v128256", "bf16_v_lt_tile", N=33, H=72, V=100, n_ignored=3, seed=11),
+    # with 1024-column slabs the last slab has 6 columns: the second input-gradient K part is empty
+    "f32_v1030": _case("tiny_f32", "f32_v1030", N=64, H=128, V=1030, seed=12),
 }
 
 _oracle_cache = {}
@@ -102,11 +104,15 @@ def test_parity_all_reductions(red):
     check("c3_small", got, f, bw)
 
 
-@pytest.mark.parametrize("cols", ["256", "512"])
+@pytest.mark.parametrize("cols", ["256", "512", "1024"])
 def test_forced_small_slabs(monkeypatch, cols):
     # Many vocabulary slabs: the fp32 dx accumulator carries across launches.
+    # 1024 columns: these token counts give the input-gradient product too few
+    # tiles for the GPU, so each slab's columns are split in two K parts (each
+    # with its own accumulator, summed at the end); the last slabs of c3_small
+    # and f32_v1030 leave the second part without columns.
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", cols)
-    for name in ("c3_small", "c5_small", "f32_none"):
+    for name in ("c3_small", "c5_small", "f32_none") + (("f32_v1030",) if cols == "1024" else ()):
         print(f"[gpu] forced slabs {cols} {name}", flush=True)
         got = run(inputs(name))
         f, bw = oracle(name)
