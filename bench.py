@@ -4,6 +4,7 @@
     python bench.py --copy-probe BYTES          # one plain device copy of BYTES (counter calibration)
     python bench.py --summarize-trace DIR       # markdown table from a rocprofv3 --kernel-trace run
     python bench.py --summarize-pmc DIR         # markdown table from a rocprofv3 --pmc run
+    python bench.py --summarize-alloc DIR       # device allocations from a --memory-allocation-trace run
     python bench.py --shards P                  # the vocabulary-shard path: P shards in sequence
 
 A step is one pass of the whole hot path over one batch: flce_forward (logits
@@ -46,6 +47,7 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     p.add_argument("--summarize-trace", default=None, metavar="DIR")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR")
+    p.add_argument("--summarize-alloc", default=None, metavar="DIR")
     p.add_argument("--shards", type=int, default=0, metavar="P",
                    help="time the vocabulary-shard entry points: W split into P shards run one after another")
     return p.parse_args()
@@ -114,6 +116,26 @@ def summarize_trace(d):
     print("|---|---:|---:|---:|---:|")
     for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         print(f"| `{k}` | {n} | {t / n / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.1f}% |")
+
+
+def summarize_alloc(d):
+    """Device allocations of a rocprofv3 --memory-allocation-trace run, 1 MB and up."""
+    files = glob.glob(os.path.join(d, "**", "*memory_allocation_trace.csv"), recursive=True)
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            size = int(r.get("Allocation_Size", 0) or 0)
+            if size >= 1 << 20:
+                rows.append((int(r.get("Start_Timestamp", 0) or 0), r.get("Operation", "?"), size,
+                             r.get("Agent_Type", r.get("Agent_Id", ""))))
+    rows.sort()
+    total = 0
+    print("| # | operation | bytes | MB |")
+    print("|---:|---|---:|---:|")
+    for i, (_, op, size, _) in enumerate(rows):
+        total += size if "FREE" not in op.upper() else 0
+        print(f"| {i} | {op} | {size} | {size / 1e6:.1f} |")
+    print(f"\nallocated (1 MB and up, frees not subtracted): {total / 1e6:.1f} MB")
 
 
 def summarize_pmc(d):
@@ -221,6 +243,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
         return
+    if args.summarize_alloc:
+        summarize_alloc(args.summarize_alloc)
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -259,6 +284,8 @@ def main():
     tg = torch.from_numpy(inp.targets).to(dev)
     g = torch.from_numpy(inp.grad).to(dev)
     N, H, V = w.N, w.H, w.V
+    torch.cuda.synchronize()
+    mem_inputs = torch.cuda.memory_allocated(dev)   # x, W, b, targets, upstream grad
     fwd_bytes, bwd_bytes = F.flce_workspace_size(N, H, V, tdt, b is not None, w.reduction)
     ws_f = torch.empty(fwd_bytes, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bwd_bytes, dtype=torch.uint8, device=dev)
@@ -283,6 +310,7 @@ def main():
             ev[2].record(stream)
         return loss
 
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -292,6 +320,11 @@ def main():
         loss = step(events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Measured extra memory: the allocator's peak over the warmup and timed steps, less
+    # the inputs and the gradient outputs (dx, dW, db): the workspaces plus the
+    # per-call loss, lse and count.
+    out_bytes = sum(t_.numel() * t_.element_size() for t_ in (dx, dW, db) if t_ is not None)
+    extra_measured = torch.cuda.max_memory_allocated(dev) - mem_inputs - out_bytes
     fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
     bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
     fwd_med, bwd_med = fwd_ms[len(fwd_ms) // 2], bwd_ms[len(bwd_ms) // 2]
@@ -329,6 +362,7 @@ def main():
         "mfma_frac_8nhv": tflops / peak,
         "extra_hbm_mb": extra / 1e6,
         "extra_hbm_frac_of_fp32_logits": extra / (N * V * 4.0),
+        "extra_hbm_measured_mb": extra_measured / 1e6,
         "roofline": {"kernel": "fwd_lse_kernel", "bound": "mfma", "achieved": fwd_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": fwd_tflops / peak,
                      "traffic": recorded_traffic("fwd_lse_kernel", name),
