@@ -32,7 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FLCE fwd+bwd tokens/s and % bf16 MFMA peak at N=8192,H=4096,V=128256"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (fp16 the same)
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
 
 
@@ -272,7 +272,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.dtype, torch.float32)
 
     def t(a):
         if w.dtype == "bf16":
@@ -332,7 +332,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed
     flops = 8.0 * N * H * V
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = 2.0 * N * H * V / (fwd_avg * 1e-3) / 1e12
     extra = fwd_bytes + bwd_bytes + N * 4 + 8

@@ -73,7 +73,12 @@ typedef enum {
 
 typedef enum {
   FLCE_F32 = 0,  /* x, W, b are float32; gradients are float32 */
-  FLCE_BF16 = 1  /* x, W, b are bfloat16; gradients are bfloat16 (fp32 accumulation) */
+  FLCE_BF16 = 1, /* x, W, b are bfloat16; gradients are bfloat16 (fp32 accumulation) */
+  FLCE_F16 = 2   /* x, W, b are IEEE half; gradients are half (fp32 accumulation).  The dlogits
+                    slab holds dz times a power of two S = 2^(14 - e), where 2^e bounds
+                    max_n |c_n| (|1 + 2 s lse_n| + eps/V + 1 - eps) over non-ignored rows, so
+                    that values near c_n / V stay in half's normal range; S cancels exactly
+                    in dx, dW and db.  Logits and their statistics are fp32 as for bf16. */
 } flce_dtype;
 
 /*

@@ -20,6 +20,7 @@ FLCE_ERR_HIP = 4
 
 FLCE_F32 = 0
 FLCE_BF16 = 1
+FLCE_F16 = 2
 
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 

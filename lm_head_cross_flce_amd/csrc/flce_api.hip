@@ -25,12 +25,12 @@ struct Geometry {
   int64_t slab_cols;
   int dx_split;
   size_t off_partials, off_rowloss, off_rowzl, fwd_total;
-  size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, bwd_total;
+  size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, off_gscale, bwd_total;
 };
 
 flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
   if (N < 1 || H < 1 || V < 1) return FLCE_ERR_INVALID_ARGUMENT;
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_UNSUPPORTED;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16 && dtype != FLCE_F16) return FLCE_ERR_UNSUPPORTED;
   if (N > (int64_t(1) << 30) || V > (int64_t(1) << 30) || H > (int64_t(1) << 20)) return FLCE_ERR_UNSUPPORTED;
   if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   return FLCE_OK;
@@ -47,7 +47,7 @@ flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
 // FLCE_DEBUG_SLAB_COLS (a positive multiple of 256) overrides it; the tests
 // use it to force many slabs.
 int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
-  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
+  const int64_t es = dtype == FLCE_F32 ? 4 : 2;
   const int64_t vmax = cdiv(V, kTile) * kTile;
   if (const char* env = std::getenv("FLCE_DEBUG_SLAB_COLS")) {
     const long long c = std::atoll(env);
@@ -83,7 +83,7 @@ int dx_split(int64_t N, int64_t H, int64_t slab_cols) {
 // backward accumulates into the caller's buffer instead).
 Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true) {
   Geometry g{};
-  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
+  const int64_t es = dtype == FLCE_F32 ? 4 : 2;
   g.NT = (int)cdiv(N, kTile);
   g.VT = (int)cdiv(V, kTile);
   int P = kCUs / g.NT;
@@ -112,6 +112,8 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   off = align_up(off + (size_t)N * 16);
   g.off_yv = off;
   off = align_up(off + (size_t)N * 4);
+  g.off_gscale = off;   // fp16: the dlogits slab's scale {S, 1/S}
+  if (dtype == FLCE_F16) off = align_up(off + 8);
   g.bwd_total = off;
   return g;
 }
@@ -135,7 +137,7 @@ flce_status check_shard(int64_t V_shard, int64_t vocab_start, int64_t V_total) {
 flce_status check_inputs(const void* x, const void* W, const void* b, const int64_t* targets, int dtype) {
   if (!x || !W || !targets) return FLCE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(targets, 8)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (b && !aligned(b, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (b && !aligned(b, dtype == FLCE_F32 ? 4 : 2)) return FLCE_ERR_INVALID_ARGUMENT;
   return FLCE_OK;
 }
 
@@ -280,7 +282,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   if (!lse || !n_valid || !grad_loss) return FLCE_ERR_INVALID_ARGUMENT;
   if (!aligned(lse, 4) || !aligned(n_valid, 8) || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   if ((dx && !aligned(dx, 16)) || (dW && !aligned(dW, 16))) return FLCE_ERR_INVALID_ARGUMENT;
-  if (db && !aligned(db, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (db && !aligned(db, dtype == FLCE_F32 ? 4 : 2)) return FLCE_ERR_INVALID_ARGUMENT;
   const Geometry g = geometry(N, H, V, dtype, b != nullptr);
   if (workspace_bytes < g.bwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
@@ -307,6 +309,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   a.dx_acc = (float*)(ws + g.off_dxacc);
   a.dx_split = g.dx_split;
   a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
+  a.gscale = dtype == FLCE_F16 ? (float*)(ws + g.off_gscale) : nullptr;
   a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
 
   return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream);
@@ -399,7 +402,7 @@ flce_status flce_shard_backward(const void* x, const void* W_shard, const void* 
   if (!lse || !n_valid || !grad_loss) return FLCE_ERR_INVALID_ARGUMENT;
   if (!aligned(lse, 4) || !aligned(n_valid, 8) || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   if ((dx_partial && !aligned(dx_partial, 16)) || (dW_shard && !aligned(dW_shard, 16))) return FLCE_ERR_INVALID_ARGUMENT;
-  if (db_shard && !aligned(db_shard, dtype == FLCE_BF16 ? 2 : 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (db_shard && !aligned(db_shard, dtype == FLCE_F32 ? 4 : 2)) return FLCE_ERR_INVALID_ARGUMENT;
   const Geometry g = geometry(N, H, V_shard, dtype, b_shard != nullptr, false);
   if (workspace_bytes < g.bwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
@@ -425,6 +428,7 @@ flce_status flce_shard_backward(const void* x, const void* W_shard, const void* 
   a.ldS = g.slab_cols;
   a.dx_acc = dx_partial;
   a.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
+  a.gscale = dtype == FLCE_F16 ? (float*)(ws + g.off_gscale) : nullptr;
   a.dx = dx_partial; a.dW = dW_shard; a.db = want_db ? db_shard : nullptr;
   return run_backward(a, g, V_shard, dtype, want_db, true, accumulate_dx != 0, (hipStream_t)stream);
 }

@@ -42,10 +42,35 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
+// 16-bit element types: uint16_t holds bfloat16 bits, _Float16 is IEEE half.
+// Both travel through the same copies and LDS layouts; they differ in the
+// MFMA instruction and in the conversions to and from fp32.
+template <class T> struct IsF16 { static constexpr bool value = false; };
+template <> struct IsF16<_Float16> { static constexpr bool value = true; };
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+// fp32 of one 16-bit element's bits (bf16 or fp16).
+template <class T> __device__ __forceinline__ float h16_to_f32(uint32_t v) {
+  if constexpr (IsF16<T>::value) return f16_bits_to_f32(v);
+  else return bf16_bits_to_f32(v & 0xffffu);
+}
+
 // Round-to-nearest-even pack of two floats into bf16x2 (hardware convert).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Round-to-nearest-even pack of two floats into IEEE half x 2.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo), b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  return a | (b << 16);
+}
+template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (IsF16<T>::value) return pack_f16x2(lo, hi);
+  else return pack_bf16x2(lo, hi);
 }
 
 // Store four consecutive output values (one lane's run of four rows) as T.
@@ -55,6 +80,9 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
 }
 template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
   *(u32x2*)p = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+template <> __device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+  *(u32x2*)p = u32x2{pack_f16x2(a, b), pack_f16x2(c, d)};
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -126,7 +154,7 @@ template <class T> struct BiasTile {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(b + r0), (short)0, nrec, 0x00020000);
     if constexpr (sizeof(T) == 2) {
-      v = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)tid * 2u, 0, 0));
+      v = h16_to_f32<T>(__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)tid * 2u, 0, 0));
     } else {
       v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)tid * 4u, 0, 0));
     }
@@ -154,16 +182,21 @@ template <class T> struct Opnd {
 // (i, j) in lane l is row 16 i + 4 (l / 16) + r, column 16 j + l % 16.
 typedef f32x4 Acc[8][8];
 
-// One v_mfma_f32_16x16x32_bf16 into an accumulator kept in AGPRs.  The
+// One v_mfma_f32_16x16x32_bf16 (F16: _f16) into an accumulator kept in AGPRs.  The
 // accumulator is tied to the destination in inline asm: the compiler's own
 // register choice for this instruction moves accumulators between registers
 // on every step.  ZERO starts the accumulator at zero.  The compiler does not
 // see the instruction's latency: acc_drain() must precede any read of the
 // accumulators (acc_read4).
-template <bool ZERO>
+template <bool ZERO, bool F16 = false>
 __device__ __forceinline__ void mfma16(f32x4& c, const u32x4& a, const u32x4& b) {
-  if (ZERO) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
-  else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  if constexpr (F16) {
+    if (ZERO) asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  } else {
+    if (ZERO) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
 }
 template <bool ZERO>
 __device__ __forceinline__ void mfma16_f32(f32x4& c, float a, float b) {
@@ -391,10 +424,11 @@ template <> struct Dma<true> {
   uint32_t off[8];
   const uint16_t* base;
   int wave;
-  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid, bool perm = false) {
+  template <class E>
+  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, bool perm = false) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    base = o.p + (int64_t)m0 * o.ld;
+    base = (const uint16_t*)o.p + (int64_t)m0 * o.ld;
     const int c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -417,10 +451,11 @@ template <> struct Dma<false> {
   const uint16_t* base;
   int64_t ld;
   int wave;
-  __device__ __forceinline__ void init(const Opnd<uint16_t>& o, int m0, int tid, bool = false) {
+  template <class E>
+  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, bool = false) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    base = o.p + m0;
+    base = (const uint16_t*)o.p + m0;
     ld = o.ld;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -547,11 +582,12 @@ template <int RA, int RB, int PAR> struct StagePlan {
 // (no previous MFMAs; blocks 0..3 start from zero); SECOND: blocks 4..7
 // start from zero.  Every instruction slot ends in a scheduling barrier,
 // which pins this order.
-template <int PAR, int BUF, bool FIRST, bool SECOND, bool AK, bool BK, int VMW, bool TAIL>
+template <int PAR, int BUF, bool FIRST, bool SECOND, bool AK, bool BK, int VMW, bool TAIL, class E>
 __device__ __forceinline__ void stage_bf16(Acc& acc, Frag& P, Frag& C, const FragAddr<AK>& fa,
-                                           const FragAddr<BK>& fb, const Lds& L, int lane, const Opnd<uint16_t>& A,
-                                           const Opnd<uint16_t>& B, const Dma<AK>& da, const Dma<BK>& db,
+                                           const FragAddr<BK>& fb, const Lds& L, int lane, const Opnd<E>& A,
+                                           const Opnd<E>& B, const Dma<AK>& da, const Dma<BK>& db,
                                            int k_copy) {
+  constexpr bool F16 = IsF16<E>::value;
   typedef StagePlan<FragAddr<AK>::kReads, FragAddr<BK>::kReads, PAR> Plan;
   const lds_t* bA = L.a[BUF];
   const lds_t* bB = L.b[BUF];
@@ -564,14 +600,14 @@ __device__ __forceinline__ void stage_bf16(Acc& acc, Frag& P, Frag& C, const Fra
   };
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    if (!FIRST) mfma16<SECOND>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
+    if (!FIRST) mfma16<SECOND, F16>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
     if (Plan::kind1(k) == 1) frag_read<AK, BK, PAR>(C, fa, fb, bA, bB, Plan::idx1(k));
     else if (Plan::kind1(k) == 2) copy(Plan::idx1(k));
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    mfma16<FIRST>(acc[k / 8][k % 8], C.a[k / 8], C.b[k % 8]);
+    mfma16<FIRST, F16>(acc[k / 8][k % 8], C.a[k / 8], C.b[k % 8]);
     if (Plan::kind2(k) == 1) frag_read<AK, BK, PAR>(C, fa, fb, bA, bB, Plan::idx2(k));
     else if (Plan::kind2(k) == 2) copy(Plan::idx2(k));
     __builtin_amdgcn_sched_barrier(0);
@@ -584,11 +620,11 @@ __device__ __forceinline__ void stage_bf16(Acc& acc, Frag& P, Frag& C, const Fra
 }
 
 // The upper half (blocks 4..7) of a tile's last stage.
-template <bool ZERO>
+template <bool ZERO, bool F16 = false>
 __device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    mfma16<ZERO>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
+    mfma16<ZERO, F16>(acc[4 + k / 8][k % 8], P.a[4 + k / 8], P.b[k % 8]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -602,7 +638,8 @@ __device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
 template <bool AK, bool BK> struct TileCopy {
   Dma<AK> da;
   Dma<BK> db;
-  __device__ __forceinline__ void start(const Opnd<uint16_t>& A, int m0, const Opnd<uint16_t>& B, int n0,
+  template <class E>
+  __device__ __forceinline__ void start(const Opnd<E>& A, int m0, const Opnd<E>& B, int n0,
                                         const Lds& L, int tid, bool perm_a = false) {
     da.init(A, m0, tid, perm_a);
     db.init(B, n0, tid);
@@ -625,8 +662,8 @@ template <bool AK, bool BK> struct TileCopy {
 // stall; every counted instruction must be issued unconditionally by every
 // wave.  Returns with all copies complete; the accumulators need acc_drain()
 // before they are read.
-template <bool AK, bool BK, int EXTRA = 0>
-__device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t>& A, const Opnd<uint16_t>& B, int K,
+template <bool AK, bool BK, int EXTRA = 0, class E>
+__device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<E>& A, const Opnd<E>& B, int K,
                                                    const Lds& L, int tid, const TileCopy<AK, BK>& tc) {
   static_assert(EXTRA >= 0 && EXTRA <= 63, "vmcnt holds at most 63");
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -672,11 +709,11 @@ __device__ __forceinline__ void gemm_tile_bf16_run(Acc& acc, const Opnd<uint16_t
     stage_bf16<0, 1, false, false, AK, BK, 0, true>(acc, Y, X, fa, fb, L, lane, A, B, da, db, (kt / 2 + 2) * kBlockK);
     stage_bf16<1, 1, false, false, AK, BK, 0, true>(acc, X, Y, fa, fb, L, lane, A, B, da, db, 0);
   }
-  stage_last_half<false>(acc, Y);   // upper half of stage KTp - 1 (odd)
+  stage_last_half<false, IsF16<E>::value>(acc, Y);   // upper half of stage KTp - 1 (odd)
 }
 
-template <bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_bf16(Acc& acc, const Opnd<uint16_t>& A, int m0, const Opnd<uint16_t>& B,
+template <bool AK, bool BK, class E>
+__device__ __forceinline__ void gemm_tile_bf16(Acc& acc, const Opnd<E>& A, int m0, const Opnd<E>& B,
                                                int n0, int K, const Lds& L, int tid) {
   TileCopy<AK, BK> tc;
   tc.start(A, m0, B, n0, L, tid);

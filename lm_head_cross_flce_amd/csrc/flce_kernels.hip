@@ -297,7 +297,9 @@ static hipError_t launch_forward_t(const FwdLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
-  return dtype == 1 ? launch_forward_t<uint16_t>(a, st) : launch_forward_t<float>(a, st);
+  if (dtype == 1) return launch_forward_t<uint16_t>(a, st);
+  if (dtype == 2) return launch_forward_t<_Float16>(a, st);
+  return launch_forward_t<float>(a, st);
 }
 
 template <class T>
@@ -313,7 +315,9 @@ static hipError_t launch_shard_forward_t(const FwdLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
-  return dtype == 1 ? launch_shard_forward_t<uint16_t>(a, st) : launch_shard_forward_t<float>(a, st);
+  if (dtype == 1) return launch_shard_forward_t<uint16_t>(a, st);
+  if (dtype == 2) return launch_shard_forward_t<_Float16>(a, st);
+  return launch_shard_forward_t<float>(a, st);
 }
 
 hipError_t launch_merge(const FwdLaunch& a, hipStream_t st) {
@@ -326,19 +330,64 @@ hipError_t launch_merge(const FwdLaunch& a, hipStream_t st) {
 // Backward
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= a.N) return;
-  const int64_t t = a.targets[n];
-  const bool valid = t != a.ignore_index;
+// Per-token dlogits coefficient c_n: the upstream gradient (per token for
+// reduction none), divided by the non-ignored count for mean, times the
+// logits' scale (the gradient of the raw logits); 0 for ignored rows.
+__device__ __forceinline__ float token_coef(const BwdLaunch& a, int n, bool valid) {
   const float g = a.reduction == kNone ? a.grad[n] : a.grad[0];
   const long long T = a.n_valid[0];
   float c = g;
   if (a.reduction == kMean) c = T > 0 ? g / (float)T : 0.f;
   if (!valid) c = 0.f;
+  return c * a.logit_scale;
+}
+
+// fp16 inputs: the dlogits slab holds dz * S, with S a power of two chosen
+// so that the largest possible |dz * S| is at most 2^14.  |dz_nj| <= |c_n|
+// (|1 + 2 s lse_n| + eps / V + 1 - eps), and |c_n| is about g / T for the
+// mean: at the Llama-3-sized head an unscaled dz of c_n p ~ 1e-9 would
+// underflow fp16 (smallest subnormal 6e-8).  The slab's products are scaled
+// back by 1/S (exact) in the dx, dW and db epilogues.  One block; writes
+// gscale = {S, 1/S}.
+__global__ void __launch_bounds__(1024) bwd_scale_kernel(BwdLaunch a) {
+  __shared__ float smax[1024];
+  const int tid = threadIdx.x;
+  float mx = 0.f;
+  for (int n = tid; n < a.N; n += 1024) {
+    const bool valid = a.targets[n] != a.ignore_index;
+    const float c = fabsf(token_coef(a, n, valid));
+    const float bound = c * (fabsf(1.f + 2.f * a.s * a.lse[n]) + a.eps_over_v + (1.f - a.eps));
+    if (valid && bound > mx) mx = bound;   // NaN bounds are skipped
+  }
+  smax[tid] = mx;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) smax[tid] = fmaxf(smax[tid], smax[tid + w]);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    float S = 1.f;
+    const float m = smax[0];
+    if (m > 0.f && m <= 3.0e38f) {
+      int e;
+      (void)frexpf(m, &e);                 // m <= 2^e
+      int k = 14 - e;
+      k = k > 126 ? 126 : (k < -126 ? -126 : k);
+      S = ldexpf(1.f, k);
+    }
+    a.gscale[0] = S;
+    a.gscale[1] = 1.f / S;
+  }
+}
+
+__global__ void __launch_bounds__(256) bwd_coef_kernel(BwdLaunch a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const int64_t t = a.targets[n];
+  const bool valid = t != a.ignore_index;
+  float c = token_coef(a, n, valid);
+  if (a.gscale) c *= a.gscale[0];   // fp16: the slab holds dz * S
   const float lse = a.lse[n];
-  // Gradients of the raw logits: the logits' scale multiplies every term.
-  c *= a.logit_scale;
   ((f32x4*)a.coef)[n] = f32x4{c * (1.f + 2.f * a.s * lse), c * a.eps_over_v, c * (1.f - a.eps), lse * kLog2e};
   const int64_t lt = t - a.vocab_start;   // row of W holding the target, if any
   a.yv[n] = (valid && lt >= 0 && lt < a.V) ? (int)lt : -1;
@@ -485,8 +534,8 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
         const uint32_t off =
             n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.ldS + (v0 - vs) + r0) * 2) : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3]), pack_bf16x2(dz[4], dz[5]),
-                  pack_bf16x2(dz[6], dz[7])},
+            u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]),
+                  pack2<T>(dz[6], dz[7])},
             rslab, off, 0, 0);
       } else {
         if (n0 + nl < a.N) {
@@ -565,13 +614,14 @@ __device__ __forceinline__ void slab_db(const BwdLaunch& a, int vs, int width, i
   if (c >= width) return;
   float s = 0.f;
   for (int t = 0; t < a.NT; ++t) s += a.dbp[(int64_t)t * a.ldS + c];
+  if constexpr (IsF16<T>::value) s *= a.gscale[1];   // partials of dz * S
   if constexpr (sizeof(T) == 4) {
     float* p = (float*)a.db + vs + c;
     *p = a.accumulate ? *p + s : s;
   } else {
     uint16_t* p = (uint16_t*)a.db + vs + c;
-    if (a.accumulate) s += bf16_bits_to_f32(*p);
-    *p = (uint16_t)(pack_bf16x2(s, 0.f) & 0xffffu);
+    if (a.accumulate) s += h16_to_f32<T>(*p);
+    *p = (uint16_t)(pack2<T>(s, 0.f) & 0xffffu);
   }
 }
 
@@ -582,6 +632,10 @@ template <> __device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) 
   const u32x2 v = *(const u32x2*)p;
   return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
                __uint_as_float(v[1] & 0xffff0000u)};
+}
+template <> __device__ __forceinline__ f32x4 load4<_Float16>(const _Float16* p) {
+  const u32x2 v = *(const u32x2*)p;
+  return f32x4{f16_bits_to_f32(v[0]), f16_bits_to_f32(v[0] >> 16), f16_bits_to_f32(v[1]), f16_bits_to_f32(v[1] >> 16)};
 }
 
 // dW[vs + v, h] for the slab: C[h][v] = sum_n x[n][h] dz[n][v].  ACC: added
@@ -600,6 +654,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
   const Opnd<T> B{(const T*)a.slab, a.ldS, wpad, a.N};
   Acc acc;
   gemm_tile<T, false, false>(acc, A, h0, B, v0, a.N, L, tid);
+  const float inv = IsF16<T>::value ? a.gscale[1] : 1.f;   // fp16: the slab holds dz * S
   acc_drain();
   T* dW = (T*)a.dW;
   const int g = lane >> 4;
@@ -610,6 +665,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dw_kernel(BwdLaunch a, int vs
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       f32x4 z = acc_read4(acc[i][j]);
+      if constexpr (IsF16<T>::value) z *= inv;
       const int h = h0 + wm * kWaveTile + 16 * i + 4 * g;
       if (v < width && h < a.H) {
         if (ACC) z += load4<T>(rowp + h);
@@ -631,7 +687,7 @@ __device__ __forceinline__ void store4_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
   if constexpr (sizeof(T) == 4) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3])}, r, off, 0, 0);
   }
 }
 
@@ -641,8 +697,7 @@ __device__ __forceinline__ f32x4 load4_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_bit_cast(f32x4, buf_load16(r, off));
   } else {
     const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
-                 __uint_as_float(v[1] & 0xffff0000u)};
+    return f32x4{h16_to_f32<T>(v[0]), h16_to_f32<T>(v[0] >> 16), h16_to_f32<T>(v[1]), h16_to_f32<T>(v[1] >> 16)};
   }
 }
 
@@ -687,6 +742,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
     const int h = h0 + wm * kWaveTile + 16 * i + 4 * g;
     return (n0 + nl < a.N && h < a.H) ? (uint32_t)(nl * a.H + h) * es : kOOB;
   };
+  const float inv = IsF16<T>::value ? a.gscale[1] : 1.f;   // fp16: the slab holds dz * S
   acc_drain();
   // Loads run kAhead blocks ahead (12 x 1 KB in flight per wave), about what
   // one CU's share of HBM bandwidth needs while every CU makes its
@@ -705,6 +761,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
     if (kRead && bn < 64) old[bn % (kAhead + 1)] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn, 4u)));
     if (kOld && bn < 64) oldx[bn % (kAhead + 1)] = load4_buf<T>(rdx, boff(bn, (uint32_t)sizeof(T)));
     f32x4 v = acc_read4(acc[b & 7][b >> 3]);
+    if constexpr (IsF16<T>::value) v *= inv;
     if (kRead) v += old[b % (kAhead + 1)];
     if (kOld) v += oldx[b % (kAhead + 1)];
     if (kAcc) {
@@ -738,6 +795,9 @@ hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st)
   if (dtype == 1) {
     if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, true>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, false>), grid, blk, 0, st, a);
+  } else if (dtype == 2) {
+    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<_Float16, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<_Float16, false>), grid, blk, 0, st, a);
   } else {
     if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, true>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, false>), grid, blk, 0, st, a);
@@ -752,6 +812,7 @@ __global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a, int vs, int wi
 }
 
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
+  if (a.gscale) hipLaunchKernelGGL(bwd_scale_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(bwd_coef_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -789,8 +850,9 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
 
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
                            hipStream_t st) {
-  return dtype == 1 ? launch_bwd_slab_t<uint16_t>(a, vs, width, dx_mode, want_db, st)
-                    : launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, st);
+  if (dtype == 1) return launch_bwd_slab_t<uint16_t>(a, vs, width, dx_mode, want_db, st);
+  if (dtype == 2) return launch_bwd_slab_t<_Float16>(a, vs, width, dx_mode, want_db, st);
+  return launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, st);
 }
 
 

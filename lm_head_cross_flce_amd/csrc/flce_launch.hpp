@@ -45,10 +45,11 @@ struct BwdLaunch {
   float* dx_acc;          // [dx_split][N][H]
   int dx_split;           // input-gradient K split: parts of each slab's columns, one accumulator each
   float* dbp;             // [NT][ldS]: per token tile db partials of the current slab; null if no db
+  float* gscale;          // fp16 inputs: {S, 1/S}, the dlogits slab's power-of-two scale; null otherwise
   void* dx; void* dW; void* db;
 };
 
-// dtype: 0 = fp32, 1 = bf16.  Each returns the launch error code.
+// dtype: 0 = fp32, 1 = bf16, 2 = fp16.  Each returns the launch error code.
 hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st);
 // Shard forward: logits statistics of W's rows only, merged over phases into a.stats.
 hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st);

@@ -17,12 +17,12 @@ import torch
 
 from . import _lib
 
-_DTYPES = {torch.bfloat16: _lib.FLCE_BF16, torch.float32: _lib.FLCE_F32}
+_DTYPES = {torch.bfloat16: _lib.FLCE_BF16, torch.float16: _lib.FLCE_F16, torch.float32: _lib.FLCE_F32}
 
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16, float16 or float32")
     return _DTYPES[t.dtype]
 
 

@@ -123,11 +123,12 @@ def _workers() -> int:
 def normal(seed: int, tag: str, count: int, std: float, dtype: str) -> np.ndarray:
     """``count`` draws from N(0, std**2) rounded to ``dtype``.
 
-    dtype "bf16" returns uint16 bit patterns; "f32" returns float32.
+    dtype "bf16" returns uint16 bit patterns; "f16" returns float16 (numpy's
+    fp64 -> half conversion rounds to nearest-even); "f32" returns float32.
     """
     key = stream_key(seed, tag)
     npairs = (count + 1) // 2
-    out = np.empty(count, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty(count, dtype={"bf16": np.uint16, "f16": np.float16}.get(dtype, np.float32))
     chunk_pairs = _CHUNK // 2
 
     def work(p0: int) -> None:
@@ -137,6 +138,8 @@ def normal(seed: int, tag: str, count: int, std: float, dtype: str) -> np.ndarra
         vals = vals[: hi - lo]
         if dtype == "bf16":
             out[lo:hi] = f64_to_bf16_bits(vals)
+        elif dtype == "f16":
+            out[lo:hi] = vals.astype(np.float16)
         else:
             out[lo:hi] = vals.astype(np.float32)
 
@@ -205,7 +208,7 @@ class Workload:
     N: int
     H: int
     V: int
-    dtype: str                    # "bf16" or "f32": dtype of x, W and b
+    dtype: str                    # "bf16", "f16" or "f32": dtype of x, W and b
     x_std: float = 1.0
     w_std: Optional[float] = None  # None -> 1/sqrt(H)
     b_std: Optional[float] = None  # None -> no bias
@@ -222,7 +225,7 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads.  Seeds are 42 + index.
+# The five workloads (seeds 42 + index) and an fp16 variant of the Llama-3-sized head.
 WORKLOADS = {
     "tiny_f32": Workload(
         "tiny_f32", N=64, H=128, V=1000, dtype="f32", b_std=math.sqrt(0.1),
@@ -246,6 +249,12 @@ WORKLOADS = {
         targets="zipf", label_smoothing=0.05, z_loss_scale=1e-4,
         reduction="none", grad="vector_normal", seed=46,
         notes="small H / large V: Zipf(1.1) targets, eps 0.05, s 1e-4, none"),
+    # The Llama-3-sized head with fp16 inputs: the same draws (seed 44) rounded to half.
+    "n8192_h4096_v128256_f16": Workload(
+        "n8192_h4096_v128256_f16", N=8192, H=4096, V=128256, dtype="f16",
+        b_std=math.sqrt(0.02), n_ignored=410, label_smoothing=0.1,
+        z_loss_scale=1e-4, reduction="mean", grad="one", seed=44,
+        notes="Llama-3-sized head in fp16: bias N(0, 0.02), 5% ignored, eps 0.1, s 1e-4"),
 }
 
 BENCH_WORKLOAD = "n8192_h4096_v128256"

@@ -11,7 +11,7 @@ from lm_head_cross_flce_amd import synth
 # Tolerances of the parity bar: loss relative error, gradient relative
 # Frobenius error by input dtype.
 LOSS_RTOL = 1e-3
-GRAD_RTOL = {"bf16": 1e-2, "f32": 1e-5}
+GRAD_RTOL = {"bf16": 1e-2, "f16": 1e-2, "f32": 1e-5}
 LSE_RTOL = 1e-5
 
 

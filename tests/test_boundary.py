@@ -73,6 +73,19 @@ def test_workspace_size_arithmetic(lib):
     assert b - b_nobias >= NT * slab * 4
 
 
+def test_fp16_workspace_adds_the_slab_scale(lib):
+    # fp16 inputs use the bf16 layout plus one 256-byte slot for the slab's scale {S, 1/S}
+    for args in ((8192, 4096, 128256, True), (4096, 2048, 32000, False), (64, 128, 1000, True)):
+        N, H, V, bias = args
+        fh, bh = _lib.flce_workspace_size(N, H, V, _lib.FLCE_F16, bias, 2)
+        fb, bb = _lib.flce_workspace_size(N, H, V, _lib.FLCE_BF16, bias, 2)
+        assert fh == fb and bh == bb + 256
+        assert _lib.flce_backward_slab_cols(N, H, V, _lib.FLCE_F16) == _lib.flce_backward_slab_cols(N, H, V, 1)
+    fs, ms, bs = _lib.flce_shard_workspace_size(8192, 4096, 16032, _lib.FLCE_F16, True)
+    _, _, bs16 = _lib.flce_shard_workspace_size(8192, 4096, 16032, _lib.FLCE_BF16, True)
+    assert bs == bs16 + 256
+
+
 def test_workspace_holds_one_dx_accumulator_per_k_part(lib):
     # N=4096, H=2048: the dx product has 16 x 8 = 128 output tiles, half the
     # 256 CUs, so each slab's columns are split in two parts with an fp32

@@ -24,7 +24,15 @@ from flce_gpu_util import GRAD_RTOL, LOSS_RTOL, LSE_RTOL, device_inputs, rel, ru
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-FULL = ["n4096_h2048_v32000", "n8192_h4096_v128256", "n32768_h2048_v128000", "n16384_h1024_v256000"]
+FULL = ["n4096_h2048_v32000", "n8192_h4096_v128256", "n32768_h2048_v128000", "n16384_h1024_v256000",
+        "n8192_h4096_v128256_f16"]
+
+
+def _x_rows(inp, rows):
+    """Exact fp64 copy of the chosen rows of x."""
+    if inp.w.dtype == "bf16":
+        return synth.bf16_bits_to_f64(inp.x[rows])
+    return inp.x[rows].astype(np.float64)
 N_SAMPLE = 12
 
 
@@ -59,14 +67,14 @@ def test_full_size_sampled_rows(cache, name):
         np.testing.assert_allclose(got["loss"][0], got_none["loss"].sum() / T, rtol=1e-5)
     rows = O.sample_rows(w.N, N_SAMPLE, seed=w.seed)
     print(f"[gpu] full size {name}: oracle on {rows.size} rows", flush=True)
-    x_rows = synth.bf16_bits_to_f64(inp.x[rows])
+    x_rows = _x_rows(inp, rows)
     g_rows = inp.grad[rows] if w.reduction == "none" else inp.grad
     r = O.rows(x_rows, W64, b64, inp.targets[rows], T, g_rows, w.label_smoothing, w.z_loss_scale,
                w.ignore_index, w.reduction)
     assert rel(got["lse"][rows], r["lse"]) <= LSE_RTOL
     assert rel(got_none["loss"][rows], r["row_loss"]) <= LOSS_RTOL
     rows_t = torch.from_numpy(rows).to(got["dx"].device)
-    assert rel(to_f64(got["dx"][rows_t]), r["dx"]) <= GRAD_RTOL["bf16"]
+    assert rel(to_f64(got["dx"][rows_t]), r["dx"]) <= GRAD_RTOL[w.dtype]
     assert bool(torch.isfinite(got["dW"]).all()) and bool(torch.isfinite(got["dx"]).all())
     if got["db"] is not None:
         assert bool(torch.isfinite(got["db"]).all())
@@ -84,7 +92,7 @@ def test_full_size_sixteen_live_rows(cache, name):
     print(f"[gpu] full size {name}: 16 live rows, GPU run", flush=True)
     got = run(sparse, raw=True)
     print(f"[gpu] full size {name}: oracle", flush=True)
-    x_live = synth.bf16_bits_to_f64(inp.x[live])
+    x_live = _x_rows(inp, live)
     g = inp.grad[live] if w.reduction == "none" else inp.grad
     r = O.rows(x_live, W64, b64, targets[live], 16, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
                w.reduction)
@@ -99,14 +107,14 @@ def test_full_size_sixteen_live_rows(cache, name):
     assert rel(got["loss"], ref_loss) <= LOSS_RTOL
     dev = got["dx"].device
     live_t = torch.from_numpy(live).to(dev)
-    assert rel(to_f64(got["dx"][live_t]), r["dx"]) <= GRAD_RTOL["bf16"]
+    assert rel(to_f64(got["dx"][live_t]), r["dx"]) <= GRAD_RTOL[w.dtype]
     dead = torch.ones(w.N, dtype=torch.bool, device=dev)
     dead[live_t] = False
     assert bool((got["dx"][dead] == 0).all())
     if got["db"] is not None:
-        assert rel(to_f64(got["db"]), r["dz"].sum(axis=0)) <= GRAD_RTOL["bf16"]
+        assert rel(to_f64(got["db"]), r["dz"].sum(axis=0)) <= GRAD_RTOL[w.dtype]
     vs = np.unique(np.concatenate([targets[live], O.sample_rows(w.V, 48, seed=w.seed + 2)]))
     dW_ref = r["dz"][:, vs].T @ x_live
-    assert rel(to_f64(got["dW"][torch.from_numpy(vs).to(dev)]), dW_ref) <= GRAD_RTOL["bf16"]
+    assert rel(to_f64(got["dW"][torch.from_numpy(vs).to(dev)]), dW_ref) <= GRAD_RTOL[w.dtype]
     del got
     torch.cuda.empty_cache()

@@ -26,6 +26,7 @@ W_ = synth.WORKLOADS
 CASES = {
     "c3_small": synth.scaled(W_["n8192_h4096_v128256"], "c3_small", N=600, H=328, V=2083, n_ignored=30),
     "c5_small": synth.scaled(W_["n16384_h1024_v256000"], "c5_small", N=777, H=128, V=5003),
+    "c3_f16": synth.scaled(W_["n8192_h4096_v128256"], "c3_f16", N=600, H=328, V=2083, n_ignored=30, dtype="f16"),
     "f32_none": synth.scaled(W_["tiny_f32"], "f32_none", N=300, H=136, V=1100, n_ignored=11, label_smoothing=0.1,
                              z_loss_scale=1e-3, reduction="none", grad="vector_normal", seed=8),
 }

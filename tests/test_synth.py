@@ -48,6 +48,26 @@ def test_bf16_rounding_is_nearest_even():
     np.testing.assert_array_equal(synth.f64_to_bf16_bits(v32), tb32)
 
 
+def test_f16_draws_round_to_nearest_even():
+    # the fp16 workloads round each fp64 draw once to half, nearest-even
+    a = synth.normal(44, "x", 50001, 1.0, "f16")
+    assert a.dtype == np.float16
+    key = synth.stream_key(44, "x")
+    v = synth._normals_chunk(key, 0, 25001).reshape(-1)[:50001]
+    h = a.astype(np.float64)
+    up = np.nextafter(a, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(a, np.float16(-np.inf)).astype(np.float64)
+    assert np.all(np.abs(v - h) <= np.abs(v - up)) and np.all(np.abs(v - h) <= np.abs(v - dn))
+    # agrees with torch's fp32 -> fp16 rounding on fp32-representable values (torch
+    # converts fp64 through fp32, a double rounding, so it is not compared on v)
+    v32 = v.astype(np.float32)
+    np.testing.assert_array_equal(torch.from_numpy(v32).to(torch.float16).numpy(),
+                                  v32.astype(np.float64).astype(np.float16))
+    # and ties go to the even pattern
+    ties = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -(1.0 + 2.0 ** -11)])
+    assert np.all(ties.astype(np.float16).view(np.uint16) % 2 == 0)
+
+
 def test_normal_moments_and_determinism():
     a = synth.normal(42, "x", 200001, 2.0, "bf16")
     b = synth.normal(42, "x", 200001, 2.0, "bf16")
