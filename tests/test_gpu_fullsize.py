@@ -28,6 +28,17 @@ FULL = ["n4096_h2048_v32000", "n8192_h4096_v128256", "n32768_h2048_v128000", "n1
         "n8192_h4096_v128256_f16"]
 
 
+def _out(ref, dtype):
+    """The reference as the output dtype can hold it, for fp16.  With a mean
+    over ~7800 rows and W ~ N(0, 1/H), |dx| is about 2e-6 at the Llama-3-sized
+    head: subnormal in fp16 (spacing 6e-8), so rounding the exact result to
+    fp16 alone costs about 1% (the reason fp16 training scales its loss).
+    Compared with the rounded reference, the tolerance measures the kernels'
+    own error.  bf16 and fp32 outputs have fp32's exponent range and are
+    compared with the exact result."""
+    return ref.astype(np.float16).astype(np.float64) if dtype == "f16" else ref
+
+
 def _x_rows(inp, rows):
     """Exact fp64 copy of the chosen rows of x."""
     if inp.w.dtype == "bf16":
@@ -74,7 +85,7 @@ def test_full_size_sampled_rows(cache, name):
     assert rel(got["lse"][rows], r["lse"]) <= LSE_RTOL
     assert rel(got_none["loss"][rows], r["row_loss"]) <= LOSS_RTOL
     rows_t = torch.from_numpy(rows).to(got["dx"].device)
-    assert rel(to_f64(got["dx"][rows_t]), r["dx"]) <= GRAD_RTOL[w.dtype]
+    assert rel(to_f64(got["dx"][rows_t]), _out(r["dx"], w.dtype)) <= GRAD_RTOL[w.dtype]
     assert bool(torch.isfinite(got["dW"]).all()) and bool(torch.isfinite(got["dx"]).all())
     if got["db"] is not None:
         assert bool(torch.isfinite(got["db"]).all())
@@ -107,14 +118,14 @@ def test_full_size_sixteen_live_rows(cache, name):
     assert rel(got["loss"], ref_loss) <= LOSS_RTOL
     dev = got["dx"].device
     live_t = torch.from_numpy(live).to(dev)
-    assert rel(to_f64(got["dx"][live_t]), r["dx"]) <= GRAD_RTOL[w.dtype]
+    assert rel(to_f64(got["dx"][live_t]), _out(r["dx"], w.dtype)) <= GRAD_RTOL[w.dtype]
     dead = torch.ones(w.N, dtype=torch.bool, device=dev)
     dead[live_t] = False
     assert bool((got["dx"][dead] == 0).all())
     if got["db"] is not None:
-        assert rel(to_f64(got["db"]), r["dz"].sum(axis=0)) <= GRAD_RTOL[w.dtype]
+        assert rel(to_f64(got["db"]), _out(r["dz"].sum(axis=0), w.dtype)) <= GRAD_RTOL[w.dtype]
     vs = np.unique(np.concatenate([targets[live], O.sample_rows(w.V, 48, seed=w.seed + 2)]))
     dW_ref = r["dz"][:, vs].T @ x_live
-    assert rel(to_f64(got["dW"][torch.from_numpy(vs).to(dev)]), dW_ref) <= GRAD_RTOL[w.dtype]
+    assert rel(to_f64(got["dW"][torch.from_numpy(vs).to(dev)]), _out(dW_ref, w.dtype)) <= GRAD_RTOL[w.dtype]
     del got
     torch.cuda.empty_cache()
