@@ -38,12 +38,16 @@ flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
 
 // Vocabulary slab width for the backward: the wider of (a) enough vocabulary
 // tiles that the dW contraction of one slab (H/256 x slab/256 output tiles)
-// fills every CU twice and (b) the widest slab within 256 MiB whose dW tiles
-// fill whole rounds of 256 CUs; capped at 1 GiB.  Every slab after the first
-// costs one read-modify-write pass over the fp32 dx accumulator
-// (N x H x 8 bytes), which all CUs make at the same moment, so wider slabs
-// save HBM time; (b) gives the Llama-3-sized head (N=8192, H=4096,
-// V=128256) 16384 columns, with all extra memory at 9.7% of its fp32 logits.
+// fills every CU twice (once when the fp32 dx accumulator is under 128 MiB)
+// and (b) the widest slab within 256 MiB whose dW tiles fill whole rounds of
+// 256 CUs; capped at 1 GiB.  Every slab after the first costs one
+// read-modify-write pass over the fp32 dx accumulator (N x H x 8 bytes),
+// which all CUs make at the same moment, so wider slabs save HBM time when
+// the accumulator is large; when it is small, a narrower slab is faster (at
+// N=16384, H=1024, V=256000: 16384 columns instead of 32768, backward -1.7%,
+// as more of the slab is still cached when dx and dW read it).  (b) gives the
+// Llama-3-sized head (N=8192, H=4096, V=128256) 16384 columns, with all extra
+// memory at 9.7% of its fp32 logits.
 // FLCE_DEBUG_SLAB_COLS (a positive multiple of 256) overrides it; the tests
 // use it to force many slabs.
 int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
@@ -54,7 +58,8 @@ int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
     if (c > 0 && c % kTile == 0) return c < vmax ? c : vmax;
   }
   const int64_t th = cdiv(H, kTile);
-  int64_t want = cdiv(2 * kCUs, th) * kTile;
+  const bool small_acc = (size_t)N * (size_t)H * 4 < (size_t(128) << 20);
+  int64_t want = cdiv((small_acc ? 1 : 2) * kCUs, th) * kTile;
   const int64_t round_cols = kTile * (kCUs / std::gcd((int64_t)kCUs, th));   // whole dW rounds
   const int64_t by_bytes = (int64_t)(kSlabTargetBytes / (size_t)(N * es)) / round_cols * round_cols;
   if (by_bytes > want) want = by_bytes;

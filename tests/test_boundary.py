@@ -103,13 +103,14 @@ def test_workspace_holds_one_dx_accumulator_per_k_part(lib):
 
 
 def test_slab_width_heuristic(lib):
-    # the wider of: one slab's dW tiles cover 256 CUs twice, or the widest
+    # the wider of: one slab's dW tiles cover 256 CUs twice (once when the fp32 dx
+    # accumulator is under 128 MiB), or the widest
     # slab within 256 MiB whose dW tiles fill whole rounds of 256 CUs; capped
     # at 1 GiB and at V rounded up to a tile
     assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 16384
     assert _lib.flce_backward_slab_cols(4096, 2048, 32000, 1) == 32000
     assert _lib.flce_backward_slab_cols(32768, 2048, 128000, 1) == 16384
-    assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 32768
+    assert _lib.flce_backward_slab_cols(16384, 1024, 256000, 1) == 16384   # small accumulator: one dW round
     assert _lib.flce_backward_slab_cols(64, 128, 1000, 0) == 1024     # capped at V rounded up
     assert _lib.flce_backward_slab_cols(64, 12, 1000, 0) == 0         # H % 8 != 0
 
