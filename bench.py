@@ -251,7 +251,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path would shard "
-              "tokens across GPUs with a dW reduce-scatter, which this build does not implement)",
+              "tokens across GPUs with a dW reduce-scatter, which this library does not implement)",
               file=sys.stderr)
         sys.exit(2)
 

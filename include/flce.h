@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, misalignment, eps/s out of range */
-  FLCE_ERR_UNSUPPORTED = 2,      /* dtype or shape this build does not handle (e.g. H % 8 != 0) */
+  FLCE_ERR_UNSUPPORTED = 2,      /* dtype or shape the library does not handle (e.g. H % 8 != 0) */
   FLCE_ERR_WORKSPACE_TOO_SMALL = 3,
   FLCE_ERR_HIP = 4               /* a HIP launch failed; see hipGetLastError on the caller side */
 } flce_status;
