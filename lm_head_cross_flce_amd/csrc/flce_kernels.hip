@@ -107,9 +107,10 @@ __device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&
 //
 // XFIRST: each K block's x copies are issued before W's.  Same-box A/Bs of the
 // forward: x first is 3.6% faster at N=8192, H=4096, V=128256 (8 phases),
-// 4.4% at N=4096 (16 phases) and 3.1% at N=16384 (4 phases), but 0.7% slower
-// at N=32768 (2 phases, where 16 token tiles per XCD share each W tile); the
-// launch takes x first when there are at least 4 phases.
+// 4.4% at N=4096 (16 phases) and 3.1% at N=16384 (4 phases at the time), but
+// was 0.7% slower with 2 phases (16 token tiles per XCD sharing each W tile).
+// The launch takes x first with at least 4 phases, which the phase rule
+// (at least 8 when the vocabulary has 8 tiles) makes the usual case.
 template <class T, bool BIAS, bool SMOOTH, bool XFIRST>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   FLCE_LDS(L, T);
