@@ -84,9 +84,13 @@ typedef enum {
 /*
  * Workspace bytes that flce_forward (*fwd_bytes) and flce_backward
  * (*bwd_bytes) need for this problem.  Pure host arithmetic: no HIP call.
- * Either output pointer may be NULL.  The backward figure includes one
+ * Either output pointer may be NULL.  The forward figure holds per-token
+ * partial statistics for each of P vocabulary phases (P x N x 16 bytes, P =
+ * min(V/256 rounded up, max(8, 256 / (N/256 rounded up)))) and per-row losses.
+ * The backward figure includes one
  * vocabulary slab of dlogits [N, slab] in the input dtype and an fp32 [N, H]
- * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch.  When the dx
+ * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch (and, for fp16,
+ * 256 bytes for the slab's scale).  When the dx
  * product has too few 256 x 256 output tiles to fill the GPU (at most half
  * of its 256 CUs), each slab's columns are split into P <= 8 parts, each with
  * its own fp32 [N, H] accumulator (P x N x H x 4 bytes, at most about 64 MB).
