@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(1024) fwd_finalize_kernel(FwdLaunch a) {
 }
 
 template <class T, bool XFIRST>
-static void launch_fwd_lse(const FwdLaunch& a, hipStream_t st) {
+static void launch_fwd_lse_order(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
   if (bias && smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
@@ -303,10 +303,10 @@ static void launch_fwd_lse(const FwdLaunch& a, hipStream_t st) {
 template <class T>
 static void launch_fwd_lse(const FwdLaunch& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    if (a.P >= 4) launch_fwd_lse<T, true>(a, st);
-    else launch_fwd_lse<T, false>(a, st);
+    if (a.P >= 4) launch_fwd_lse_order<T, true>(a, st);
+    else launch_fwd_lse_order<T, false>(a, st);
   } else {
-    launch_fwd_lse<T, false>(a, st);   // fp32 operands are staged through registers, not by block copies
+    launch_fwd_lse_order<T, false>(a, st);   // fp32 operands are staged through registers, not by block copies
   }
 }
 
