@@ -54,7 +54,9 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 // Logits are scale * acc + bias, the bias already multiplied by scale.
 // rb: tile row index of the lane's row 0 (v0 + wave row offset + 4 g); t: the
 // token's target minus rb (negative if ignored or elsewhere).
-template <bool SMOOTH, bool RAGGED>
+// UNIT: no bias and a logit scale of 1, so the logits are the accumulators
+// themselves (skips one fma per logit; bit-identical).
+template <bool SMOOTH, bool RAGGED, bool UNIT = false>
 __device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&bias)[8], float scale, float& m,
                                            float& d, float& sz, float& zy, int t, int rb, int V) {
   float z[32];
@@ -64,7 +66,7 @@ __device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&
     const f32x4 v = acc_read4(acc[i][j]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float x = fmaf(v[r], scale, bias[i][r]);
+      float x = UNIT ? v[r] : fmaf(v[r], scale, bias[i][r]);
       if (RAGGED) {
         const bool ok = rb + 16 * i + r < V;
         if (SMOOTH) zs += ok ? x : 0.f;
@@ -174,10 +176,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
     }
     const int rb = v0 + rloc;
     const bool full = v0 + kTile <= a.V;
+    const bool unit = !BIAS && a.logit_scale == 1.f;   // logits are the accumulators themselves
     acc_drain();
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (full) lse_column<SMOOTH, false>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      if (full && unit) lse_column<SMOOTH, false, true>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
+      else if (full) lse_column<SMOOTH, false>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
       else lse_column<SMOOTH, true>(acc, j, bias, a.logit_scale, m[j], d[j], sz[j], zy[j], ycol[j] - rb, rb, a.V);
       // One column at a time keeps the live logits to 32 registers.
       __builtin_amdgcn_sched_barrier(0);
