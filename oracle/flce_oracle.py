@@ -60,11 +60,17 @@ and fp32 widen exactly).  Memory is bounded by processing rows in chunks, so no
 from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
+from contextlib import contextmanager
 from dataclasses import dataclass
 import os
 from typing import Optional, Sequence
 
 import numpy as np
+
+try:
+    from threadpoolctl import threadpool_limits
+except ImportError:  # pragma: no cover - optional: only affects speed
+    threadpool_limits = None
 
 REDUCTIONS = ("none", "sum", "mean")
 
@@ -178,6 +184,19 @@ def _pool():
     return ThreadPoolExecutor(_workers())
 
 
+@contextmanager
+def _blas_per_chunk(nchunks):
+    """While several row chunks run on the thread pool, each chunk's matrix
+    products use one BLAS thread (the pool is the parallelism; BLAS pools
+    inside every worker would oversubscribe the cores).  Execution only: the
+    arithmetic is unchanged."""
+    if nchunks > 1 and threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            yield
+    else:
+        yield
+
+
 def forward(x, W, b, targets, eps=0.0, s=0.0, ignore_index=-100, reduction="mean",
             rows_per_chunk=256, logit_scale=1.0) -> ForwardResult:
     """Loss, per-row lse and the non-ignored count (and the z-loss term alone)."""
@@ -192,8 +211,9 @@ def forward(x, W, b, targets, eps=0.0, s=0.0, ignore_index=-100, reduction="mean
         lse[lo:hi] = _lse(z)
         rl[lo:hi] = _row_loss(z, lse[lo:hi], t[lo:hi], valid[lo:hi], eps, s, V)
 
-    with _pool() as ex:
-        list(ex.map(work, _chunks(N, rows_per_chunk)))
+    chunks = _chunks(N, rows_per_chunk)
+    with _blas_per_chunk(len(chunks)), _pool() as ex:
+        list(ex.map(work, chunks))
     T = int(np.sum(valid))
     rzl = np.where(valid, s * lse * lse, 0.0)
     return ForwardResult(_reduce(rl, reduction, T), lse, rl, T, _reduce(rzl, reduction, T), rzl)
@@ -224,7 +244,7 @@ def backward(x, W, b, targets, grad, eps=0.0, s=0.0, ignore_index=-100,
     # Chunks run in parallel batches sized so their [V, H] partials stay under
     # ~2 GB; partials are added in chunk order.
     batch = max(1, min(_workers(), int(2e9 // (8 * V * H + 1))))
-    with _pool() as ex:
+    with _blas_per_chunk(min(batch, len(chunks))), _pool() as ex:
         for k0 in range(0, len(chunks), batch):
             ks = range(k0, min(len(chunks), k0 + batch))
             list(ex.map(work, ks))
@@ -267,6 +287,62 @@ def rows(x_rows, W, b, targets_rows, T, grad_rows, eps=0.0, s=0.0, ignore_index=
     return {"lse": lse, "row_loss": rl, "dz": dz, "dx": dz @ W64}
 
 
+@dataclass
+class DenseColumnsResult:
+    loss: np.ndarray        # reduced like the forward's loss
+    lse: np.ndarray         # [N]
+    row_loss: np.ndarray    # [N]
+    n_valid: int
+    db: np.ndarray          # [V]: sum over all rows of dz (formed with or without a bias)
+    dW_cols: np.ndarray     # [len(cols), H]: rows ``cols`` of dW, summed over all N rows
+    dx: Optional[np.ndarray]  # [N, H] if asked for
+
+
+def dense_columns(x, W, b, targets, grad, cols, eps=0.0, s=0.0, ignore_index=-100, reduction="mean",
+                  rows_per_chunk=256, logit_scale=1.0, want_dx=True) -> DenseColumnsResult:
+    """Every token's lse, loss and dx row, all of db, and the dW rows ``cols``.
+
+    The same definition as ``forward`` and ``backward`` (each row chunk holds
+    its logits over the whole vocabulary, so its lse and its dlogits rows are
+    complete), restricted to the outputs that a check of a large problem can
+    afford: dW[j] = sum_n dz[n, j] x[n] only for j in ``cols``, so the cost
+    is one logits product plus one dx product.  db_j = sum_n dz[n, j] and the
+    dW rows sum the chunks' contributions in chunk order.
+    """
+    N, H, V, t, valid = _check(x, W, b, targets, eps, s, ignore_index, reduction)
+    W64, b64 = _f64(W), _f64(b)
+    cols = np.asarray(cols, dtype=np.int64).reshape(-1)
+    if cols.size and (cols.min() < 0 or cols.max() >= V):
+        raise ValueError("cols must lie in [0, V)")
+    T = int(np.sum(valid))
+    lse = np.empty(N)
+    rl = np.empty(N)
+    dx = np.empty((N, H)) if want_dx else None
+    chunks = _chunks(N, rows_per_chunk)
+    parts = [None] * len(chunks)
+
+    def work(k):
+        lo, hi = chunks[k]
+        x64 = _f64(x[lo:hi])
+        z = _logits(x64, W64, b64, logit_scale)
+        lse[lo:hi] = _lse(z)
+        rl[lo:hi] = _row_loss(z, lse[lo:hi], t[lo:hi], valid[lo:hi], eps, s, V)
+        c = _coeff(valid[lo:hi], grad, reduction, T, np.arange(lo, hi))
+        dz = _dlogits(z, lse[lo:hi], t[lo:hi], valid[lo:hi], c, eps, s, V, logit_scale)
+        if want_dx:
+            dx[lo:hi] = dz @ W64
+        parts[k] = (dz.sum(axis=0), dz[:, cols].T @ x64)
+
+    db = np.zeros(V)
+    dWc = np.zeros((cols.size, H))
+    with _blas_per_chunk(len(chunks)), _pool() as ex:
+        list(ex.map(work, range(len(chunks))))
+    for pb, pw in parts:
+        db += pb
+        dWc += pw
+    return DenseColumnsResult(_reduce(rl, reduction, T), lse, rl, T, db, dWc, dx)
+
+
 def count_valid(targets, ignore_index=-100) -> int:
     return int(np.sum(np.asarray(targets).reshape(-1) != ignore_index))
 
@@ -289,5 +365,5 @@ def sample_rows(N: int, k: int, seed: int = 0) -> np.ndarray:
     return np.array(sorted(picks), dtype=np.int64)
 
 
-__all__: Sequence[str] = ("forward", "backward", "rows", "count_valid", "loss_and_grads",
-                          "sample_rows", "ForwardResult", "BackwardResult", "REDUCTIONS")
+__all__: Sequence[str] = ("forward", "backward", "rows", "dense_columns", "count_valid", "loss_and_grads",
+                          "sample_rows", "ForwardResult", "BackwardResult", "DenseColumnsResult", "REDUCTIONS")

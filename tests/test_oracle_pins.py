@@ -292,6 +292,53 @@ def test_rows_matches_full_oracle():
         np.testing.assert_allclose(r["dx"], bw.dx[sel], rtol=1e-12, atol=1e-16)
 
 
+@pytest.mark.parametrize("red", RED)
+@pytest.mark.parametrize("bias", [True, False])
+def test_dense_columns_matches_full_oracle_and_brute_force(red, bias):
+    # The all-token check of large problems: lse, per-row loss, dx, all of db
+    # and chosen dW rows, against the full oracle (rows per chunk smaller than
+    # N, so several chunks are summed) and against the pure-loop brute force.
+    rng = np.random.default_rng(16)
+    N, H, V = 9, 6, 13
+    x, W, b, t = _rand_problem(rng, N, H, V, bias=bias, n_ign=2, scale=2.0)
+    g = _grad(rng, red, N)
+    eps, s, alpha = 0.1, 1e-2, 1.3
+    cols = np.array([0, 4, 12, int(t[t >= 0][0])])
+    d = O.dense_columns(x, W, b, t, g, cols, eps=eps, s=s, reduction=red, rows_per_chunk=4, logit_scale=alpha)
+    f = O.forward(x, W, b, t, eps=eps, s=s, reduction=red, logit_scale=alpha)
+    bw = O.backward(x, W, b, t, g, eps=eps, s=s, reduction=red, logit_scale=alpha)
+    assert d.n_valid == f.n_valid
+    np.testing.assert_allclose(d.loss, f.loss, rtol=1e-13)
+    np.testing.assert_allclose(d.lse, f.lse, rtol=1e-14)
+    np.testing.assert_allclose(d.row_loss, f.row_loss, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(d.dx, bw.dx, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(d.dW_cols, bw.dW[cols], rtol=1e-12, atol=1e-16)
+    loss, lse, rl, dx, dW, db = brute.run(x.tolist(), W.tolist(), None if b is None else b.tolist(), t.tolist(),
+                                          g.tolist(), eps, s, -100, red, logit_scale=alpha)
+    np.testing.assert_allclose(d.dW_cols, np.array(dW)[cols], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(d.dx, np.array(dx), rtol=1e-12, atol=1e-13)
+    if bias:
+        np.testing.assert_allclose(d.db, bw.db, rtol=1e-12, atol=1e-16)
+        np.testing.assert_allclose(d.db, np.array(db), rtol=1e-12, atol=1e-13)
+    # Without a bias db is still the dlogits' column sums: dW's rows against
+    # a bias-free problem agree with the same sums formed by the brute force.
+    else:
+        _, _, _, _, _, db_b = brute.run(x.tolist(), W.tolist(), [0.0] * V, t.tolist(), g.tolist(), eps, s,
+                                        -100, red, logit_scale=alpha)
+        np.testing.assert_allclose(d.db, np.array(db_b), rtol=1e-12, atol=1e-13)
+    d2 = O.dense_columns(x, W, b, t, g, cols, eps=eps, s=s, reduction=red, logit_scale=alpha, want_dx=False)
+    assert d2.dx is None
+    np.testing.assert_array_equal(d2.dW_cols, O.dense_columns(x, W, b, t, g, cols, eps=eps, s=s, reduction=red,
+                                                              logit_scale=alpha).dW_cols)
+
+
+def test_dense_columns_rejects_columns_outside_the_vocabulary():
+    rng = np.random.default_rng(17)
+    x, W, b, t = _rand_problem(rng, 4, 3, 5)
+    with pytest.raises(ValueError):
+        O.dense_columns(x, W, b, t, np.ones(1), [5])
+
+
 # --- P9: scale sanity (not a pin): unit-variance logits give ~ log V + 1/2 ----
 
 def test_p9_scale_sanity():
