@@ -504,9 +504,14 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   if (BIAS) bt.publish(L.bias, tid);
   lds_barrier();
   acc_drain();
-  // Vocabulary rows past V read W and b as zeros, so their dlogits are finite
-  // and are stored unmasked: the weight-gradient and bias kernels drop those
-  // columns and the input-gradient kernel multiplies them by zero rows of W.
+  // Vocabulary rows past V read W and b as zeros; their dlogits are stored as
+  // exact zeros.  The input-gradient product reads the slab up to the next
+  // multiple of 8 columns (whole 16-byte copies), and the unmasked value of
+  // such a row, c (1 + 2 s lse) e^(-lse), overflows to inf when lse is very
+  // negative (a large negative bias; sooner with fp16's scaled slab), which
+  // times W's zero rows would give NaN.  Only the vocabulary's last tile is
+  // ragged (vleft < 256), so the mask is a wave-uniform branch.
+  const int vleft = a.V - v0;
   // Slab rows of this tile's tokens, from token n0 on.
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
   const float sl2e = a.logit_scale * kLog2e;   // p = 2^((scale (z + b)) log2 e - lse log2 e)
@@ -543,6 +548,13 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
         for (int r = 0; r < 4; ++r) {
           if (t0 == r) dz[r] -= cf[2];
           if (t1 == r) dz[4 + r] -= cf[2];
+        }
+      }
+      if (vleft < kTile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (r0 + r >= vleft) dz[r] = 0.f;
+          if (r1 + r >= vleft) dz[4 + r] = 0.f;
         }
       }
       if (DB) {

@@ -37,13 +37,47 @@ def _prep(x, W, b, targets):
         raise ValueError("x must be [N, H] and W must be [V, H]")
     if not x.is_cuda:
         raise ValueError("tensors must live on a GPU")
+    if W.shape[1] != x.shape[1]:
+        raise ValueError("x and W disagree on the hidden size")
     if W.dtype != x.dtype or (b is not None and b.dtype != x.dtype):
         raise TypeError("x, W and b must share one dtype")
-    x = x.contiguous()
-    W = W.contiguous()
+    if W.device != x.device or targets.device != x.device or (b is not None and b.device != x.device):
+        raise ValueError("x, W, b and targets must be on one device")
+    if b is not None and b.shape != (W.shape[0],):
+        raise ValueError("b must be [V]")
+    x = _pad_hidden(x.contiguous())
+    W = _pad_hidden(W.contiguous())
     b = b.contiguous() if b is not None else None
     targets = targets.reshape(-1).to(torch.int64).contiguous()
+    if targets.numel() != x.shape[0]:
+        raise ValueError("targets must have one entry per row of x")
     return x, W, b, targets
+
+
+def _pad_hidden(t: torch.Tensor) -> torch.Tensor:
+    """The library moves rows in 16-byte pieces and needs H % 8 == 0: other H
+    get zero columns up to the next multiple of 8 (a copy), which changes no
+    logit, loss or gradient entry of the original columns."""
+    H = t.shape[1]
+    if H % 8 == 0:
+        return t
+    out = torch.zeros(t.shape[0], H + (-H) % 8, dtype=t.dtype, device=t.device)
+    out[:, :H] = t
+    return out
+
+
+def _check_out(t: Optional[torch.Tensor], shape, like: torch.Tensor, what: str) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {like.dtype} tensor of shape {tuple(shape)} on {like.device}")
+
+
+def _check_ctx(lse: torch.Tensor, n_valid: torch.Tensor, N: int, dev) -> None:
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (N,) or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError(f"lse must be a contiguous float32 [{N}] tensor on {dev} (as flce_forward returns it)")
+    if n_valid.dtype != torch.int64 or n_valid.numel() != 1 or n_valid.device != dev:
+        raise ValueError(f"n_valid must be an int64 [1] tensor on {dev} (as flce_forward returns it)")
 
 
 def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype, has_bias: bool,
@@ -97,11 +131,13 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
                   out: Optional[Tuple] = None, logit_scale: float = 1.0, accumulate: bool = False):
     """Returns (dx, dW, db) in the input dtype (None where not requested).  With
     accumulate, the gradients are added to the ``out`` tensors' contents."""
+    H0 = x.shape[1] if x.dim() == 2 else -1
     x, W, b, targets = _prep(x, W, b, targets)
     N, H = x.shape
     V = W.shape[0]
     dt, red = _dtype_code(x), _reduction_code(reduction)
     dev = x.device
+    _check_ctx(lse, n_valid, N, dev)
     g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
     if g.numel() != (N if reduction == "none" else 1):
         raise ValueError("grad_loss must have N entries for none and one otherwise")
@@ -110,26 +146,49 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
         workspace = torch.empty(max(bwd_bytes, 1), dtype=torch.uint8, device=dev)
     if out is not None:
         dx, dW, db = out
+        _check_out(dx, (N, H0), x, "out dx")
+        _check_out(dW, (V, H0), x, "out dW")
+        _check_out(db, (V,), x, "out db")
     else:
         if accumulate:
             raise ValueError("accumulate needs the out tensors to add to")
-        dx = torch.empty_like(x) if need_dx else None
-        dW = torch.empty_like(W) if need_dW else None
+        dx = torch.empty(N, H0, dtype=x.dtype, device=dev) if need_dx else None
+        dW = torch.empty(V, H0, dtype=x.dtype, device=dev) if need_dW else None
         db = torch.empty_like(b) if (need_db and b is not None) else None
+    # H padded to a multiple of 8: the library writes padded gradients, whose
+    # first H0 columns are the result (with accumulate, they start from out's).
+    kx, kW = dx, dW
+    if H != H0:
+        kx = _pad_hidden(dx) if (dx is not None and accumulate) else (
+            torch.empty(N, H, dtype=x.dtype, device=dev) if dx is not None else None)
+        kW = _pad_hidden(dW) if (dW is not None and accumulate) else (
+            torch.empty(V, H, dtype=x.dtype, device=dev) if dW is not None else None)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if logit_scale == 1.0 and not accumulate:
             _lib.flce_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
                                float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
-                               lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db),
+                               lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(kx), _ptr(kW), _ptr(db),
                                workspace.data_ptr(), workspace.numel(), stream)
         else:
             _lib.flce_backward_ex(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
                                   float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
                                   _lib.options(logit_scale, accumulate, None), lse.data_ptr(), n_valid.data_ptr(),
-                                  g.data_ptr(), _ptr(dx), _ptr(dW), _ptr(db), workspace.data_ptr(),
+                                  g.data_ptr(), _ptr(kx), _ptr(kW), _ptr(db), workspace.data_ptr(),
                                   workspace.numel(), stream)
+    if H != H0:
+        if dx is not None:
+            dx.copy_(kx[:, :H0])
+        if dW is not None:
+            dW.copy_(kW[:, :H0])
     return dx, dW, db
+
+
+def _shard_hidden(x: torch.Tensor) -> None:
+    # The shard entry points hand the caller fp32 dx partials of x's width,
+    # so they take H as the library does (a multiple of 8) rather than pad.
+    if x.dim() == 2 and x.shape[1] % 8 != 0:
+        raise ValueError("the vocabulary-shard entry points need H % 8 == 0; pad x and W with zero columns")
 
 
 def flce_shard_workspace_size(N: int, H: int, V_shard: int, dtype: torch.dtype,
@@ -143,6 +202,7 @@ def flce_shard_forward(x: torch.Tensor, W_shard: torch.Tensor, b_shard: Optional
                        ignore_index: int = -100, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-token statistics float32 [N, 4] = (m, d, sum z, z_y) over the shard's rows
     W[vocab_start : vocab_start + V_shard] (W_shard); targets are global indices."""
+    _shard_hidden(x)
     x, W_shard, b_shard, targets = _prep(x, W_shard, b_shard, targets)
     N, H = x.shape
     V_shard = W_shard.shape[0]
@@ -194,10 +254,12 @@ def flce_shard_backward(x: torch.Tensor, W_shard: torch.Tensor, b_shard: Optiona
                         workspace: Optional[torch.Tensor] = None):
     """Returns (dx_partial float32 [N, H], dW_shard, db_shard) (None where not requested).
     dx_partial: the buffer to write (or, with accumulate_dx, to add to); allocated if None."""
+    _shard_hidden(x)
     x, W_shard, b_shard, targets = _prep(x, W_shard, b_shard, targets)
     N, H = x.shape
     V_shard = W_shard.shape[0]
     dt, red, dev = _dtype_code(x), _reduction_code(reduction), x.device
+    _check_ctx(lse, n_valid, N, dev)
     g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
     if g.numel() != (N if reduction == "none" else 1):
         raise ValueError("grad_loss must have N entries for none and one otherwise")

@@ -120,8 +120,8 @@ def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def normal(seed: int, tag: str, count: int, std: float, dtype: str) -> np.ndarray:
-    """``count`` draws from N(0, std**2) rounded to ``dtype``.
+def normal(seed: int, tag: str, count: int, std: float, dtype: str, mean: float = 0.0) -> np.ndarray:
+    """``count`` draws from N(mean, std**2) rounded to ``dtype``.
 
     dtype "bf16" returns uint16 bit patterns; "f16" returns float16 (numpy's
     fp64 -> half conversion rounds to nearest-even); "f32" returns float32.
@@ -134,6 +134,8 @@ def normal(seed: int, tag: str, count: int, std: float, dtype: str) -> np.ndarra
     def work(p0: int) -> None:
         n = min(chunk_pairs, npairs - p0)
         vals = _normals_chunk(key, p0, n) * std
+        if mean != 0.0:
+            vals = vals + mean
         lo, hi = 2 * p0, min(count, 2 * (p0 + n))
         vals = vals[: hi - lo]
         if dtype == "bf16":
@@ -212,6 +214,7 @@ class Workload:
     x_std: float = 1.0
     w_std: Optional[float] = None  # None -> 1/sqrt(H)
     b_std: Optional[float] = None  # None -> no bias
+    b_mean: float = 0.0           # mean of the bias draws
     targets: str = "uniform"      # "uniform" or "zipf"
     zipf_a: float = 1.1
     n_ignored: int = 0
@@ -303,7 +306,7 @@ def make_inputs(w: Workload, parts=("x", "W", "b", "targets", "grad")) -> Inputs
     W = normal(s, "W", w.V * w.H, w_std, w.dtype).reshape(w.V, w.H) if "W" in parts else None
     b = None
     if w.b_std is not None and "b" in parts:
-        b = normal(s, "b", w.V, w.b_std, w.dtype)
+        b = normal(s, "b", w.V, w.b_std, w.dtype, w.b_mean)
     targets = None
     if "targets" in parts:
         if w.targets == "zipf":

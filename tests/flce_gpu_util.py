@@ -13,6 +13,16 @@ from lm_head_cross_flce_amd import synth
 LOSS_RTOL = 1e-3
 GRAD_RTOL = {"bf16": 1e-2, "f16": 1e-2, "f32": 1e-5}
 LSE_RTOL = 1e-5
+# Per-row (2-D outputs) and per-element (1-D outputs) bound, beside the
+# Frobenius bar: each row's relative error may be at most ROW_FACTOR times
+# the tensor's bar.  A row's error is a sum of the same independent rounding
+# terms as the whole tensor's, so typical rows sit near the Frobenius figure;
+# a wrong row (a wrong index, a missing or doubled term) errs by O(1).  Rows
+# far smaller than the tensor's typical row are measured against
+# ROW_FLOOR x the typical row norm instead, since their relative error is
+# dominated by the rounding of their larger neighbours' shared terms.
+ROW_FACTOR = 4.0
+ROW_FLOOR = 0.1
 
 
 def to_torch(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
@@ -68,3 +78,31 @@ def rel(a: np.ndarray, ref: np.ndarray) -> float:
     if nr == 0.0:
         return 0.0 if np.all(np.asarray(a) == 0.0) else float("inf")
     return float(np.linalg.norm(np.asarray(a) - ref) / nr)
+
+
+def row_rel_max(a: np.ndarray, ref: np.ndarray, floor: float = ROW_FLOOR) -> float:
+    """Largest per-row relative error (per element for 1-D arrays), each row's
+    reference norm floored at ``floor`` times the root-mean-square row norm.
+    Where the whole reference is zero, exact zeros are required."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if a.shape != ref.shape:
+        raise ValueError(f"shape mismatch {a.shape} vs {ref.shape}")
+    if ref.ndim == 1:
+        a, ref = a[:, None], ref[:, None]
+    err = np.linalg.norm(a - ref, axis=1)
+    nrm = np.linalg.norm(ref, axis=1)
+    typical = float(np.sqrt(np.mean(nrm * nrm)))
+    if typical == 0.0:
+        return 0.0 if np.all(a == 0.0) else float("inf")
+    return float(np.max(err / np.maximum(nrm, floor * typical)))
+
+
+def check_close(a, ref, tol: float, what: str = "") -> None:
+    """The parity bar: relative Frobenius error <= tol and every row within
+    ROW_FACTOR * tol (see row_rel_max)."""
+    e = rel(a, ref)
+    r = row_rel_max(a, ref)
+    print(f"  {what}: frobenius {e:.3e}, worst row {r:.3e}", flush=True)
+    assert e <= tol, (what, "frobenius", e, tol)
+    assert r <= ROW_FACTOR * tol, (what, "row", r, ROW_FACTOR * tol)

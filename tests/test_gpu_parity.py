@@ -46,6 +46,9 @@ CASES = {
     "bf16_v_lt_tile": _case("n8192_h4096_v128256", "bf16_v_lt_tile", N=33, H=72, V=100, n_ignored=3, seed=11),
     # with 1024-column slabs the last slab has 6 columns: the second input-gradient K part is empty
     "f32_v1030": _case("tiny_f32", "f32_v1030", N=64, H=128, V=1030, seed=12),
+    # H not a multiple of 8: the binding pads x and W with zero columns
+    "bf16_h100": _case("n8192_h4096_v128256", "bf16_h100", N=130, H=100, V=700, n_ignored=5, seed=14),
+    "f32_h13": _case("tiny_f32", "f32_h13", N=40, H=13, V=300, seed=15),
 }
 
 _oracle_cache = {}
@@ -155,6 +158,29 @@ def test_ignore_index_inside_vocabulary():
     check("ign5", got, f, bw)
 
 
+@pytest.mark.parametrize("dtype,b_mean", [("bf16", -120.0), ("f16", -20.0), ("f32", -105.0)])
+def test_ragged_vocabulary_with_very_negative_lse(dtype, b_mean):
+    # V = 1001 leaves a ragged last vocabulary tile, and a bias far below zero
+    # puts lse near b_mean (softmax is shift-invariant, so the exact gradients
+    # are ordinary).  The dlogits slab's padded vocabulary rows must hold
+    # zeros: the input-gradient product reads the slab up to the next multiple
+    # of 8 columns, where an unmasked c e^(-lse) overflows to inf and times
+    # W's zero rows gives NaN (fp16's slab is scaled to ~2^13 per unit of c, so
+    # lse ~ -13 suffices; fp32 arithmetic overflows past lse ~ -94 here).
+    name = f"ragged_neg_lse_{dtype}"
+    w = _case("n8192_h4096_v128256", name, dtype=dtype, N=300, H=136, V=1001, n_ignored=9,
+              label_smoothing=0.0, z_loss_scale=0.0, b_std=0.1, b_mean=b_mean, seed=13)
+    inp = synth.make_inputs(w)
+    _input_cache[name], CASES[name] = inp, w
+    print(f"[gpu] ragged vocabulary, lse ~ {b_mean}, {dtype}", flush=True)
+    got = run(inp)
+    f, bw = oracle(name)
+    assert f.lse.max() < b_mean + 10.0
+    for k in ("dx", "dW", "db"):
+        assert np.all(np.isfinite(got[k])), k
+    check(name, got, f, bw)
+
+
 def test_deterministic():
     inp = inputs("c3_small")
     dev = device_inputs(inp)
@@ -238,3 +264,49 @@ def test_no_reads_past_operands_or_of_unwritten_memory(name):
            "db": None if db is None else to_f64(db)}
     f, bw = oracle(name)
     check(name, got, f, bw)
+
+
+def test_padded_hidden_size_with_accumulation():
+    # H = 100: the padded gradients are sliced back, and accumulation adds to
+    # the caller's unpadded buffers.
+    inp = inputs("bf16_h100")
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    print("[gpu] padded H with accumulation", flush=True)
+    loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    f, bw = oracle("bf16_h100")
+    # start from values of the gradients' own size (the exact ones, times -0.5, in bf16)
+    base = tuple(torch.from_numpy(-0.5 * r).to(x.device).to(torch.bfloat16) for r in (bw.dx, bw.dW, bw.db))
+    out = tuple(o.clone() for o in base)
+    F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                    out=out, accumulate=True)
+    torch.cuda.synchronize()
+    for got, b0, ref, name in zip(out, base, (bw.dx, bw.dW, bw.db), ("dx", "dW", "db")):
+        assert rel(to_f64(got), to_f64(b0) + ref) <= GRAD_RTOL["bf16"], name
+
+
+def test_binding_rejects_bad_out_and_ctx_tensors():
+    inp = inputs("c3_small")
+    w = inp.w
+    x, W, b, t, g = device_inputs(inp)
+    loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    args = (x, W, b, t)
+    opts = (w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    bad_outs = [
+        (torch.empty(w.N - 1, w.H, dtype=x.dtype, device=x.device), None, None),          # too small
+        (torch.empty(w.N, w.H, dtype=torch.float32, device=x.device), None, None),        # wrong dtype
+        (None, torch.empty(w.H, w.V, dtype=x.dtype, device=x.device).t(), None),          # not contiguous
+        (None, None, torch.empty(w.V + 1, dtype=x.dtype, device=x.device)),               # wrong length
+    ]
+    print("[gpu] binding argument checks", flush=True)
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            F.flce_backward(*args, lse, nv, g, *opts, out=out)
+    with pytest.raises(ValueError):
+        F.flce_backward(*args, lse[:-1], nv, g, *opts)
+    with pytest.raises(ValueError):
+        F.flce_backward(*args, lse.double(), nv, g, *opts)
+    with pytest.raises(ValueError):
+        F.flce_backward(*args, lse, nv.int(), g, *opts)
+    with pytest.raises(ValueError):
+        F.flce_backward(*args, lse, nv, g, *opts, accumulate=True)
