@@ -32,6 +32,29 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FLCE fwd+bwd tokens/s and % bf16 MFMA peak at N=8192,H=4096,V=128256"
+
+
+def metric_for(w):
+    """The metric string of a workload: the headline's wording at its own shape
+    (fp16 and fp32 inputs say so)."""
+    m = f"FLCE fwd+bwd tokens/s and % bf16 MFMA peak at N={w.N},H={w.H},V={w.V}"
+    if w.dtype == "f16":
+        m += " (fp16 inputs; fp16 MFMA peak = bf16's)"
+    elif w.dtype == "f32":
+        m = f"FLCE fwd+bwd tokens/s and % fp32 MFMA peak at N={w.N},H={w.H},V={w.V}"
+    return m
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (fp16 the same)
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
 
@@ -181,6 +204,7 @@ def cpu_baseline(inp, rows):
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"first {rows} of {w.N} tokens, full V={w.V} and H={w.H}, fp64 forward+backward "
                       f"(logits computed twice), {dt:.2f} s"}
 
@@ -328,20 +352,27 @@ def main():
     fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
     bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
     fwd_med, bwd_med = fwd_ms[len(fwd_ms) // 2], bwd_ms[len(bwd_ms) // 2]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    fwd_avg, bwd_avg = sum(fwd_ms) / len(fwd_ms), sum(bwd_ms) / len(bwd_ms)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = N * args.steps / elapsed
     flops = 8.0 * N * H * V
     peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    fwd_tflops = 2.0 * N * H * V / (fwd_avg * 1e-3) / 1e12
     extra = fwd_bytes + bwd_bytes + N * 4 + 8
     loss_v = loss.sum().item() if loss.numel() > 1 else loss.item()   # reduction none: report the sum
     print(f"[bench] loss {loss_v:.6f}; fwd {fwd_med:.3f} ms, bwd {bwd_med:.3f} ms (median)",
           file=sys.stderr, flush=True)
 
+    kernels = kernel_times(F, w, (x, W, b, tg, g), (dx, dW, db), ws_f, ws_b, fwd_avg, bwd_avg, peak,
+                           max(3, args.steps // 2))
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dominant]
+    print(f"[bench] per kernel: " + ", ".join(f"{k} {v['avg_us']:.1f} us x {v['launches_per_step']} "
+                                              f"({100 * v['frac']:.1f}%)" for k, v in kernels.items()),
+          file=sys.stderr, flush=True)
+
     out = {
-        "metric": METRIC,
+        "metric": METRIC if name == synth.BENCH_WORKLOAD else metric_for(w),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -363,11 +394,11 @@ def main():
         "extra_hbm_mb": extra / 1e6,
         "extra_hbm_frac_of_fp32_logits": extra / (N * V * 4.0),
         "extra_hbm_measured_mb": extra_measured / 1e6,
-        "roofline": {"kernel": "fwd_lse_kernel", "bound": "mfma", "achieved": fwd_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": fwd_tflops / peak,
-                     "traffic": recorded_traffic("fwd_lse_kernel", name),
-                     "note": "2NHV flops per launch / average duration of the forward call "
-                             "(HIP events on the launch stream; the call adds two O(N) kernels)"},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": kd["tflops"], "peak": peak,
+                     "unit": "TFLOP/s", "frac": kd["frac"], "traffic": recorded_traffic(dominant, name),
+                     "avg_launch_us": kd["avg_us"], "flops_per_launch": kd["flops_per_launch"],
+                     "note": kd["method"]},
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         del x, W, b, dx, dW, db, ws_f, ws_b
@@ -376,6 +407,66 @@ def main():
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, rows)
     print(json.dumps(out), flush=True)
+
+
+def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, reps):
+    """Average launch duration of each of the four GEMM kernels, from HIP events
+    recorded on the launch stream around public calls that isolate them.
+
+    fwd_lse_kernel: the forward call (one launch, plus two O(N) kernels of a
+    few microseconds).  The backward runs, per vocabulary slab, the recompute
+    (bwd_dz_kernel), the dx product and the dW product; a backward asked for
+    dx only runs the recompute and dx, one asked for dW only the recompute and
+    dW, and one asked for db only (with a bias) the recompute and a small
+    column-sum kernel.  So, per slab: bwd_dz = the db-only call (with a bias)
+    or dx-only + dW-only - full (without); bwd_dx = full - dW-only; bwd_dw =
+    full - dx-only.  Each call also runs the O(N) coefficient kernel."""
+    import torch
+    from lm_head_cross_flce_amd import _lib
+
+    x, W, b, tg, g = inputs
+    dx, dW, db = outs
+    N, H, V = w.N, w.H, w.V
+    code = {"bf16": _lib.FLCE_BF16, "f16": _lib.FLCE_F16, "f32": _lib.FLCE_F32}[w.dtype]
+    nslab = -(-V // _lib.flce_backward_slab_cols(N, H, V, code))
+    stream = torch.cuda.current_stream()
+    loss, lse, nv = F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                                   workspace=ws_f)
+
+    def timed(out):
+        def call():
+            F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                            w.reduction, workspace=ws_b, out=out)
+        call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
+    t_dx = timed((dx, None, None))
+    t_dw = timed((None, dW, None))
+    if b is not None:
+        t_dz, how = timed((None, None, db)), "db-only backward call / slabs"
+    else:
+        t_dz, how = t_dx + t_dw - bwd_avg_ms, "(dx-only + dW-only - full backward call) / slabs"
+    per_slab = 2.0 * N * H * V / nslab
+    rows = {
+        "fwd_lse_kernel": (fwd_avg_ms, 1, 2.0 * N * H * V, "forward call (one launch) / 1"),
+        "bwd_dz_kernel": (t_dz / nslab, nslab, per_slab, how),
+        "bwd_dx_kernel": ((bwd_avg_ms - t_dw) / nslab, nslab, per_slab, "(full - dW-only backward call) / slabs"),
+        "bwd_dw_kernel": ((bwd_avg_ms - t_dx) / nslab, nslab, per_slab, "(full - dx-only backward call) / slabs"),
+    }
+    out = {}
+    for k, (ms, n, fl, method) in rows.items():
+        tf = fl / (ms * 1e-3) / 1e12
+        out[k] = {"avg_us": ms * 1e3, "launches_per_step": n, "ms_per_step": ms * n, "flops_per_launch": fl,
+                  "tflops": tf, "frac": tf / peak,
+                  "method": "flops per launch / average launch duration from HIP events on the launch "
+                            f"stream: {method}"}
+    return out
 
 
 if __name__ == "__main__":

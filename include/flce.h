@@ -33,11 +33,18 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    allocates nothing and never synchronises the host.  Work is enqueued on
- *    `stream` (a hipStream_t; NULL means the default stream) and completes
- *    asynchronously in stream order.
+ *    `stream` (NULL means the default stream) and completes asynchronously in
+ *    stream order.
  *  - Tensors are dense and row-major: x [N, H] and W [V, H] with H contiguous,
  *    b [V], targets [N] int64.  x, W and b share one dtype (flce_dtype).
- *  - Pointers must be 16-byte aligned; H must be a multiple of 8.
+ *  - x, W, dx, dW and the workspaces must be 16-byte aligned, targets and
+ *    n_valid 8-byte, every float32 buffer 4-byte and b, db element-aligned;
+ *    H must be a multiple of 8 (FLCE_ERR_UNSUPPORTED otherwise).  Both
+ *    follow from the kernels' copies, which move 16 bytes (8 bf16/fp16
+ *    elements) of a row at a time; the pages set no such limit.  Callers
+ *    with other H pad x and W with zero columns up to a multiple of 8 (the
+ *    logits, the loss and dx's first H columns are unchanged) or use the
+ *    PyTorch binding, which does so.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    failed validation returns an error code and enqueues nothing.
  *  - Targets outside [0, V) that are not ignore_index are a precondition
@@ -52,6 +59,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h>   /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -95,25 +104,32 @@ typedef enum {
  * of its 256 CUs), each slab's columns are split into P <= 8 parts, each with
  * its own fp32 [N, H] accumulator (P x N x H x 4 bytes, at most about 64 MB).
  */
-flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias,
-                                int reduction, size_t* fwd_bytes, size_t* bwd_bytes);
+flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
+                                flce_reduction reduction, size_t* fwd_bytes, size_t* bwd_bytes);
 /* (The figures also cover the _ex entry points.) */
 
 /*
- * Forward: writes
+ * Forward (the logits product with an online log-sum-exp epilogue, then the
+ * loss and its reduction): writes
  *   loss    float32, [1] for sum/mean, [N] for none
  *   lse     float32 [N]   (kept by the caller for flce_backward)
  *   n_valid int64 [1]     T, the non-ignored count (kept for flce_backward)
  * b may be NULL (no bias).  eps = label_smoothing in [0, 1]; s = z_loss_scale
  * >= 0; reduction is a flce_reduction.  workspace must hold at least
  * *fwd_bytes from flce_workspace_size for the same arguments.
+ * Passages: fla fused_linear_cross_entropy.py, the forward driver (the
+ * F.linear logits; total = the non-ignored count) and cross_entropy_kernel
+ * (lse - z_y with the label-smoothing blend, the ignore_index early exit);
+ * Liger-Kernel PR 239 "Details" (lse from the running max m and
+ * d = sum exp(z - m); the z-loss s lse^2 added to the CE); DeepSpeed PR 8792
+ * "What" (per-token statistics in forward, reduction none).
  */
 flce_status flce_forward(const void* x, const void* W, const void* b, const int64_t* targets,
-                         int64_t N, int64_t H, int64_t V, int dtype,
+                         int64_t N, int64_t H, int64_t V, flce_dtype dtype,
                          float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                         int reduction,
+                         flce_reduction reduction,
                          float* loss, float* lse, int64_t* n_valid,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward: given the forward's lse and n_valid and the upstream gradient
@@ -123,14 +139,19 @@ flce_status flce_forward(const void* x, const void* W, const void* b, const int6
  *   db [V]     (may be NULL: no bias, or not needed; ignored when b is NULL)
  * in the input dtype.  The other arguments must equal the forward's.
  * workspace must hold at least *bwd_bytes from flce_workspace_size.
+ * Passages: Liger-Kernel PR 239 "Details" (the total gradient of the
+ * smoothed CE plus z-loss with respect to the logits, dz above); fla forward
+ * driver (dx = dz W, dW = dz^T x, db = the column sums of dz, the 1/total
+ * scaling of mean); DeepSpeed PR 8792 "What" and "Memory and time" (logits
+ * recomputed block by block in backward; dx summed in fp32 and cast once).
  */
 flce_status flce_backward(const void* x, const void* W, const void* b, const int64_t* targets,
-                          int64_t N, int64_t H, int64_t V, int dtype,
+                          int64_t N, int64_t H, int64_t V, flce_dtype dtype,
                           float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                          int reduction, const float* lse, const int64_t* n_valid,
+                          flce_reduction reduction, const float* lse, const int64_t* n_valid,
                           const float* grad_loss,
                           void* dx, void* dW, void* db,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Options of the _ex entry points (a NULL options pointer means the
@@ -156,19 +177,19 @@ typedef struct flce_options {
 } flce_options;
 
 flce_status flce_forward_ex(const void* x, const void* W, const void* b, const int64_t* targets,
-                            int64_t N, int64_t H, int64_t V, int dtype,
+                            int64_t N, int64_t H, int64_t V, flce_dtype dtype,
                             float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                            int reduction, const flce_options* opts,
+                            flce_reduction reduction, const flce_options* opts,
                             float* loss, float* lse, int64_t* n_valid,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 flce_status flce_backward_ex(const void* x, const void* W, const void* b, const int64_t* targets,
-                             int64_t N, int64_t H, int64_t V, int dtype,
+                             int64_t N, int64_t H, int64_t V, flce_dtype dtype,
                              float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                             int reduction, const flce_options* opts,
+                             flce_reduction reduction, const flce_options* opts,
                              const float* lse, const int64_t* n_valid, const float* grad_loss,
                              void* dx, void* dW, void* db,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Vocabulary shards.  DeepSpeed PR 8792 ("What"; "Memory and time") splits W's
@@ -186,7 +207,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
  * (*fwd_bytes), flce_shard_merge (*merge_bytes) and flce_shard_backward
  * (*bwd_bytes); pure host arithmetic; outputs may be NULL.
  */
-flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int dtype, int has_bias,
+flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, flce_dtype dtype, int has_bias,
                                       size_t* fwd_bytes, size_t* merge_bytes, size_t* bwd_bytes);
 
 /*
@@ -198,8 +219,8 @@ flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int
  */
 flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
                                int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
-                               int dtype, float label_smoothing, int64_t ignore_index, float* stats,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               flce_dtype dtype, float label_smoothing, int64_t ignore_index, float* stats,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Merge of num_shards shards' statistics, stacked as float32
@@ -211,8 +232,8 @@ flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b
  */
 flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64_t* targets, int64_t N,
                              int64_t V_total, float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                             int reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             flce_reduction reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Shard backward: with the merged lse and n_valid, overwrites
@@ -225,17 +246,17 @@ flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64
  */
 flce_status flce_shard_backward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
                                 int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
-                                int dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                                int reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
+                                flce_dtype dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                flce_reduction reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
                                 float* dx_partial, int accumulate_dx, void* dW_shard, void* db_shard,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
-const char* flce_status_string(int status);
+const char* flce_status_string(flce_status status);
 
 /* Vocabulary slab width (columns of dlogits held at once) the backward uses
  * for this problem; pure host arithmetic.  Returns 0 on invalid arguments. */
-int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, int dtype);
+int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, flce_dtype dtype);
 
 #ifdef __cplusplus
 }

@@ -188,3 +188,4 @@ def flce_backward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_s
                                    ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
                                    lse, n_valid, grad_loss, dx or None, dW or None, db or None, workspace,
                                    workspace_bytes, stream or None), "flce_backward_ex")
+

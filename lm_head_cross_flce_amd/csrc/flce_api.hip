@@ -192,11 +192,52 @@ flce_options default_options() {
   return o;
 }
 
+// Host-side checks of a forward call (no HIP call).
+flce_status check_forward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                          int64_t H, int64_t V, int dtype, float eps, float s, int reduction, const flce_options& o,
+                          const float* loss, const float* lse, const int64_t* n_valid) {
+  if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (o.z_loss && !aligned(o.z_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if ((st = check_options(eps, s, reduction)) != FLCE_OK) return st;
+  if ((st = check_inputs(x, W, b, targets, dtype)) != FLCE_OK) return st;
+  if (!loss || !lse || !n_valid || !aligned(loss, 4) || !aligned(lse, 4) || !aligned(n_valid, 8))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+// The forward's launches, with its per-phase partials and per-row losses in
+// ws (g.fwd_total bytes, laid out by geometry()).
+flce_status forward_into(const Geometry& g, const void* x, const void* W, const void* b, const int64_t* targets,
+                         int64_t N, int64_t H, int64_t V, int dtype, float eps, float s, int64_t ignore_index,
+                         int reduction, const flce_options& o, float* loss, float* lse, int64_t* n_valid, char* ws,
+                         hipStream_t stream) {
+  flce::FwdLaunch a{};
+  a.x = x; a.W = W; a.b = b; a.targets = targets;
+  a.N = (int)N; a.H = (int)H; a.V = (int)V;
+  a.NT = g.NT; a.P = g.P; a.VT = g.VT;
+  a.ignore_index = ignore_index;
+  a.eps = eps;
+  a.eps_over_v = (float)((double)eps / (double)V);
+  a.s = s;
+  a.reduction = reduction;
+  a.logit_scale = o.logit_scale;
+  a.partials = ws + g.off_partials;
+  a.rowloss = (float*)(ws + g.off_rowloss);
+  a.rowzl = (float*)(ws + g.off_rowzl);
+  a.zloss = o.z_loss;
+  a.loss = loss; a.lse = lse; a.n_valid = n_valid;
+  (void)hipGetLastError();
+  if (flce::launch_forward(a, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* flce_status_string(int status) {
+const char* flce_status_string(flce_status status) {
   switch (status) {
     case FLCE_OK: return "ok";
     case FLCE_ERR_INVALID_ARGUMENT: return "invalid argument";
@@ -207,12 +248,12 @@ const char* flce_status_string(int status) {
   }
 }
 
-int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
+int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, flce_dtype dtype) {
   if (check_shape(N, H, V, dtype) != FLCE_OK) return 0;
   return slab_cols(N, H, V, dtype);
 }
 
-flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, int reduction,
+flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias, flce_reduction reduction,
                                 size_t* fwd_bytes, size_t* bwd_bytes) {
   flce_status st = check_shape(N, H, V, dtype);
   if (st != FLCE_OK) return st;
@@ -225,65 +266,42 @@ flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, int 
 }
 
 flce_status flce_forward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
-                         int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
-                         int64_t ignore_index, int reduction, float* loss, float* lse, int64_t* n_valid,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                         int64_t ignore_index, flce_reduction reduction, float* loss, float* lse, int64_t* n_valid,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return flce_forward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
                          nullptr, loss, lse, n_valid, workspace, workspace_bytes, stream);
 }
 
 flce_status flce_forward_ex(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
-                            int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
-                            int64_t ignore_index, int reduction, const flce_options* opts, float* loss, float* lse,
-                            int64_t* n_valid, void* workspace, size_t workspace_bytes, void* stream) {
+                            int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                            int64_t ignore_index, flce_reduction reduction, const flce_options* opts, float* loss, float* lse,
+                            int64_t* n_valid, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const flce_options o = opts ? *opts : default_options();
-  if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (o.z_loss && !aligned(o.z_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
-  flce_status st = check_shape(N, H, V, dtype);
+  flce_status st = check_forward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, reduction, o,
+                                 loss, lse, n_valid);
   if (st != FLCE_OK) return st;
-  if ((st = check_options(label_smoothing, z_loss_scale, reduction)) != FLCE_OK) return st;
-  if ((st = check_inputs(x, W, b, targets, dtype)) != FLCE_OK) return st;
-  if (!loss || !lse || !n_valid || !aligned(loss, 4) || !aligned(lse, 4) || !aligned(n_valid, 8))
-    return FLCE_ERR_INVALID_ARGUMENT;
   const Geometry g = geometry(N, H, V, dtype, b != nullptr);
   if (workspace_bytes < g.fwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
-
-  char* ws = (char*)workspace;
-  flce::FwdLaunch a{};
-  a.x = x; a.W = W; a.b = b; a.targets = targets;
-  a.N = (int)N; a.H = (int)H; a.V = (int)V;
-  a.NT = g.NT; a.P = g.P; a.VT = g.VT;
-  a.ignore_index = ignore_index;
-  a.eps = label_smoothing;
-  a.eps_over_v = (float)((double)label_smoothing / (double)V);
-  a.s = z_loss_scale;
-  a.reduction = reduction;
-  a.logit_scale = o.logit_scale;
-  a.partials = ws + g.off_partials;
-  a.rowloss = (float*)(ws + g.off_rowloss);
-  a.rowzl = (float*)(ws + g.off_rowzl);
-  a.zloss = o.z_loss;
-  a.loss = loss; a.lse = lse; a.n_valid = n_valid;
-  (void)hipGetLastError();
-  if (flce::launch_forward(a, dtype, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
-  return FLCE_OK;
+  return forward_into(g, x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
+                      o, loss, lse, n_valid, (char*)workspace, (hipStream_t)stream);
 }
 
 flce_status flce_backward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
-                          int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
-                          int64_t ignore_index, int reduction, const float* lse, const int64_t* n_valid,
+                          int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                          int64_t ignore_index, flce_reduction reduction, const float* lse, const int64_t* n_valid,
                           const float* grad_loss, void* dx, void* dW, void* db, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, hipStream_t stream) {
   return flce_backward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
                           nullptr, lse, n_valid, grad_loss, dx, dW, db, workspace, workspace_bytes, stream);
 }
 
 flce_status flce_backward_ex(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
-                             int64_t H, int64_t V, int dtype, float label_smoothing, float z_loss_scale,
-                             int64_t ignore_index, int reduction, const flce_options* opts, const float* lse,
+                             int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                             int64_t ignore_index, flce_reduction reduction, const flce_options* opts, const float* lse,
                              const int64_t* n_valid, const float* grad_loss, void* dx, void* dW, void* db,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const flce_options o = opts ? *opts : default_options();
   if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status st = check_shape(N, H, V, dtype);
@@ -326,7 +344,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream);
 }
 
-flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int dtype, int has_bias,
+flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, flce_dtype dtype, int has_bias,
                                       size_t* fwd_bytes, size_t* merge_bytes, size_t* bwd_bytes) {
   flce_status st = check_shape(N, H, V_shard, dtype);
   if (st != FLCE_OK) return st;
@@ -339,8 +357,8 @@ flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, int
 
 flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
                                int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
-                               int dtype, float label_smoothing, int64_t ignore_index, float* stats,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               flce_dtype dtype, float label_smoothing, int64_t ignore_index, float* stats,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   flce_status st = check_shape(N, H, V_shard, dtype);
   if (st != FLCE_OK) return st;
   if ((st = check_shard(V_shard, vocab_start, V_total)) != FLCE_OK) return st;
@@ -369,8 +387,8 @@ flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b
 
 flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64_t* targets, int64_t N,
                              int64_t V_total, float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                             int reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             flce_reduction reduction, float* loss, float* lse, int64_t* n_valid, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   if (N < 1 || N > (int64_t(1) << 30) || V_total < 1 || V_total > (int64_t(1) << 30)) return FLCE_ERR_INVALID_ARGUMENT;
   if (num_shards < 1 || num_shards > (int64_t(1) << 20)) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status st = check_options(label_smoothing, z_loss_scale, reduction);
@@ -401,10 +419,10 @@ flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64
 
 flce_status flce_shard_backward(const void* x, const void* W_shard, const void* b_shard, const int64_t* targets,
                                 int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
-                                int dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
-                                int reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
+                                flce_dtype dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                flce_reduction reduction, const float* lse, const int64_t* n_valid, const float* grad_loss,
                                 float* dx_partial, int accumulate_dx, void* dW_shard, void* db_shard,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   flce_status st = check_shape(N, H, V_shard, dtype);
   if (st != FLCE_OK) return st;
   if ((st = check_shard(V_shard, vocab_start, V_total)) != FLCE_OK) return st;

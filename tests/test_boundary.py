@@ -269,3 +269,4 @@ def test_ex_entry_points_validate_options(lib):
                                P2, 1 << 30, None) == 1
     assert lib.flce_backward_ex(P, P, None, P, 64, 12, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(ok), P2, P2, P2,
                                 P2, P2, None, P2, 1 << 30, None) == 2
+
