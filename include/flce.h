@@ -71,7 +71,9 @@ typedef enum {
   FLCE_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, misalignment, eps/s out of range */
   FLCE_ERR_UNSUPPORTED = 2,      /* dtype or shape the library does not handle (e.g. H % 8 != 0) */
   FLCE_ERR_WORKSPACE_TOO_SMALL = 3,
-  FLCE_ERR_HIP = 4               /* a HIP launch failed; see hipGetLastError on the caller side */
+  FLCE_ERR_HIP = 4,              /* a HIP launch failed; see hipGetLastError on the caller side */
+  FLCE_ERR_SCRATCH_TOO_SMALL = 5 /* flce_forward_noalloc: the problem needs more than
+                                    FLCE_FORWARD_SCRATCH_BYTES of forward scratch */
 } flce_status;
 
 typedef enum {
@@ -190,6 +192,29 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
                              const float* lse, const int64_t* n_valid, const float* grad_loss,
                              void* dx, void* dW, void* db,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * flce_forward_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The forward's per-phase partials and
+ * per-row losses live in a static device array of FLCE_FORWARD_SCRATCH_BYTES
+ * that each GPU holds (at its own address) from the library's first use on
+ * it until the process ends; nothing is allocated or freed.  The problem must
+ * fit: *fwd_bytes of flce_workspace_size <= FLCE_FORWARD_SCRATCH_BYTES (about
+ * N <= 120k tokens at 8 vocabulary phases; N = 8192 needs 1.1 MB), else
+ * FLCE_ERR_SCRATCH_TOO_SMALL with nothing enqueued.  `stream` must belong to
+ * the current device (FLCE_ERR_INVALID_ARGUMENT otherwise); the first call
+ * on a device looks up its array's address with that device current.  Every
+ * call on one GPU shares that GPU's array: calls whose work overlaps on one
+ * GPU (different streams, or threads) race and must be ordered by the caller.
+ * Results are identical to flce_forward_ex's for the same arguments.
+ */
+#define FLCE_FORWARD_SCRATCH_BYTES ((size_t)16 << 20)
+flce_status flce_forward_noalloc(const void* x, const void* W, const void* b, const int64_t* targets,
+                                 int64_t N, int64_t H, int64_t V, flce_dtype dtype,
+                                 float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                 flce_reduction reduction, const flce_options* opts,
+                                 float* loss, float* lse, int64_t* n_valid, hipStream_t stream);
 
 /*
  * Vocabulary shards.  DeepSpeed PR 8792 ("What"; "Memory and time") splits W's

@@ -17,6 +17,10 @@ FLCE_ERR_INVALID_ARGUMENT = 1
 FLCE_ERR_UNSUPPORTED = 2
 FLCE_ERR_WORKSPACE_TOO_SMALL = 3
 FLCE_ERR_HIP = 4
+FLCE_ERR_SCRATCH_TOO_SMALL = 5
+
+# Bytes of the static device scratch of flce_forward_noalloc (FLCE_FORWARD_SCRATCH_BYTES).
+FORWARD_SCRATCH_BYTES = 16 << 20
 
 FLCE_F32 = 0
 FLCE_BF16 = 1
@@ -26,7 +30,7 @@ REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 
 # Every symbol the public header declares.
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex", "flce_backward_ex",
-           "flce_status_string",
+           "flce_forward_noalloc", "flce_status_string",
            "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
            "flce_shard_backward")
 
@@ -73,6 +77,9 @@ def load() -> ctypes.CDLL:
         lib.flce_backward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
                                          vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flce_backward_ex.restype = c_int
+        lib.flce_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                             vp, vp, vp, vp]
+        lib.flce_forward_noalloc.restype = c_int
         lib.flce_status_string.argtypes = [c_int]
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
@@ -189,3 +196,10 @@ def flce_backward_ex(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_s
                                    lse, n_valid, grad_loss, dx or None, dW or None, db or None, workspace,
                                    workspace_bytes, stream or None), "flce_backward_ex")
 
+
+def flce_forward_noalloc(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                         reduction, opts, loss, lse, n_valid, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_forward_noalloc(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                       ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
+                                       loss, lse, n_valid, stream or None), "flce_forward_noalloc")

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 
 #include "flce.h"
@@ -16,6 +17,7 @@ constexpr int kTile = 256;
 constexpr size_t kAlign = 256;
 constexpr size_t kSlabCapBytes = size_t(1) << 30;
 constexpr size_t kSlabTargetBytes = size_t(256) << 20;
+constexpr size_t kScratchBytes = FLCE_FORWARD_SCRATCH_BYTES;   // flce_forward_noalloc's static scratch
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -233,6 +235,42 @@ flce_status forward_into(const Geometry& g, const void* x, const void* W, const 
   return FLCE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static forward scratch (flce_forward_noalloc).  Each GPU holds its own copy
+// of this array at its own address for the life of the process; host code
+// uses only the address hipGetSymbolAddress returns for a device (the array's
+// name on the host is a stand-in, not a device address).  The address is
+// looked up once per device, with that device current, and cached.  The
+// forward writes every byte it later reads (each phase's partials for every
+// token, each row's loss), so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array of the device that `stream` belongs to, which must be the
+// current device (the symbol lookup is made with that device current).
+flce_status scratch_on_stream_device(hipStream_t stream, char** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur < 0 || cur >= kMaxDevices) return FLCE_ERR_HIP;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return FLCE_ERR_HIP;
+    if (sd != cur) return FLCE_ERR_INVALID_ARGUMENT;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FLCE_ERR_HIP;
+    g_scratch_ptr[cur] = (char*)p;
+  }
+  *out = g_scratch_ptr[cur];
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,6 +282,7 @@ const char* flce_status_string(flce_status status) {
     case FLCE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FLCE_ERR_HIP: return "HIP launch failed";
+    case FLCE_ERR_SCRATCH_TOO_SMALL: return "problem needs more forward scratch than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -286,6 +325,22 @@ flce_status flce_forward_ex(const void* x, const void* W, const void* b, const i
   if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
   return forward_into(g, x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
                       o, loss, lse, n_valid, (char*)workspace, (hipStream_t)stream);
+}
+
+flce_status flce_forward_noalloc(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                                 int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                                 int64_t ignore_index, flce_reduction reduction, const flce_options* opts, float* loss,
+                                 float* lse, int64_t* n_valid, hipStream_t stream) {
+  const flce_options o = opts ? *opts : default_options();
+  flce_status st = check_forward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, reduction, o,
+                                 loss, lse, n_valid);
+  if (st != FLCE_OK) return st;
+  const Geometry g = geometry(N, H, V, dtype, b != nullptr);
+  if (g.fwd_total > kScratchBytes) return FLCE_ERR_SCRATCH_TOO_SMALL;
+  char* ws = nullptr;
+  if ((st = scratch_on_stream_device((hipStream_t)stream, &ws)) != FLCE_OK) return st;
+  return forward_into(g, x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction,
+                      o, loss, lse, n_valid, ws, (hipStream_t)stream);
 }
 
 flce_status flce_backward(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert _lib.status_string(0) == "ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert _lib.status_string(s) not in ("ok", "unknown status")
     assert _lib.status_string(99) == "unknown status"
 
@@ -270,3 +270,50 @@ def test_ex_entry_points_validate_options(lib):
     assert lib.flce_backward_ex(P, P, None, P, 64, 12, 1000, 0, 0.0, 0.0, -100, 2, ctypes.byref(ok), P2, P2, P2,
                                 P2, P2, None, P2, 1 << 30, None) == 2
 
+
+def _fna(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100,
+                red=2, opts=None, loss=P2, lse=P2, nv=P2, stream=None)
+    args.update(over)
+    return lib.flce_forward_noalloc(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"],
+                                    args["V"], args["dtype"], args["eps"], args["s"], args["ign"], args["red"],
+                                    args["opts"], args["loss"], args["lse"], args["nv"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=12), 2), (dict(dtype=7), 2), (dict(eps=1.5), 1), (dict(s=-1.0), 1),
+    (dict(red=3), 1), (dict(x=None), 1), (dict(W=P + 2), 1), (dict(targets=P + 4), 1), (dict(loss=None), 1),
+    (dict(nv=P2 + 4), 1),
+    # 8 phases x 2^20 tokens x 16 bytes of partials = 128 MiB: more than the static scratch
+    (dict(N=1 << 20, V=4000), 5),
+])
+def test_noalloc_forward_validation(lib, over, code):
+    # every case fails on the host, before the scratch address is looked up
+    assert _fna(lib, **over) == code
+
+
+def test_noalloc_forward_rejects_bad_options(lib):
+    bad = _lib.options(logit_scale=float("inf"))
+    assert _fna(lib, opts=ctypes.byref(bad)) == 1
+    misaligned = _lib.options(z_loss=P2 + 2)
+    assert _fna(lib, opts=ctypes.byref(misaligned)) == 1
+
+
+def test_noalloc_scratch_bound(lib):
+    # The header's constant is the binding's; every workload's forward fits,
+    # and the first token count past the bound is rejected on the host.
+    m = re.search(r"#define FLCE_FORWARD_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.FORWARD_SCRATCH_BYTES
+    for N, H, V in ((64, 128, 1000), (4096, 2048, 32000), (8192, 4096, 128256), (32768, 2048, 128000),
+                    (16384, 1024, 256000)):
+        f, _ = _lib.flce_workspace_size(N, H, V, _lib.FLCE_BF16, True, 2)
+        assert f <= _lib.FORWARD_SCRATCH_BYTES
+    lo, hi = 8192, 1 << 20
+    fits = lambda n: _lib.flce_workspace_size(n, 128, 4000, _lib.FLCE_BF16, False, 2)[0] <= \
+        _lib.FORWARD_SCRATCH_BYTES
+    assert fits(lo) and not fits(hi)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if fits(mid) else (lo, mid)
+    assert _fna(lib, N=hi, V=4000, dtype=1) == _lib.FLCE_ERR_SCRATCH_TOO_SMALL
+    assert 100_000 < lo < 130_000
