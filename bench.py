@@ -128,17 +128,20 @@ def _kernel_rows(d):
 
 
 def summarize_trace(d):
+    """Per kernel: launches, average duration, and the warm average that leaves
+    out each kernel's first launch (cold caches and clocks)."""
     rows = _kernel_rows(d)
     agg = {}
     for name, dur in rows:
         key = name.split("(")[0].replace("void ", "")
-        n, t = agg.get(key, (0, 0))
-        agg[key] = (n + 1, t + dur)
-    total = sum(t for _, t in agg.values())
-    print("| kernel | calls | avg us | total ms | share |")
-    print("|---|---:|---:|---:|---:|")
-    for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
-        print(f"| `{k}` | {n} | {t / n / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.1f}% |")
+        agg.setdefault(key, []).append(dur)
+    total = sum(sum(v) for v in agg.values())
+    print("| kernel | calls | avg us | warm avg us | total ms | share |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        t, n = sum(v), len(v)
+        warm = (t - v[0]) / (n - 1) if n > 1 else t
+        print(f"| `{k}` | {n} | {t / n / 1e3:.1f} | {warm / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.1f}% |")
 
 
 def summarize_alloc(d):
