@@ -73,6 +73,12 @@ def parse():
     p.add_argument("--summarize-alloc", default=None, metavar="DIR")
     p.add_argument("--shards", type=int, default=0, metavar="P",
                    help="time the vocabulary-shard entry points: W split into P shards run one after another")
+    p.add_argument("--schedule", choices=("recompute", "fused"), default="recompute",
+                   help="recompute: flce_forward + flce_backward (the headline); fused: the gradients formed "
+                        "in the forward pass (flce_fused_forward_backward)")
+    p.add_argument("--chunk", type=int, default=0, help="fused schedule: tokens per chunk (0: equal memory)")
+    p.add_argument("--no-fused-line", action="store_true",
+                   help="leave the fused schedule's comparison out of the recompute line")
     return p.parse_args()
 
 
@@ -323,6 +329,25 @@ def main():
     if args.shards > 0:
         shard_bench(args, w, x, W, b, tg, g, name)
         return
+    if args.schedule == "fused":
+        del ws_f, ws_b
+        torch.cuda.empty_cache()
+        r = fused_bench(F, w, (x, W, b, tg, g), (dx, dW, db), args.chunk, args.warmup, args.steps)
+        peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
+        ms = r["ms_per_step"]
+        print(json.dumps({
+            "metric": (METRIC if name == synth.BENCH_WORKLOAD else metric_for(w)) + ", fused schedule",
+            "value": N * 1e3 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic (seeded SplitMix64 draws, random-init weights)",
+            "config": {"workload": name, "N": N, "H": H, "V": V, "schedule": "fused", "chunk": r["chunk"]},
+            "tflops_8nhv": 8.0 * N * H * V / (ms * 1e-3) / 1e12,
+            "mfma_frac_8nhv": 8.0 * N * H * V / (ms * 1e-3) / 1e12 / peak,
+            "tflops_6nhv": 6.0 * N * H * V / (ms * 1e-3) / 1e12,
+            "extra_hbm_mb": r["extra_hbm_mb"], "extra_hbm_frac_of_fp32_logits": r["extra_hbm_mb"] * 1e6 / (N * V * 4.0),
+            "loss": r["loss"],
+        }), flush=True)
+        return
 
     def step(ev=None):
         if ev is not None:
@@ -403,13 +428,54 @@ def main():
                      "note": kd["method"]},
         "kernels": kernels,
     }
+    if not args.no_fused_line:
+        del ws_f, ws_b
+        torch.cuda.empty_cache()
+        r = fused_bench(F, w, (x, W, b, tg, g), (dx, dW, db), 0, 1, max(3, args.steps // 2))
+        r["mfma_frac_8nhv"] = 8.0 * N * H * V / (r["ms_per_step"] * 1e-3) / 1e12 / peak
+        out["fused_schedule"] = r
+        print(f"[bench] fused schedule: {r['ms_per_step']:.3f} ms per step, chunk {r['chunk']}, "
+              f"{r['extra_hbm_mb']:.1f} MB", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        del x, W, b, dx, dW, db, ws_f, ws_b
+        del x, W, b, dx, dW, db
+        ws_f = ws_b = None
         torch.cuda.empty_cache()
         rows = args.cpu_rows or max(8, min(N, int(1.0e13 // (8.0 * H * V))))
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, rows)
     print(json.dumps(out), flush=True)
+
+
+def fused_bench(F, w, inputs, outs, chunk, warmup, steps):
+    """The fused schedule (gradients formed in the forward pass) on the same
+    inputs and outputs: ms per step from HIP events on the launch stream, the
+    chunk, and its extra memory (workspace plus loss, lse and count)."""
+    import torch
+
+    x, W, b, tg, g = inputs
+    N, H, V = w.N, w.H, w.V
+    nbytes, used = F.flce_fused_workspace_size(N, H, V, x.dtype, b is not None, chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+
+    def step():
+        return F.flce_fused_forward_backward(x, W, b, tg, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                             w.reduction, chunk_tokens=chunk, workspace=ws, out=outs)[0]
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        loss = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del ws
+    return {"ms_per_step": ms, "chunk": used, "extra_hbm_mb": (nbytes + N * 4 + 8) / 1e6,
+            "loss": loss.sum().item() if loss.numel() > 1 else loss.item(),
+            "method": "flce_fused_forward_backward, HIP events on the launch stream over the timed steps"}
 
 
 def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, reps):

@@ -194,6 +194,45 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Fused schedule: loss and gradients in one pass, the gradients formed while
+ * the forward runs, as fla's fused_linear_cross_entropy_forward and
+ * Liger-Kernel commit 95b01e9 ("Summary"; the production-defaults table)
+ * compute them.  Tokens are taken chunk_tokens at a time.  Each chunk's
+ * logits are formed once: the logits product, then dx = dz W and
+ * dW += dz^T x (three products, 6NHV flops, against four for
+ * flce_forward + flce_backward).  Between the logits product and the
+ * dlogits the chunk's logits are kept as e = exp(z - m_h) in the input
+ * dtype, m_h (fp32) being the token's max over each half of a 256-row
+ * vocabulary tile: e lies in (0, 1], so 16 bits keep a relative error of at
+ * most 2^-9 however large the logits.  grad_loss must be known before the
+ * pass (float32, [1] for sum/mean, [N] for none); a caller that learns it
+ * later passes 1 and scales the gradients, which are linear in it.  dW is
+ * accumulated over the chunks in its own dtype, as the pages' schedule adds
+ * each chunk into grad_weight: one rounding per chunk, where the recompute
+ * schedule rounds once.  db is summed in fp32 over all chunks and rounded
+ * once.
+ *
+ * Writes loss, lse and n_valid as flce_forward does and dx, dW, db (each may
+ * be NULL) as flce_backward does; opts as for the _ex entry points.
+ * chunk_tokens is a multiple of 256, or 0 for the default: the fewest chunks
+ * whose workspace fits in what flce_forward plus flce_backward take for the
+ * same problem (the two schedules then use equal extra memory), balanced.
+ * flce_fused_workspace_size gives the workspace bytes (*bytes) and the chunk
+ * used (*chunk_used); pure host arithmetic, either output may be NULL.
+ */
+flce_status flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
+                                      int64_t chunk_tokens, int64_t* chunk_used, size_t* bytes);
+
+flce_status flce_fused_forward_backward(const void* x, const void* W, const void* b, const int64_t* targets,
+                                        int64_t N, int64_t H, int64_t V, flce_dtype dtype,
+                                        float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                                        flce_reduction reduction, const flce_options* opts,
+                                        const float* grad_loss, int64_t chunk_tokens,
+                                        float* loss, float* lse, int64_t* n_valid,
+                                        void* dx, void* dW, void* db,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * flce_forward_ex without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  The forward's per-phase partials and

@@ -30,7 +30,8 @@ REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 
 # Every symbol the public header declares.
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex", "flce_backward_ex",
-           "flce_forward_noalloc", "flce_status_string",
+           "flce_forward_noalloc", "flce_fused_workspace_size", "flce_fused_forward_backward",
+           "flce_status_string",
            "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
            "flce_shard_backward")
 
@@ -80,6 +81,12 @@ def load() -> ctypes.CDLL:
         lib.flce_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
                                              vp, vp, vp, vp]
         lib.flce_forward_noalloc.restype = c_int
+        lib.flce_fused_workspace_size.argtypes = [i64, i64, i64, c_int, c_int, i64, ctypes.POINTER(i64),
+                                                  ctypes.POINTER(sz)]
+        lib.flce_fused_workspace_size.restype = c_int
+        lib.flce_fused_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                                    vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flce_fused_forward_backward.restype = c_int
         lib.flce_status_string.argtypes = [c_int]
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
@@ -203,3 +210,23 @@ def flce_forward_noalloc(x, W, b, targets, N, H, V, dtype, label_smoothing, z_lo
     _check(load().flce_forward_noalloc(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
                                        ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
                                        loss, lse, n_valid, stream or None), "flce_forward_noalloc")
+
+
+def flce_fused_workspace_size(N: int, H: int, V: int, dtype: int, has_bias: bool, chunk_tokens: int = 0):
+    """(workspace bytes, chunk used) of the fused schedule."""
+    c, b = ctypes.c_int64(0), ctypes.c_size_t(0)
+    _check(load().flce_fused_workspace_size(N, H, V, dtype, int(bool(has_bias)), chunk_tokens, ctypes.byref(c),
+                                            ctypes.byref(b)), "flce_fused_workspace_size")
+    return b.value, c.value
+
+
+def flce_fused_forward_backward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                                reduction, opts, grad_loss, chunk_tokens, loss, lse, n_valid, dx, dW, db,
+                                workspace, workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_fused_forward_backward(x, W, b or None, targets, N, H, V, dtype, label_smoothing,
+                                              z_loss_scale, ignore_index, reduction,
+                                              ctypes.byref(opts) if opts is not None else None, grad_loss,
+                                              chunk_tokens, loss, lse, n_valid, dx or None, dW or None, db or None,
+                                              workspace, workspace_bytes, stream or None),
+           "flce_fused_forward_backward")

@@ -86,6 +86,15 @@ int dx_split(int64_t N, int64_t H, int64_t slab_cols) {
   return p < 2 ? 1 : (int)p;
 }
 
+// Forward phases for NT token tiles: enough that the grid (token tiles x
+// phases) fills the CUs, and at least 8 (see geometry), at most VT.
+int fwd_phases(int NT, int VT) {
+  int P = kCUs / NT;
+  if (P < 8) P = 8;
+  if (P > VT) P = VT;
+  return P;
+}
+
 // with_dx_acc: the backward keeps its own fp32 dx accumulator (the shard
 // backward accumulates into the caller's buffer instead).
 Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true) {
@@ -99,9 +108,7 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   // would stream 18) and take x's copies first.  Past 256 workgroups the grid
   // runs in rounds.  N=32768, H=2048, V=128000: 8 phases instead of 2, forward
   // -3.7% (same-box A/B).
-  int P = kCUs / g.NT;
-  if (P < 8) P = 8;
-  if (P > g.VT) P = g.VT;
+  const int P = fwd_phases(g.NT, g.VT);
   g.P = P;
   size_t off = 0;
   g.off_partials = off;
@@ -129,6 +136,83 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   if (dtype == FLCE_F16) off = align_up(off + 8);
   g.bwd_total = off;
   return g;
+}
+
+// Fused schedule (gradients formed in the forward pass, one token chunk at a
+// time).  Workspace: the chunk's kept logits [chunk][VT * 256] in the input
+// dtype (turned into dlogits in place), their per-(token, tile, half) maxima,
+// the chunk forward's per-phase partials, per-row losses of all N tokens,
+// per-token coefficients, the dx product's K-split accumulators, and db's
+// per-256-token column sums and fp32 running total.  Sized for the largest
+// chunk and for the shorter last chunk, whichever needs more.
+struct FusedGeometry {
+  int64_t chunk;
+  int VT;
+  int64_t lde;
+  size_t off_partials, off_rowloss, off_rowzl, off_e, off_mref, off_coef, off_yv, off_dxacc, off_dbp, off_dbacc,
+      off_gscale, total;
+};
+
+FusedGeometry fused_geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, int64_t chunk) {
+  FusedGeometry g{};
+  const int64_t es = dtype == FLCE_F32 ? 4 : 2;
+  g.chunk = chunk < N ? chunk : N;
+  g.VT = (int)cdiv(V, kTile);
+  g.lde = (int64_t)g.VT * kTile;
+  const int64_t nchunks = cdiv(N, g.chunk);
+  const int64_t sizes[2] = {g.chunk, N - (nchunks - 1) * g.chunk};
+  size_t part = 0, dxacc = 0;
+  for (int64_t c : sizes) {
+    const int NTc = (int)cdiv(c, kTile);
+    const size_t p = (size_t)fwd_phases(NTc, g.VT) * c * 16;
+    const int split = dx_split(c, H, g.lde);
+    const size_t a = split > 1 ? (size_t)split * c * H * 4 : 0;
+    if (p > part) part = p;
+    if (a > dxacc) dxacc = a;
+  }
+  size_t off = 0;
+  g.off_partials = off;
+  off = align_up(off + part);
+  g.off_rowloss = off;
+  off = align_up(off + (size_t)N * 4);
+  g.off_rowzl = off;
+  off = align_up(off + (size_t)N * 4);
+  g.off_e = off;
+  off = align_up(off + (size_t)g.chunk * g.lde * es);
+  g.off_mref = off;
+  off = align_up(off + (size_t)g.chunk * g.VT * 2 * 4);
+  g.off_coef = off;
+  off = align_up(off + (size_t)g.chunk * 16);
+  g.off_yv = off;
+  off = align_up(off + (size_t)g.chunk * 4);
+  g.off_dxacc = off;
+  off = align_up(off + dxacc);
+  g.off_dbp = off;
+  if (has_bias) off = align_up(off + (size_t)cdiv(g.chunk, kTile) * g.lde * 4);
+  g.off_dbacc = off;
+  if (has_bias) off = align_up(off + (size_t)V * 4);
+  g.off_gscale = off;
+  if (dtype == FLCE_F16) off = align_up(off + 8);
+  g.total = off;
+  return g;
+}
+
+// Default chunk: the fewest chunks whose workspace fits in what the recompute
+// schedule uses for the same problem (forward plus backward workspace: the
+// two schedules then compare at equal extra memory), then balanced, in
+// multiples of 256 tokens.  At least 256 tokens.
+int64_t fused_default_chunk(int64_t N, int64_t H, int64_t V, int dtype, int has_bias) {
+  const Geometry r = geometry(N, H, V, dtype, has_bias);
+  const size_t budget = r.fwd_total + r.bwd_total;
+  int64_t best = kTile;
+  for (int64_t c = cdiv(N, kTile) * kTile; c >= kTile; c -= kTile) {
+    if (fused_geometry(N, H, V, dtype, has_bias, c).total <= budget) {
+      best = c;
+      break;
+    }
+  }
+  const int64_t nchunks = cdiv(N, best);
+  return cdiv(cdiv(N, nchunks), kTile) * kTile;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -397,6 +481,127 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
 
   return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream);
+}
+
+flce_status flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
+                                      int64_t chunk_tokens, int64_t* chunk_used, size_t* bytes) {
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if (chunk_tokens < 0 || chunk_tokens % kTile != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  const int64_t chunk = chunk_tokens ? chunk_tokens : fused_default_chunk(N, H, V, dtype, has_bias);
+  const FusedGeometry g = fused_geometry(N, H, V, dtype, has_bias, chunk);
+  if (chunk_used) *chunk_used = g.chunk;
+  if (bytes) *bytes = g.total;
+  return FLCE_OK;
+}
+
+flce_status flce_fused_forward_backward(const void* x, const void* W, const void* b, const int64_t* targets,
+                                        int64_t N, int64_t H, int64_t V, flce_dtype dtype, float label_smoothing,
+                                        float z_loss_scale, int64_t ignore_index, flce_reduction reduction,
+                                        const flce_options* opts, const float* grad_loss, int64_t chunk_tokens,
+                                        float* loss, float* lse, int64_t* n_valid, void* dx, void* dW, void* db,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const flce_options o = opts ? *opts : default_options();
+  flce_status st = check_forward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, reduction, o,
+                                 loss, lse, n_valid);
+  if (st != FLCE_OK) return st;
+  if (!grad_loss || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((dx && !aligned(dx, 16)) || (dW && !aligned(dW, 16))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (db && !aligned(db, dtype == FLCE_F32 ? 4 : 2)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (chunk_tokens < 0 || chunk_tokens % kTile != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  const int64_t chunk = chunk_tokens ? chunk_tokens : fused_default_chunk(N, H, V, dtype, b != nullptr);
+  const FusedGeometry g = fused_geometry(N, H, V, dtype, b != nullptr, chunk);
+  if (workspace_bytes < g.total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  const bool want_db = b != nullptr && db != nullptr;
+  const bool grads = dx || dW || want_db;
+  const int64_t es = dtype == FLCE_F32 ? 4 : 2;
+  const bool none = reduction == FLCE_REDUCTION_NONE;
+  char* ws = (char*)workspace;
+  float* gscale = dtype == FLCE_F16 ? (float*)(ws + g.off_gscale) : nullptr;
+
+  flce::FwdLaunch base{};
+  base.W = W; base.b = b;
+  base.H = (int)H; base.V = (int)V; base.VT = g.VT;
+  base.ignore_index = ignore_index;
+  base.eps = label_smoothing;
+  base.eps_over_v = (float)((double)label_smoothing / (double)V);
+  base.s = z_loss_scale;
+  base.reduction = reduction;
+  base.logit_scale = o.logit_scale;
+  base.n_valid = n_valid;
+  (void)hipGetLastError();
+  // The mean's count is needed by the first chunk's dlogits.
+  flce::FwdLaunch cnt = base;
+  cnt.targets = targets;
+  cnt.N = (int)N;
+  if (grads && flce::launch_fused_count(cnt, stream) != hipSuccess) return FLCE_ERR_HIP;
+  for (int64_t c0 = 0; c0 < N; c0 += g.chunk) {
+    const int nc = (int)((N - c0) < g.chunk ? (N - c0) : g.chunk);
+    const int NTc = (int)cdiv(nc, kTile);
+    const bool first = c0 == 0, last = c0 + nc >= N;
+    flce::FwdLaunch fa = base;
+    fa.x = (const char*)x + c0 * H * es;
+    fa.targets = targets + c0;
+    fa.N = nc;
+    fa.NT = NTc;
+    fa.P = fwd_phases(NTc, g.VT);
+    fa.partials = ws + g.off_partials;
+    fa.rowloss = (float*)(ws + g.off_rowloss) + c0;
+    fa.rowzl = (float*)(ws + g.off_rowzl) + c0;
+    fa.zloss = o.z_loss ? (none ? o.z_loss + c0 : o.z_loss) : nullptr;
+    fa.loss = none ? loss + c0 : loss;
+    fa.lse = lse + c0;
+    fa.ebuf = ws + g.off_e;
+    fa.lde = g.lde;
+    fa.mref = (float*)(ws + g.off_mref);
+    if (flce::launch_fused_forward(fa, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
+    if (!grads) continue;
+    flce::BwdLaunch ba{};
+    ba.x = fa.x; ba.W = W; ba.b = b; ba.targets = targets + c0;
+    ba.N = nc; ba.H = (int)H; ba.V = (int)V; ba.NT = NTc;
+    ba.ignore_index = ignore_index;
+    ba.eps = label_smoothing;
+    ba.eps_over_v = base.eps_over_v;
+    ba.s = z_loss_scale;
+    ba.logit_scale = o.logit_scale;
+    ba.reduction = reduction;
+    ba.accumulate = o.accumulate != 0;
+    ba.lse = lse + c0; ba.n_valid = n_valid;
+    ba.grad = none ? grad_loss + c0 : grad_loss;
+    ba.coef = ws + g.off_coef;
+    ba.yv = (int*)(ws + g.off_yv);
+    ba.slab = ws + g.off_e;
+    ba.ldS = g.lde;
+    ba.dx_acc = (float*)(ws + g.off_dxacc);
+    ba.dx_split = dx_split(nc, H, g.lde);
+    ba.gscale = gscale;
+    ba.dx = dx ? (char*)dx + c0 * H * es : nullptr;
+    ba.dW = dW;
+    ba.db = nullptr;
+    if (flce::launch_bwd_prepare(ba, stream) != hipSuccess) return FLCE_ERR_HIP;
+    flce::FusedDz fd{};
+    fd.ebuf = ws + g.off_e; fd.lde = g.lde;
+    fd.mref = (const float*)(ws + g.off_mref);
+    fd.coef = ba.coef; fd.yv = ba.yv;
+    fd.N = nc; fd.V = (int)V; fd.VT = g.VT;
+    fd.dbp = want_db ? (float*)(ws + g.off_dbp) : nullptr;
+    fd.gscale = gscale;
+    if (flce::launch_fused_dz(fd, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
+    if (want_db && flce::launch_fused_db(fd.dbp, NTc, g.lde, (float*)(ws + g.off_dbacc), (int)V, first, last, db,
+                                         dtype, o.accumulate != 0, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+    if ((dx || dW) && flce::launch_fused_products(ba, dtype, first, stream) != hipSuccess) return FLCE_ERR_HIP;
+  }
+  flce::FwdLaunch fin = base;
+  fin.targets = targets;
+  fin.N = (int)N;
+  fin.rowloss = (float*)(ws + g.off_rowloss);
+  fin.rowzl = (float*)(ws + g.off_rowzl);
+  fin.zloss = o.z_loss;
+  fin.loss = loss;
+  if (flce::launch_finalize(fin, stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
 }
 
 flce_status flce_shard_workspace_size(int64_t N, int64_t H, int64_t V_shard, flce_dtype dtype, int has_bias,

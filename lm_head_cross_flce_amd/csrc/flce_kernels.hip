@@ -889,4 +889,452 @@ hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int
 }
 
 
+// ---------------------------------------------------------------------------
+// Fused schedule: the gradients are formed during the forward pass, one token
+// chunk at a time, as fla's fused_linear_cross_entropy_forward does (logits of
+// a chunk, its dlogits, dx = dz W and dW += dz^T x; three products, 6NHV
+// flops, instead of the recompute schedule's four).  Each chunk's logits are
+// kept between its forward product and its dlogits pass.
+// ---------------------------------------------------------------------------
+
+// Stores per wave and chunk tile: 32 pieces of kept e values (16-bit
+// inputs) and 8 of m_h.
+constexpr int kFusedStoresVm = 40;
+
+// One tile of the chunk forward: the logits product, then an epilogue that
+// (pass 1) takes each token's max m_h over the 128 rows this wave holds,
+// (pass 2) keeps e = exp(z - m_h) for every row, in T, and folds the tile
+// into the running (m, d), sum z and z_y exactly as the forward does
+// (d gains sum e exp(m_h - m')).  e lies in (0, 1], so a 16-bit copy has a
+// relative error of at most 2^-9 however large the logits (a 16-bit copy of z
+// itself would put |z| 2^-9 into the exponent).  16-bit tiles copy W with
+// permuted rows (tile_row_perm), so a lane's values in blocks 2s and 2s + 1
+// of a token column are eight consecutive vocabulary rows: one 16-byte store.
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, int EXTRA>
+__device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n0, TileCopy<true, true>& tc,
+                                               const Lds& L, const int (&ycol)[8], float (&m)[8], float (&d)[8],
+                                               float (&sz)[8], float (&zy)[8], __amdgpu_buffer_rsrc_t re,
+                                               __amdgpu_buffer_rsrc_t rm, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
+  const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
+  const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
+  const int v0 = vt * kTile;
+  BiasTile<T> bt;
+  if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
+  Acc acc;
+  if constexpr (sizeof(T) == 2) {
+    gemm_tile_bf16_run<true, true, EXTRA, XFIRST>(acc, A, B, a.H, L, tid, tc);
+    if (vt + a.P < a.VT) tc.start(A, v0 + a.P * kTile, B, n0, L, tid, true);
+  } else {
+    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
+  }
+  if (BIAS) {
+    bt.publish(L.bias, tid, a.logit_scale);
+    lds_barrier();
+  }
+  acc_drain();
+  const int rw = wm * kWaveTile;
+  const int vleft = a.V - v0;          // rows of this tile inside the vocabulary
+  const bool ragged = vleft < kTile;   // the vocabulary's last tile (wave-uniform)
+  const float sc = a.logit_scale;
+  auto logit = [&](float v, float bv, int row) -> float {
+    const float z = fmaf(v, sc, bv);
+    return (!ragged || row < vleft) ? z : -INFINITY;
+  };
+  // Pass 1: m_h of each token column.
+  float mh[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mh[j] = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r0 = rw + dz_row<T>(2 * s, g), r1 = rw + dz_row<T>(2 * s + 1, g);
+    const f32x4 b0 = BIAS ? read_bias4(L.bias, r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 b1 = BIAS ? read_bias4(L.bias, r1) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 z0 = acc_read4(acc[2 * s][j]);
+      const f32x4 z1 = acc_read4(acc[2 * s + 1][j]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mh[j] = fmaxf(mh[j], logit(z0[r], b0[r], r0 + r));
+        mh[j] = fmaxf(mh[j], logit(z1[r], b1[r], r1 + r));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one column at a time keeps few values live
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mh[j] = fmaxf(mh[j], __shfl_xor(mh[j], 16));
+    mh[j] = fmaxf(mh[j], __shfl_xor(mh[j], 32));
+  }
+  // m_h of token column j: lanes of group 0 store it (the other lanes' stores
+  // are dropped by an out-of-range offset, so every wave issues all 8).
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int nl = wn * kWaveTile + 16 * j + (lane & 15);
+    const uint32_t off =
+        (g == 0 && n0 + nl < a.N) ? (uint32_t)(((int64_t)nl * 2 * a.VT + 2 * vt + wm) * 4) : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mh[j]), rm, off, 0, 0);
+  }
+  // Pass 2: kept values, sums and the target logit.
+  float se[8], zs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    se[j] = 0.f;
+    zs[j] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r0 = rw + dz_row<T>(2 * s, g), r1 = rw + dz_row<T>(2 * s + 1, g);
+    const f32x4 b0 = BIAS ? read_bias4(L.bias, r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 b1 = BIAS ? read_bias4(L.bias, r1) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int nl = wn * kWaveTile + 16 * j + (lane & 15);
+      const f32x4 z0 = acc_read4(acc[2 * s][j]);
+      const f32x4 z1 = acc_read4(acc[2 * s + 1][j]);
+      float z[8], e[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[r] = logit(z0[r], b0[r], r0 + r);
+        z[4 + r] = logit(z1[r], b1[r], r1 + r);
+      }
+      const float nml = -mh[j] * kLog2e;
+      const bool live = !ragged || mh[j] != -INFINITY;   // a half tile wholly past V keeps zeros
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        e[k] = live ? fast_exp2(fmaf(z[k], kLog2e, nml)) : 0.f;
+        se[j] += e[k];
+        if (SMOOTH) zs[j] += (!ragged || z[k] != -INFINITY) ? z[k] : 0.f;
+      }
+      // Target logit by selects: a branch here (as in the other epilogues)
+      // makes the compiler keep this pass's values live across it and spill.
+      const int t0 = ycol[j] - (v0 + r0), t1 = ycol[j] - (v0 + r1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        zy[j] = t0 == r ? z[r] : zy[j];
+        zy[j] = t1 == r ? z[4 + r] : zy[j];
+      }
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t off = n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.lde + v0 + r0) * 2) : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7])}, re,
+            off, 0, 0);
+      } else {
+        const bool ok = n0 + nl < a.N;
+        const uint32_t o0 = ok ? (uint32_t)(((int64_t)nl * a.lde + v0 + r0) * 4) : kOOB;
+        const uint32_t o1 = ok ? (uint32_t)(((int64_t)nl * a.lde + v0 + r1) * 4) : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{e[0], e[1], e[2], e[3]}), re, o0,
+                                               0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{e[4], e[5], e[6], e[7]}), re, o1,
+                                               0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float mn = fmaxf(m[j], mh[j]);
+    if (!ragged || mn != -INFINITY) {
+      d[j] = d[j] * fast_exp2((m[j] - mn) * kLog2e) + se[j] * fast_exp2((mh[j] - mn) * kLog2e);
+      m[j] = mn;
+    }
+    if (SMOOTH) sz[j] += zs[j];
+  }
+}
+
+// Chunk forward: the forward kernel's schedule (persistent over token tile and
+// vocabulary phase, one workgroup per CU) with fused_fwd_tile's epilogue;
+// writes the same per-phase partials, which fwd_combine_kernel merges.
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST>
+__global__ void __launch_bounds__(kThreads, 1) fused_fwd_kernel(FwdLaunch a) {
+  FLCE_LDS(L, T);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int w = blockIdx.x;
+  int nt, ph;
+  if ((a.NT & 7) == 0) {
+    const int slot = w >> 3;
+    ph = slot % a.P;
+    nt = (w & 7) * (a.NT >> 3) + slot / a.P;
+  } else {
+    ph = w % a.P;
+    nt = w / a.P;
+  }
+  const int n0 = nt * kTile;
+  int ycol[8];
+  float m[8], d[8], sz[8], zy[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = n0 + wn * kWaveTile + 16 * j + (lane & 15);
+    const int64_t t = n < a.N ? a.targets[n] : a.ignore_index;
+    ycol[j] = (t == a.ignore_index || t < 0 || t >= a.V) ? -1 : (int)t;
+    m[j] = -INFINITY;
+    d[j] = 0.f;
+    sz[j] = 0.f;
+    zy[j] = 0.f;
+  }
+  // Descriptors start at the tile's first token, so offsets stay below 2^31.
+  const __amdgpu_buffer_rsrc_t re = make_rsrc((const T*)a.ebuf + (int64_t)n0 * a.lde);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.mref + (int64_t)n0 * 2 * a.VT);
+  TileCopy<true, true> tc;
+  if constexpr (sizeof(T) == 2) {
+    const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
+    const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
+    if (ph < a.VT) tc.start(A, ph * kTile, B, n0, L, tid, true);
+  }
+  int vt = ph;
+  // The first tile is peeled: later tiles start with the previous tile's
+  // kept-value stores still in flight (counted in the mainloop's first wait).
+  if (vt < a.VT) {
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, BIAS ? 1 : 0>(a, vt, n0, tc, L, ycol, m, d, sz, zy, re, rm, tid);
+    vt += a.P;
+  }
+  for (; vt < a.VT; vt += a.P)
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, (BIAS ? 1 : 0) + kFusedStoresVm>(a, vt, n0, tc, L, ycol, m, d, sz, zy,
+                                                                             re, rm, tid);
+  // Merge the four lanes of a token, then the two waves, as the forward does.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float m2 = __shfl_xor(m[j], mask), d2 = __shfl_xor(d[j], mask);
+      const float s2 = __shfl_xor(sz[j], mask), y2 = __shfl_xor(zy[j], mask);
+      merge_md(m[j], d[j], m2, d2);
+      sz[j] += s2;
+      zy[j] += y2;
+    }
+  }
+  lds_f32x4* red = (lds_f32x4*)L.a[0];
+  __syncthreads();   // every wave's last LDS read of the final tile is done
+  if (wm == 1 && lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[wn * kWaveTile + 16 * j + lane] = f32x4{m[j], d[j], sz[j], zy[j]};
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 16) {
+    f32x4* part = (f32x4*)a.partials;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 o = red[wn * kWaveTile + 16 * j + lane];
+      merge_md(m[j], d[j], o[0], o[1]);
+      const int n = n0 + wn * kWaveTile + 16 * j + lane;
+      if (n < a.N) part[(int64_t)ph * a.N + n] = f32x4{m[j], d[j], sz[j] + o[2], zy[j] + o[3]};
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) fused_count_kernel(FwdLaunch a) {
+  __shared__ long long scnt[1024];
+  const int tid = threadIdx.x;
+  long long c = 0;
+  for (int n = tid; n < a.N; n += 1024) c += (a.targets[n] != a.ignore_index) ? 1 : 0;
+  scnt[tid] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) scnt[tid] += scnt[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) a.n_valid[0] = scnt[0];
+}
+
+// Dlogits of a chunk, in place over the kept values:
+//   dz = c (1 + 2 s lse) e exp(m_h - lse) - c eps / V - c (1 - eps) [j = y]
+// (Liger-Kernel PR 239's total gradient, with p = e exp(m_h - lse)), zero
+// past V, stored in T, and with DB the fp32 column sums of dz over each block
+// of 256 tokens.  For fp16 the coefficients carry the slab scale S (as in the
+// recompute schedule), so the stored values are dz S and the column sums are
+// multiplied by 1/S (exact: a power of two).  Thread t of block (bx, by) takes the 8
+// columns 2048 bx + 8 t .. + 7 (one half tile: one m_h per token) of tokens
+// 256 by .. 256 by + 255, eight rows at a time.
+template <class T, bool DB>
+__global__ void __launch_bounds__(256) fused_dz_kernel(FusedDz f) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= f.VT * kTile) return;   // no barriers below
+  const int vt = c >> 8, h = (c >> 7) & 1;
+  const int n0 = blockIdx.y * kTile;
+  const int n1 = min(n0 + kTile, f.N);
+  const float inv_s = (IsF16<T>::value && f.gscale) ? f.gscale[1] : 1.f;
+  const f32x4* coef = (const f32x4*)f.coef;
+  float cs[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cs[k] = 0.f;
+  constexpr int kRows = 8;
+  for (int nb = n0; nb < n1; nb += kRows) {
+    float v[kRows][8];
+    float mr[kRows];
+#pragma unroll
+    for (int q = 0; q < kRows; ++q) {
+      const int n = min(nb + q, n1 - 1);   // rows past the block repeat the last (not stored, not summed)
+      const int64_t base = (int64_t)n * f.lde + c;
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 u = *(const u32x4*)((const T*)f.ebuf + base);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[q][2 * k] = h16_to_f32<T>(u[k]);
+          v[q][2 * k + 1] = h16_to_f32<T>(u[k] >> 16);
+        }
+      } else {
+        const f32x4 u0 = *(const f32x4*)((const float*)f.ebuf + base);
+        const f32x4 u1 = *(const f32x4*)((const float*)f.ebuf + base + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[q][k] = u0[k];
+          v[q][4 + k] = u1[k];
+        }
+      }
+      mr[q] = f.mref[(int64_t)n * 2 * f.VT + 2 * vt + h];
+    }
+#pragma unroll
+    for (int q = 0; q < kRows; ++q) {
+      const int n = nb + q;
+      if (n >= n1) break;
+      const f32x4 cf = coef[n];
+      const int y = f.yv[n];
+      const float p_scale = cf[0] * fast_exp2(fmaf(mr[q], kLog2e, -cf[3]));   // c (1 + 2 s lse) e^(m_h - lse)
+      float dz[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float z = fmaf(p_scale, v[q][k], -cf[1]);
+        if (c + k == y) z -= cf[2];
+        z = c + k < f.V ? z : 0.f;
+        if (DB) cs[k] += z;
+        dz[k] = z;
+      }
+      const int64_t base = (int64_t)n * f.lde + c;
+      if constexpr (sizeof(T) == 2) {
+        *(u32x4*)((T*)f.ebuf + base) =
+            u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]), pack2<T>(dz[6], dz[7])};
+      } else {
+        *(f32x4*)((float*)f.ebuf + base) = f32x4{dz[0], dz[1], dz[2], dz[3]};
+        *(f32x4*)((float*)f.ebuf + base + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
+      }
+    }
+  }
+  if (DB) {
+    float* o = f.dbp + (int64_t)blockIdx.y * f.lde + c;
+    *(f32x4*)o = f32x4{cs[0], cs[1], cs[2], cs[3]} * inv_s;
+    *(f32x4*)(o + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]} * inv_s;
+  }
+}
+
+// db over the chunks: dbacc[v] (+)= the chunk's block sums in block order;
+// after the last chunk, db[v] = dbacc[v] (plus db's old value when
+// accumulating), rounded once to T.
+template <class T>
+__global__ void __launch_bounds__(256) fused_db_kernel(const float* dbp, int rows, int64_t lde, float* dbacc, int V,
+                                                       int first, int last, void* db, int accumulate) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  float s = first ? 0.f : dbacc[v];
+  for (int t = 0; t < rows; ++t) s += dbp[(int64_t)t * lde + v];
+  dbacc[v] = s;
+  if (!last) return;
+  if constexpr (sizeof(T) == 4) {
+    float* p = (float*)db + v;
+    *p = accumulate ? *p + s : s;
+  } else {
+    uint16_t* p = (uint16_t*)db + v;
+    if (accumulate) s += h16_to_f32<T>(*p);
+    *p = (uint16_t)(pack2<T>(s, 0.f) & 0xffffu);
+  }
+}
+
+hipError_t launch_fused_count(const FwdLaunch& a, hipStream_t st) {
+  hipLaunchKernelGGL(fused_count_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class T, bool XFIRST>
+static void launch_fused_fwd_order(const FwdLaunch& a, hipStream_t st) {
+  const int G = a.NT * a.P;
+  const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
+  if (bias && smooth) hipLaunchKernelGGL((fused_fwd_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) hipLaunchKernelGGL((fused_fwd_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) hipLaunchKernelGGL((fused_fwd_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((fused_fwd_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+}
+
+template <class T>
+static hipError_t launch_fused_forward_t(const FwdLaunch& a, hipStream_t st) {
+  if (sizeof(T) == 2 && a.P >= 4) launch_fused_fwd_order<T, true>(a, st);
+  else launch_fused_fwd_order<T, false>(a, st);
+  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
+  if (dtype == 1) return launch_fused_forward_t<uint16_t>(a, st);
+  if (dtype == 2) return launch_fused_forward_t<_Float16>(a, st);
+  return launch_fused_forward_t<float>(a, st);
+}
+
+template <class T>
+static hipError_t launch_fused_dz_t(const FusedDz& f, hipStream_t st) {
+  const dim3 grid((unsigned)((f.VT * kTile + 2047) / 2048), (unsigned)((f.N + kTile - 1) / kTile));
+  if (f.dbp) hipLaunchKernelGGL((fused_dz_kernel<T, true>), grid, dim3(256), 0, st, f);
+  else hipLaunchKernelGGL((fused_dz_kernel<T, false>), grid, dim3(256), 0, st, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_dz(const FusedDz& f, int dtype, hipStream_t st) {
+  if (dtype == 1) return launch_fused_dz_t<uint16_t>(f, st);
+  if (dtype == 2) return launch_fused_dz_t<_Float16>(f, st);
+  return launch_fused_dz_t<float>(f, st);
+}
+
+// The chunk's products: dx rows (K = all V columns of the dlogits, one slab;
+// split along K into a.dx_split parts when its tiles cannot fill the CUs) and
+// dW += dz^T x over the chunk's tokens.
+template <class T>
+static hipError_t launch_fused_products_t(const BwdLaunch& a, bool first, hipStream_t st) {
+  const int width = a.V, wpad = (width + 7) & ~7;
+  const int TV = (width + kTile - 1) / kTile;
+  const int TH = (a.H + kTile - 1) / kTile;
+  const dim3 blk(kThreads);
+  const bool acc = a.accumulate != 0;
+  if (a.dx) {
+    const int parts = a.dx_split > 1 ? a.dx_split : 1;
+    const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
+    const dim3 gdx(TH * a.NT * parts);
+    if (parts > 1) {
+      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+      if (launch_bwd_dx_finalize(a, sizeof(T) == 4 ? 0 : (IsF16<T>::value ? 2 : 1), st) != hipSuccess)
+        return hipGetLastError();
+    } else if (acc) {
+      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+    } else {
+      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+    }
+  }
+  if (a.dW) {
+    if (first && !acc) hipLaunchKernelGGL((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
+    else hipLaunchKernelGGL((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_products(const BwdLaunch& a, int dtype, bool first, hipStream_t st) {
+  if (dtype == 1) return launch_fused_products_t<uint16_t>(a, first, st);
+  if (dtype == 2) return launch_fused_products_t<_Float16>(a, first, st);
+  return launch_fused_products_t<float>(a, first, st);
+}
+
+hipError_t launch_fused_db(const float* dbp, int rows, int64_t lde, float* dbacc, int V, bool first, bool last,
+                           void* db, int dtype, bool accumulate, hipStream_t st) {
+  const dim3 grid((unsigned)((V + 255) / 256)), blk(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL((fused_db_kernel<uint16_t>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((fused_db_kernel<_Float16>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+  else
+    hipLaunchKernelGGL((fused_db_kernel<float>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FwdLaunch& a, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace flce

@@ -26,6 +26,12 @@ struct FwdLaunch {
   float* stats;           // shard forward: float4 [N] {m, d, sum z, z_y} over the shard's rows
   float* zloss;           // optional: the z-loss term alone, [1] or [N] like loss; null if not wanted
   float* rowzl;           // [N] per-row z-loss terms (workspace), used when zloss is set
+  // Fused schedule, chunk forward only: every logit of the chunk is kept as
+  // e = exp(z - m_h) in the input dtype, m_h the max over the token's 128
+  // rows of the tile that one wave holds.
+  void* ebuf;             // [N][lde]
+  int64_t lde;            // row stride of ebuf in elements (VT * 256)
+  float* mref;            // [N][VT][2]: m_h per token, vocabulary tile and half tile
 };
 
 struct BwdLaunch {
@@ -49,6 +55,17 @@ struct BwdLaunch {
   void* dx; void* dW; void* db;
 };
 
+// Fused schedule, one chunk: the kept e values turned into dlogits in place.
+struct FusedDz {
+  void* ebuf; int64_t lde;
+  const float* mref;      // [N][VT][2]
+  const void* coef;       // float4 [N] from bwd_coef_kernel (with the fp16 slab scale)
+  const int* yv;          // [N] target rows, -1 if ignored
+  int N, V, VT;           // the chunk's tokens, vocabulary rows, vocabulary tiles
+  float* dbp;             // [ceil(N / 256)][lde]: fp32 column sums per 256 tokens; null if no db
+  const float* gscale;    // fp16: {S, 1/S}; the coefficients, so the stored dlogits, carry S; null otherwise
+};
+
 // dtype: 0 = fp32, 1 = bf16, 2 = fp16.  Each returns the launch error code.
 hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st);
 // Shard forward: logits statistics of W's rows only, merged over phases into a.stats.
@@ -61,5 +78,23 @@ hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int
 // dx = the sum of the a.dx_split fp32 accumulators (plus dx's old values when
 // a.accumulate), written in dx's dtype.
 hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st);
+
+// Fused schedule (gradients formed in the forward pass, one token chunk at a
+// time).  launch_fused_count: the non-ignored count into a.n_valid before the
+// first chunk.  launch_fused_forward: the chunk's logits tiles, statistics
+// and kept e values, then the per-row lse and loss (a.* point at the chunk's
+// rows).  launch_fused_dz: dlogits in place (and db column sums).
+// launch_fused_products: the chunk's dx rows (K = the whole vocabulary) and
+// its dW contribution, added to dW unless first (or a.accumulate) says to
+// overwrite.  launch_fused_db: db accumulated in fp32 over the chunks
+// (first: overwrite), and, with last, written to db in its dtype (added to
+// it when accumulate).  launch_finalize: the reduced loss over all rows.
+hipError_t launch_fused_count(const FwdLaunch& a, hipStream_t st);
+hipError_t launch_fused_forward(const FwdLaunch& a, int dtype, hipStream_t st);
+hipError_t launch_fused_dz(const FusedDz& f, int dtype, hipStream_t st);
+hipError_t launch_fused_products(const BwdLaunch& a, int dtype, bool first, hipStream_t st);
+hipError_t launch_fused_db(const float* dbp, int rows, int64_t lde, float* dbacc, int V, bool first, bool last,
+                           void* db, int dtype, bool accumulate, hipStream_t st);
+hipError_t launch_finalize(const FwdLaunch& a, hipStream_t st);
 
 }  // namespace flce

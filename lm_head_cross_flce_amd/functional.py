@@ -184,6 +184,63 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
     return dx, dW, db
 
 
+def flce_fused_workspace_size(N: int, H: int, V: int, dtype: torch.dtype, has_bias: bool,
+                              chunk_tokens: int = 0) -> Tuple[int, int]:
+    """(workspace bytes, tokens per chunk) of the fused schedule."""
+    return _lib.flce_fused_workspace_size(N, H, V, _DTYPES[dtype], has_bias, chunk_tokens)
+
+
+def flce_fused_forward_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
+                                grad_loss: torch.Tensor, label_smoothing: float = 0.0, z_loss_scale: float = 0.0,
+                                ignore_index: int = -100, reduction: str = "mean", need_dx: bool = True,
+                                need_dW: bool = True, need_db: bool = True, chunk_tokens: int = 0,
+                                workspace: Optional[torch.Tensor] = None, out: Optional[Tuple] = None,
+                                logit_scale: float = 1.0, accumulate: bool = False,
+                                return_z_loss: bool = False):
+    """The fused schedule: loss and gradients in one pass, the gradients formed
+    while the forward runs (grad_loss must be known up front: [1] for sum/mean,
+    [N] for none).  Returns (loss, lse, n_valid, dx, dW, db) (and z_loss with
+    return_z_loss); gradients are None where not requested."""
+    if x.dim() == 2 and x.shape[1] % 8 != 0:
+        raise ValueError("the fused schedule needs H % 8 == 0; pad x and W with zero columns")
+    x, W, b, targets = _prep(x, W, b, targets)
+    N, H = x.shape
+    V = W.shape[0]
+    dt, red = _dtype_code(x), _reduction_code(reduction)
+    dev = x.device
+    g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
+    if g.numel() != (N if reduction == "none" else 1):
+        raise ValueError("grad_loss must have N entries for none and one otherwise")
+    nbytes, _ = _lib.flce_fused_workspace_size(N, H, V, dt, b is not None, chunk_tokens)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is not None:
+        dx, dW, db = out
+        _check_out(dx, (N, H), x, "out dx")
+        _check_out(dW, (V, H), x, "out dW")
+        _check_out(db, (V,), x, "out db")
+    else:
+        if accumulate:
+            raise ValueError("accumulate needs the out tensors to add to")
+        dx = torch.empty_like(x) if need_dx else None
+        dW = torch.empty_like(W) if need_dW else None
+        db = torch.empty_like(b) if (need_db and b is not None) else None
+    loss = torch.empty(N if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    z_loss = torch.empty_like(loss) if return_z_loss else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.flce_fused_forward_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                                         float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                                         _lib.options(logit_scale, accumulate, _ptr(z_loss)), g.data_ptr(),
+                                         int(chunk_tokens), loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(),
+                                         _ptr(dx), _ptr(dW), _ptr(db), workspace.data_ptr(), workspace.numel(),
+                                         stream)
+    res = (loss, lse, n_valid, dx, dW, db)
+    return res + (z_loss,) if return_z_loss else res
+
+
 def _shard_hidden(x: torch.Tensor) -> None:
     # The shard entry points hand the caller fp32 dx partials of x's width,
     # so they take H as the library does (a multiple of 8) rather than pad.

@@ -317,3 +317,57 @@ def test_noalloc_scratch_bound(lib):
         lo, hi = (mid, hi) if fits(mid) else (lo, mid)
     assert _fna(lib, N=hi, V=4000, dtype=1) == _lib.FLCE_ERR_SCRATCH_TOO_SMALL
     assert 100_000 < lo < 130_000
+
+
+def test_fused_workspace_and_default_chunk(lib):
+    # Default chunk: the fewest chunks whose workspace fits in what the
+    # recompute schedule takes for the same problem (equal extra memory),
+    # balanced in multiples of 256 tokens.
+    for N, H, V, bias in ((8192, 4096, 128256, True), (4096, 2048, 32000, False), (32768, 2048, 128000, True),
+                          (16384, 1024, 256000, False)):
+        f, b = _lib.flce_workspace_size(N, H, V, _lib.FLCE_BF16, bias, 2)
+        fb, chunk = _lib.flce_fused_workspace_size(N, H, V, _lib.FLCE_BF16, bias, 0)
+        assert chunk % 256 == 0 and fb <= f + b
+        # one chunk of 256 more would not fit, or N is covered in fewer chunks
+        nchunks = -(-N // chunk)
+        bigger = -(-N // (nchunks - 1)) if nchunks > 1 else None
+        if bigger is not None:
+            bigger = -(-bigger // 256) * 256
+            assert _lib.flce_fused_workspace_size(N, H, V, _lib.FLCE_BF16, bias, bigger)[0] > f + b
+    assert _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 0)[1] == 1280
+    # explicit chunk: the kept logits [chunk][V rounded up to 256] in bf16 dominate
+    fb, chunk = _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 1024)
+    assert chunk == 1024
+    lde = 501 * 256
+    kept = 1024 * lde * 2
+    maxima = 1024 * 501 * 2 * 4
+    dx_parts = 4 * 1024 * 4096 * 4            # 64 output tiles: the dx product splits K in four
+    assert kept + maxima + dx_parts < fb < kept + maxima + dx_parts + 8 * (1 << 20)
+    # fp16 adds the 256-byte slab-scale slot; fp32 keeps 4-byte values
+    assert _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_F16, True, 1024)[0] == fb + 256
+    assert _lib.flce_fused_workspace_size(64, 128, 1000, _lib.FLCE_F32, True, 256) == \
+        _lib.flce_fused_workspace_size(64, 128, 1000, _lib.FLCE_F32, True, 0)
+    with pytest.raises(_lib.FlceError):
+        _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 100)
+
+
+def _ffb(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100, red=2,
+                opts=None, g=P2, chunk=0, loss=P2, lse=P2, nv=P2, dx=P2, dW=P2, db=None, ws=P2, wsb=1 << 30,
+                stream=None)
+    args.update(over)
+    return lib.flce_fused_forward_backward(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"],
+                                           args["V"], args["dtype"], args["eps"], args["s"], args["ign"],
+                                           args["red"], args["opts"], args["g"], args["chunk"], args["loss"],
+                                           args["lse"], args["nv"], args["dx"], args["dW"], args["db"], args["ws"],
+                                           args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=12), 2), (dict(dtype=5), 2), (dict(eps=1.5), 1), (dict(s=-1.0), 1), (dict(red=4), 1),
+    (dict(g=None), 1), (dict(g=P2 + 2), 1), (dict(chunk=100), 1), (dict(chunk=-256), 1),
+    (dict(x=None), 1), (dict(loss=None), 1), (dict(dx=P2 + 8), 1), (dict(dW=P2 + 4), 1),
+    (dict(wsb=16), 3), (dict(ws=None), 1),
+])
+def test_fused_validation(lib, over, code):
+    assert _ffb(lib, **over) == code
