@@ -66,7 +66,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums have int as their underlying type (C++ states it; C's enums of
+ * these values are int-sized), so a caller may pass any int and the library
+ * reports the values it does not know instead of the call being undefined. */
+#ifdef __cplusplus
+#define FLCE_ENUM(name) enum name : int
+#else
+#define FLCE_ENUM(name) enum name
+#endif
+
+typedef FLCE_ENUM(flce_status) {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARGUMENT = 1, /* bad size, null pointer, misalignment, eps/s out of range */
   FLCE_ERR_UNSUPPORTED = 2,      /* dtype or shape the library does not handle (e.g. H % 8 != 0) */
@@ -76,13 +85,13 @@ typedef enum {
                                     FLCE_FORWARD_SCRATCH_BYTES of forward scratch */
 } flce_status;
 
-typedef enum {
+typedef FLCE_ENUM(flce_reduction) {
   FLCE_REDUCTION_NONE = 0,
   FLCE_REDUCTION_SUM = 1,
   FLCE_REDUCTION_MEAN = 2
 } flce_reduction;
 
-typedef enum {
+typedef FLCE_ENUM(flce_dtype) {
   FLCE_F32 = 0,  /* x, W, b are float32; gradients are float32 */
   FLCE_BF16 = 1, /* x, W, b are bfloat16; gradients are bfloat16 (fp32 accumulation) */
   FLCE_F16 = 2   /* x, W, b are IEEE half; gradients are half (fp32 accumulation).  The dlogits
