@@ -521,9 +521,20 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // A band's row sums are reduced over the lane group as soon as the band is
   // done, so few stay live.
   float dbs[4];
+  const bool ragged = vleft < kTile;   // wave-uniform
+  // Byte offset of each of this lane's token rows in the slab, kOOB past N
+  // (a column offset below 2^31 added to kOOB stays out of range, so stores
+  // past N are dropped without a select).
+  uint32_t rowoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int nl = wn * kWaveTile + 16 * j + (lane & 15);
+    rowoff[j] = n0 + nl < a.N ? (uint32_t)((int64_t)nl * a.ldS * (int64_t)sizeof(T)) : kOOB;
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r0 = wm * kWaveTile + dz_row<T>(2 * s, g), r1 = wm * kWaveTile + dz_row<T>(2 * s + 1, g);
+    const uint32_t coff = (uint32_t)((v0 - vs + r0) * (int)sizeof(T));
     const f32x4 bias0 = BIAS ? read_bias4(L.bias, r0) : f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 bias1 = BIAS ? read_bias4(L.bias, r1) : f32x4{0.f, 0.f, 0.f, 0.f};
     float rs[8];
@@ -539,22 +550,37 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
       float dz[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        dz[r] = fmaf(cf[0], fast_exp2(fmaf(z0[r] + bias0[r], sl2e, -cf[3])), -cf[1]);
-        dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(z1[r] + bias1[r], sl2e, -cf[3])), -cf[1]);
+        // Without a bias the accumulator is the logit (an added zero could
+        // not be folded away: it would turn -0 into +0).
+        const float a0 = BIAS ? z0[r] + bias0[r] : z0[r];
+        const float a1 = BIAS ? z1[r] + bias1[r] : z1[r];
+        dz[r] = fmaf(cf[0], fast_exp2(fmaf(a0, sl2e, -cf[3])), -cf[1]);
+        dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(a1, sl2e, -cf[3])), -cf[1]);
       }
-      const int t0 = y - (v0 + r0), t1 = y - (v0 + r1);
-      if (__ballot((t0 >= 0 && t0 < 4) || (t1 >= 0 && t1 < 4))) {
+      if constexpr (sizeof(T) == 2) {
+        // r1 = r0 + 4: the lane's rows are r0 .. r0 + 7.
+        const int t = y - (v0 + r0);
+        if (__ballot((unsigned)t < 8u)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (t0 == r) dz[r] -= cf[2];
-          if (t1 == r) dz[4 + r] -= cf[2];
+          for (int k = 0; k < 8; ++k)
+            if (t == k) dz[k] -= cf[2];
+        }
+      } else {
+        const int t0 = y - (v0 + r0), t1 = y - (v0 + r1);
+        if (__ballot((unsigned)t0 < 4u || (unsigned)t1 < 4u)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (t0 == r) dz[r] -= cf[2];
+            if (t1 == r) dz[4 + r] -= cf[2];
+          }
         }
       }
-      if (vleft < kTile) {
+      if (ragged) {
+        const int lim0 = vleft - r0, lim1 = vleft - r1;   // rows of each run inside the vocabulary
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (r0 + r >= vleft) dz[r] = 0.f;
-          if (r1 + r >= vleft) dz[4 + r] = 0.f;
+          if (r >= lim0) dz[r] = 0.f;
+          if (r >= lim1) dz[4 + r] = 0.f;
         }
       }
       if (DB) {
@@ -562,10 +588,9 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
         for (int e = 0; e < 8; ++e) rs[e] += dz[e];
       }
       if constexpr (sizeof(T) == 2) {
-        // r1 = r0 + 4: sixteen contiguous bytes; a wave instruction writes 16
-        // tokens x 64 bytes.
-        const uint32_t off =
-            n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.ldS + (v0 - vs) + r0) * 2) : kOOB;
+        // Sixteen contiguous bytes; a wave instruction writes 16 tokens x 64
+        // bytes.
+        const uint32_t off = rowoff[j] + coff;
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]),
                   pack2<T>(dz[6], dz[7])},
