@@ -33,6 +33,13 @@
 
 namespace flce {
 
+// Cache policy of the dlogits slab's stores: sc0 | nt (non-temporal).  The
+// slab is written once and read once, by the two gradient products.  With
+// this policy the backward pass measured 0.5-2% faster at the bf16 workloads;
+// the same policy on the dx accumulator's read-modify-write and on the dx and
+// dW stores measured slower, so those keep the default policy.
+constexpr int kSlabPolicy = 3;
+
 // ---------------------------------------------------------------------------
 // Epilogue helpers.  Accumulator layout (Acc): element r of block (i, j) in
 // lane l is row 16 i + 4 g + r and column 16 j + l % 16 of the wave tile,
@@ -594,7 +601,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]),
                   pack2<T>(dz[6], dz[7])},
-            rslab, off, 0, 0);
+            rslab, off, 0, kSlabPolicy);
       } else {
         if (n0 + nl < a.N) {
           T* row = (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs);
