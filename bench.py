@@ -7,11 +7,14 @@
     python bench.py --summarize-alloc DIR       # device allocations from a --memory-allocation-trace run
     python bench.py --shards P                  # the vocabulary-shard path: P shards in sequence
 
-A step is one pass of the whole hot path over one batch: flce_forward (logits
-GEMM with the online log-sum-exp epilogue, combine, reduction) then
-flce_backward (per vocabulary slab: logits recompute into dlogits, dW, dx; db)
-with inputs, outputs and workspaces already resident in HBM.  Prints one JSON
-line.  Inputs are seeded synthetic data with the workload's shapes and
+A step is one pass of the whole hot path over one batch: flce_forward_keep
+(logits GEMM with the online log-sum-exp epilogue, combine, reduction; the
+first vocabulary slab's logits kept) then flce_backward_kept (that slab's
+dlogits from the kept values; per other slab the logits recompute into
+dlogits; per slab dx and dW; db), with inputs, outputs, workspaces and the
+kept buffer already resident in HBM.  --schedule recompute times
+flce_forward + flce_backward (every slab recomputed) instead.  Prints one
+JSON line.  Inputs are seeded synthetic data with the workload's shapes and
 distributions (random weights; no dataset).
 """
 
@@ -73,8 +76,10 @@ def parse():
     p.add_argument("--summarize-alloc", default=None, metavar="DIR")
     p.add_argument("--shards", type=int, default=0, metavar="P",
                    help="time the vocabulary-shard entry points: W split into P shards run one after another")
-    p.add_argument("--schedule", choices=("recompute", "fused"), default="recompute",
-                   help="recompute: flce_forward + flce_backward (the headline); fused: the gradients formed "
+    p.add_argument("--schedule", choices=("keep", "recompute", "fused"), default="keep",
+                   help="keep: flce_forward_keep + flce_backward_kept (the recompute schedule with the first "
+                        "vocabulary slab's logits kept from the forward; the headline); recompute: "
+                        "flce_forward + flce_backward (every slab recomputed); fused: the gradients formed "
                         "in the forward pass (flce_fused_forward_backward)")
     p.add_argument("--chunk", type=int, default=0, help="fused schedule: tokens per chunk (0: equal memory)")
     p.add_argument("--no-fused-line", action="store_true",
@@ -322,9 +327,14 @@ def main():
     N, H, V = w.N, w.H, w.V
     torch.cuda.synchronize()
     mem_inputs = torch.cuda.memory_allocated(dev)   # x, W, b, targets, upstream grad
-    fwd_bytes, bwd_bytes = F.flce_workspace_size(N, H, V, tdt, b is not None, w.reduction)
+    keep_mode = args.schedule == "keep"
+    if keep_mode:
+        fwd_bytes, keep_bytes, bwd_bytes = F.flce_keep_workspace_size(N, H, V, tdt, b is not None, w.reduction)
+    else:
+        (fwd_bytes, bwd_bytes), keep_bytes = F.flce_workspace_size(N, H, V, tdt, b is not None, w.reduction), 0
     ws_f = torch.empty(fwd_bytes, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bwd_bytes, dtype=torch.uint8, device=dev)
+    kbuf = torch.empty(keep_bytes, dtype=torch.uint8, device=dev) if keep_mode else None
     dx, dW = torch.empty_like(x), torch.empty_like(W)
     db = torch.empty_like(b) if b is not None else None
     stream = torch.cuda.current_stream(dev)
@@ -355,12 +365,20 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        loss, lse, nv = F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                                       w.reduction, workspace=ws_f)
+        if keep_mode:
+            loss, lse, nv, _ = F.flce_forward_keep(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                                   w.reduction, workspace=ws_f, keep=kbuf)
+        else:
+            loss, lse, nv = F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                           w.reduction, workspace=ws_f)
         if ev is not None:
             ev[1].record(stream)
-        F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                        w.reduction, workspace=ws_b, out=(dx, dW, db))
+        if keep_mode:
+            F.flce_backward_kept(x, W, b, tg, lse, nv, g, kbuf, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                 w.reduction, workspace=ws_b, out=(dx, dW, db))
+        else:
+            F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                            w.reduction, workspace=ws_b, out=(dx, dW, db))
         if ev is not None:
             ev[2].record(stream)
         return loss
@@ -389,7 +407,7 @@ def main():
     flops = 8.0 * N * H * V
     peak = PEAK_BF16_TFLOPS if w.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    extra = fwd_bytes + bwd_bytes + N * 4 + 8
+    extra = fwd_bytes + keep_bytes + bwd_bytes + N * 4 + 8
     loss_v = loss.sum().item() if loss.numel() > 1 else loss.item()   # reduction none: report the sum
     print(f"[bench] loss {loss_v:.6f}; fwd {fwd_med:.3f} ms, bwd {bwd_med:.3f} ms (median)",
           file=sys.stderr, flush=True)
@@ -401,8 +419,11 @@ def main():
                                       "method": "flops per launch / average launch duration from HIP events on "
                                                 "the launch stream: forward call (one launch) / 1"}}
     else:
-        kernels = kernel_times(F, w, (x, W, b, tg, g), (dx, dW, db), ws_f, ws_b, fwd_avg, bwd_avg, peak,
-                               max(3, args.steps // 2))
+        del ws_b, kbuf
+        ws_b = kbuf = None
+        torch.cuda.empty_cache()
+        kernels = kernel_times(F, w, (x, W, b, tg, g), (dx, dW, db), fwd_avg, peak, max(3, args.steps // 2),
+                               keep_mode)
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dominant]
     print(f"[bench] per kernel: " + ", ".join(f"{k} {v['avg_us']:.1f} us x {v['launches_per_step']} "
@@ -422,7 +443,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 draws, random-init weights)",
-        "config": {"workload": name, "N": N, "H": H, "V": V, "bias": b is not None,
+        "config": {"workload": name, "N": N, "H": H, "V": V, "schedule": args.schedule, "bias": b is not None,
                    "label_smoothing": w.label_smoothing, "z_loss_scale": w.z_loss_scale,
                    "reduction": w.reduction, "ignored_rows": w.n_ignored, "targets": w.targets},
         "fwd_ms": fwd_med,
@@ -432,6 +453,7 @@ def main():
         "extra_hbm_mb": extra / 1e6,
         "extra_hbm_frac_of_fp32_logits": extra / (N * V * 4.0),
         "extra_hbm_measured_mb": extra_measured / 1e6,
+        "keep_mb": keep_bytes / 1e6,
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": kd["tflops"], "peak": peak,
                      "unit": "TFLOP/s", "frac": kd["frac"], "traffic": recorded_traffic(dominant, name),
                      "avg_launch_us": kd["avg_us"], "flops_per_launch": kd["flops_per_launch"],
@@ -439,7 +461,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_fused_line:
-        del ws_f, ws_b
+        ws_f = ws_b = kbuf = None
         torch.cuda.empty_cache()
         r = fused_bench(F, w, (x, W, b, tg, g), (dx, dW, db), 0, 1, max(3, args.steps // 2))
         r["mfma_frac_8nhv"] = 8.0 * N * H * V / (r["ms_per_step"] * 1e-3) / 1e12 / peak
@@ -448,7 +470,7 @@ def main():
               f"{r['extra_hbm_mb']:.1f} MB", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         del x, W, b, dx, dW, db
-        ws_f = ws_b = None
+        ws_f = ws_b = kbuf = None
         torch.cuda.empty_cache()
         rows = args.cpu_rows or max(8, min(N, int(1.0e13 // (8.0 * H * V))))
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
@@ -488,18 +510,23 @@ def fused_bench(F, w, inputs, outs, chunk, warmup, steps):
             "method": "flce_fused_forward_backward, HIP events on the launch stream over the timed steps"}
 
 
-def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, reps):
-    """Average launch duration of each of the four GEMM kernels, from HIP events
-    recorded on the launch stream around public calls that isolate them.
+def kernel_times(F, w, inputs, outs, fwd_avg_ms, peak, reps, keep_mode):
+    """Average launch duration of each GEMM kernel, from HIP events recorded on
+    the launch stream around public calls that isolate them.
 
-    fwd_lse_kernel: the forward call (one launch, plus two O(N) kernels of a
-    few microseconds).  The backward runs, per vocabulary slab, the recompute
-    (bwd_dz_kernel), the dx product and the dW product; a backward asked for
-    dx only runs the recompute and dx, one asked for dW only the recompute and
-    dW, and one asked for db only (with a bias) the recompute and a small
-    column-sum kernel.  So, per slab: bwd_dz = the db-only call (with a bias)
-    or dx-only + dW-only - full (without); bwd_dx = full - dW-only; bwd_dw =
-    full - dx-only.  Each call also runs the O(N) coefficient kernel."""
+    The backward runs, per vocabulary slab, the recompute (bwd_dz_kernel),
+    the dx product and the dW product; a backward asked for dx only runs the
+    recompute and dx, one asked for dW only the recompute and dW, and one
+    asked for db only (with a bias) the recompute and a small column-sum
+    kernel.  So, per slab, from flce_backward calls (every slab recomputed):
+    bwd_dz = the db-only call (with a bias) or dx-only + dW-only - full
+    (without); bwd_dx = full - dW-only; bwd_dw = full - dx-only.  Each call
+    also runs the O(N) coefficient kernel.  The forward: fwd_lse_kernel from
+    the flce_forward call (one launch plus two O(N) kernels of a few
+    microseconds).  With keep_mode the step runs the recompute on every slab
+    but the first, and its forward call (fwd_avg_ms) is the kept-value
+    kernel on the first slab plus fwd_lse_kernel on the rest (one kernel,
+    fused_fwd_kernel, when the vocabulary fits in one slab)."""
     import torch
     from lm_head_cross_flce_amd import _lib
 
@@ -507,15 +534,14 @@ def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, r
     dx, dW, db = outs
     N, H, V = w.N, w.H, w.V
     code = {"bf16": _lib.FLCE_BF16, "f16": _lib.FLCE_F16, "f32": _lib.FLCE_F32}[w.dtype]
-    nslab = -(-V // _lib.flce_backward_slab_cols(N, H, V, code))
+    slab = _lib.flce_backward_slab_cols(N, H, V, code)
+    nslab = -(-V // slab)
+    fb, bb = F.flce_workspace_size(N, H, V, x.dtype, b is not None, w.reduction)
+    ws_f = torch.empty(fb, dtype=torch.uint8, device=x.device)
+    ws_b = torch.empty(bb, dtype=torch.uint8, device=x.device)
     stream = torch.cuda.current_stream()
-    loss, lse, nv = F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
-                                   workspace=ws_f)
 
-    def timed(out):
-        def call():
-            F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                            w.reduction, workspace=ws_b, out=out)
+    def timed(call):
         call()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for e0, e1 in ev:
@@ -525,19 +551,34 @@ def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, r
         torch.cuda.synchronize()
         return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
 
-    t_dx = timed((dx, None, None))
-    t_dw = timed((None, dW, None))
+    def fwd():
+        return F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                              workspace=ws_f)
+
+    loss, lse, nv = fwd()
+
+    def bwd(out):
+        return lambda: F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                       w.reduction, workspace=ws_b, out=out)
+
+    t_full = timed(bwd((dx, dW, db)))
+    t_dx = timed(bwd((dx, None, None)))
+    t_dw = timed(bwd((None, dW, None)))
     if b is not None:
-        t_dz, how = timed((None, None, db)), "db-only backward call / slabs"
+        t_dz, how = timed(bwd((None, None, db))), "db-only backward call / slabs"
     else:
-        t_dz, how = t_dx + t_dw - bwd_avg_ms, "(dx-only + dW-only - full backward call) / slabs"
+        t_dz, how = t_dx + t_dw - t_full, "(dx-only + dW-only - full backward call) / slabs"
     per_slab = 2.0 * N * H * V / nslab
-    rows = {
-        "fwd_lse_kernel": (fwd_avg_ms, 1, 2.0 * N * H * V, "forward call (one launch) / 1"),
-        "bwd_dz_kernel": (t_dz / nslab, nslab, per_slab, how),
-        "bwd_dx_kernel": ((bwd_avg_ms - t_dw) / nslab, nslab, per_slab, "(full - dW-only backward call) / slabs"),
-        "bwd_dw_kernel": ((bwd_avg_ms - t_dx) / nslab, nslab, per_slab, "(full - dx-only backward call) / slabs"),
-    }
+    rows = {}
+    if keep_mode:
+        fname = "fused_fwd_kernel" if nslab == 1 else "fused_fwd_kernel + fwd_lse_kernel"
+        rows[fname] = (fwd_avg_ms, 1, 2.0 * N * H * V, "flce_forward_keep call (its GEMM launches) / 1")
+    else:
+        rows["fwd_lse_kernel"] = (timed(fwd), 1, 2.0 * N * H * V, "forward call (one launch) / 1")
+    if not keep_mode or nslab > 1:
+        rows["bwd_dz_kernel"] = (t_dz / nslab, nslab - 1 if keep_mode else nslab, per_slab, how)
+    rows["bwd_dx_kernel"] = ((t_full - t_dw) / nslab, nslab, per_slab, "(full - dW-only backward call) / slabs")
+    rows["bwd_dw_kernel"] = ((t_full - t_dx) / nslab, nslab, per_slab, "(full - dx-only backward call) / slabs")
     out = {}
     for k, (ms, n, fl, method) in rows.items():
         tf = fl / (ms * 1e-3) / 1e12
@@ -545,6 +586,8 @@ def kernel_times(F, w, inputs, outs, ws_f, ws_b, fwd_avg_ms, bwd_avg_ms, peak, r
                   "tflops": tf, "frac": tf / peak,
                   "method": "flops per launch / average launch duration from HIP events on the launch "
                             f"stream: {method}"}
+    del ws_f, ws_b
+    torch.cuda.empty_cache()
     return out
 
 

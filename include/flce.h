@@ -203,6 +203,55 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Recompute schedule with the first vocabulary slab kept.  flce_forward_keep
+ * computes what flce_forward_ex computes and also leaves, in `keep`, the
+ * logits of W's first slab rows (the first flce_backward_slab_cols rows, or
+ * all V when the vocabulary fits in one slab) as e = exp(z - m_h) in the
+ * input dtype with their fp32 maxima m_h, the form the fused schedule below
+ * keeps them in.  flce_backward_kept takes that buffer and forms the first
+ * slab's dlogits from it instead of recomputing its logits product: the
+ * backward does 2NH(V - slab) fewer flops (none of the recompute when V fits
+ * in one slab).  It uses `keep` as its dlogits slab, so its own workspace
+ * holds no slab: the peak extra memory of the pair is about that of
+ * flce_forward + flce_backward (plus the maxima, N x slab/256 x 8 bytes), but
+ * `keep` is held from the forward to the backward.  Passages: fla
+ * fused_linear_cross_entropy.py, the FusedLinearCrossEntropyFunction forward
+ * docstring (the gradient formed during the forward pass, so the logits are
+ * not recomputed) combined with DeepSpeed PR 8792 "What" (the logits of the
+ * other vocabulary blocks recomputed in backward).
+ *
+ * flce_keep_workspace_size: the forward's workspace (*fwd_bytes), the keep
+ * buffer (*keep_bytes) and the backward's workspace (*bwd_bytes); pure host
+ * arithmetic, any output may be NULL.  flce_forward_keep: as
+ * flce_forward_ex, plus keep (16-byte aligned, at least *keep_bytes).
+ * flce_backward_kept: as flce_backward_ex, plus the keep buffer the forward
+ * filled, with the same problem arguments and opts->logit_scale; it consumes
+ * it (the buffer holds the last slab's dlogits afterwards), so a second
+ * backward needs a new flce_forward_keep (or flce_backward_ex, which
+ * recomputes every slab).  Results equal flce_backward_ex's up to the
+ * rounding of the kept e values (relative 2^-9 in bf16; 2^-11 in fp16, absolute
+ * 2^-25 below its normal range).
+ */
+flce_status flce_keep_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
+                                     flce_reduction reduction, size_t* fwd_bytes, size_t* keep_bytes,
+                                     size_t* bwd_bytes);
+
+flce_status flce_forward_keep(const void* x, const void* W, const void* b, const int64_t* targets,
+                              int64_t N, int64_t H, int64_t V, flce_dtype dtype,
+                              float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                              flce_reduction reduction, const flce_options* opts,
+                              float* loss, float* lse, int64_t* n_valid, void* keep, size_t keep_bytes,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+flce_status flce_backward_kept(const void* x, const void* W, const void* b, const int64_t* targets,
+                               int64_t N, int64_t H, int64_t V, flce_dtype dtype,
+                               float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                               flce_reduction reduction, const flce_options* opts,
+                               const float* lse, const int64_t* n_valid, const float* grad_loss,
+                               void* keep, size_t keep_bytes, void* dx, void* dW, void* db,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Fused schedule: loss and gradients in one pass, the gradients formed while
  * the forward runs, as fla's fused_linear_cross_entropy_forward and
  * Liger-Kernel commit 95b01e9 ("Summary"; the production-defaults table)

@@ -31,6 +31,7 @@ REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 # Every symbol the public header declares.
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex", "flce_backward_ex",
            "flce_forward_noalloc", "flce_fused_workspace_size", "flce_fused_forward_backward",
+           "flce_keep_workspace_size", "flce_forward_keep", "flce_backward_kept",
            "flce_status_string",
            "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
            "flce_shard_backward")
@@ -87,6 +88,15 @@ def load() -> ctypes.CDLL:
         lib.flce_fused_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
                                                     vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flce_fused_forward_backward.restype = c_int
+        lib.flce_keep_workspace_size.argtypes = [i64, i64, i64, c_int, c_int, c_int, ctypes.POINTER(sz),
+                                                 ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        lib.flce_keep_workspace_size.restype = c_int
+        lib.flce_forward_keep.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                          vp, vp, vp, vp, sz, vp, sz, vp]
+        lib.flce_forward_keep.restype = c_int
+        lib.flce_backward_kept.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
+                                           vp, vp, vp, vp, sz, vp, vp, vp, vp, sz, vp]
+        lib.flce_backward_kept.restype = c_int
         lib.flce_status_string.argtypes = [c_int]
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
@@ -230,3 +240,32 @@ def flce_fused_forward_backward(x, W, b, targets, N, H, V, dtype, label_smoothin
                                               chunk_tokens, loss, lse, n_valid, dx or None, dW or None, db or None,
                                               workspace, workspace_bytes, stream or None),
            "flce_fused_forward_backward")
+
+
+def flce_keep_workspace_size(N: int, H: int, V: int, dtype: int, has_bias: bool, reduction: int):
+    """(forward_bytes, keep_bytes, backward_bytes) of the kept-first-slab pair."""
+    f, k, b = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().flce_keep_workspace_size(N, H, V, dtype, int(bool(has_bias)), reduction, ctypes.byref(f),
+                                           ctypes.byref(k), ctypes.byref(b)), "flce_keep_workspace_size")
+    return f.value, k.value, b.value
+
+
+def flce_forward_keep(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                      reduction, opts, loss, lse, n_valid, keep, keep_bytes, workspace, workspace_bytes,
+                      stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_forward_keep(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                    ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
+                                    loss, lse, n_valid, keep or None, keep_bytes, workspace, workspace_bytes,
+                                    stream or None), "flce_forward_keep")
+
+
+def flce_backward_kept(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                       reduction, opts, lse, n_valid, grad_loss, keep, keep_bytes, dx, dW, db, workspace,
+                       workspace_bytes, stream) -> None:
+    """Raw call: every tensor argument is an integer device address (or 0/None)."""
+    _check(load().flce_backward_kept(x, W, b or None, targets, N, H, V, dtype, label_smoothing, z_loss_scale,
+                                     ignore_index, reduction, ctypes.byref(opts) if opts is not None else None,
+                                     lse, n_valid, grad_loss, keep or None, keep_bytes, dx or None, dW or None,
+                                     db or None, workspace, workspace_bytes, stream or None),
+           "flce_backward_kept")

@@ -28,6 +28,14 @@ struct Geometry {
   int dx_split;
   size_t off_partials, off_rowloss, off_rowzl, fwd_total;
   size_t off_slab, off_dxacc, off_dbp, off_coef, off_yv, off_gscale, bwd_total;
+  // Kept first slab (flce_forward_keep / flce_backward_kept): the forward's
+  // kept-value schedule covers W's rows [0, width0) (VT0 tiles, P0 phases),
+  // the plain forward the other VT - VT0 tiles (P1 phases); the keep buffer
+  // holds the slab [N][slab_cols] in the input dtype at 0 and the maxima
+  // [N][VT0][2] fp32 at off_kmref.
+  int64_t width0;
+  int VT0, P0, P1;
+  size_t off_kmref, keep_total;
 };
 
 flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
@@ -96,12 +104,20 @@ int fwd_phases(int NT, int VT) {
 }
 
 // with_dx_acc: the backward keeps its own fp32 dx accumulator (the shard
-// backward accumulates into the caller's buffer instead).
-Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true) {
+// backward accumulates into the caller's buffer instead).  kept: the layouts
+// of flce_forward_keep and flce_backward_kept (the forward's partials cover
+// both of its launches' phases; the backward's slab is the keep buffer).
+Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool with_dx_acc = true,
+                  bool kept = false) {
   Geometry g{};
   const int64_t es = dtype == FLCE_F32 ? 4 : 2;
   g.NT = (int)cdiv(N, kTile);
   g.VT = (int)cdiv(V, kTile);
+  g.slab_cols = slab_cols(N, H, V, dtype);
+  g.width0 = g.slab_cols < V ? g.slab_cols : V;
+  g.VT0 = (int)cdiv(g.width0, kTile);
+  g.P0 = fwd_phases(g.NT, g.VT0);
+  g.P1 = g.VT > g.VT0 ? fwd_phases(g.NT, g.VT - g.VT0) : 0;
   // Forward phases: enough that the grid (token tiles x phases) fills the CUs,
   // and at least 8, so that each XCD's 32 concurrent tiles are 4 token tiles
   // x 8 vocabulary tiles (12 operand panels per round; 16 x 2 at N=32768
@@ -112,18 +128,17 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   g.P = P;
   size_t off = 0;
   g.off_partials = off;
-  off = align_up(off + (size_t)P * N * 16);
+  off = align_up(off + (size_t)(kept ? g.P0 + g.P1 : P) * N * 16);
   g.off_rowloss = off;
   off = align_up(off + (size_t)N * 4);
   g.off_rowzl = off;
   off = align_up(off + (size_t)N * 4);
   g.fwd_total = off;
 
-  g.slab_cols = slab_cols(N, H, V, dtype);
   g.dx_split = with_dx_acc ? dx_split(N, H, g.slab_cols) : 1;
   off = 0;
   g.off_slab = off;
-  off = align_up(off + (size_t)N * g.slab_cols * es);
+  if (!kept) off = align_up(off + (size_t)N * g.slab_cols * es);
   g.off_dxacc = off;
   if (with_dx_acc) off = align_up(off + (size_t)g.dx_split * N * H * 4);
   g.off_dbp = off;
@@ -135,6 +150,9 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   g.off_gscale = off;   // fp16: the dlogits slab's scale {S, 1/S}
   if (dtype == FLCE_F16) off = align_up(off + 8);
   g.bwd_total = off;
+
+  g.off_kmref = align_up((size_t)N * g.slab_cols * es);
+  g.keep_total = align_up(g.off_kmref + (size_t)N * g.VT0 * 2 * 4);
   return g;
 }
 
@@ -242,10 +260,23 @@ flce_status check_inputs(const void* x, const void* W, const void* b, const int6
 // per-token coefficients, then per slab the recompute, dx and dW (+ db)
 // launches.  dx_out_fp32: dx is the fp32 accumulator itself (a.dx_acc),
 // never cast; accumulate: it already holds a partial sum to add to.
+// kmref (flce_backward_kept): the slab buffer a.slab already holds slab 0's
+// kept values e and kmref their maxima; slab 0's dlogits are made from them in
+// place (and its db partials written) instead of being recomputed.
 flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int dtype, bool want_db,
-                         bool dx_out_fp32, bool accumulate, hipStream_t s) {
+                         bool dx_out_fp32, bool accumulate, hipStream_t s, const float* kmref = nullptr) {
   (void)hipGetLastError();
   if (flce::launch_bwd_prepare(a, s) != hipSuccess) return FLCE_ERR_HIP;
+  if (kmref) {
+    flce::FusedDz fd{};
+    fd.ebuf = a.slab; fd.lde = a.ldS;
+    fd.mref = kmref;
+    fd.coef = a.coef; fd.yv = a.yv;
+    fd.N = a.N; fd.V = (int)g.width0; fd.VT = g.VT0;
+    fd.dbp = want_db ? a.dbp : nullptr;
+    fd.gscale = nullptr;   // db partials of dz * S, as the recompute writes them (1/S is applied in their sum)
+    if (flce::launch_fused_dz(fd, dtype, s) != hipSuccess) return FLCE_ERR_HIP;
+  }
   const int64_t cols = g.slab_cols;
   const int64_t nslab = cdiv(V, cols);
   for (int64_t k = 0; k < nslab; ++k) {
@@ -263,7 +294,8 @@ flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int d
     } else if (k == nslab - 1) {
       mode = flce::kDxLast;
     }
-    if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, s) != hipSuccess) return FLCE_ERR_HIP;
+    if (flce::launch_bwd_slab(a, dtype, (int)vs, (int)width, mode, want_db, kmref && k == 0, s) != hipSuccess)
+      return FLCE_ERR_HIP;
   }
   if (a.dx && !dx_out_fp32 && a.dx_split > 1 && flce::launch_bwd_dx_finalize(a, dtype, s) != hipSuccess)
     return FLCE_ERR_HIP;
@@ -319,6 +351,49 @@ flce_status forward_into(const Geometry& g, const void* x, const void* W, const 
   return FLCE_OK;
 }
 
+// flce_forward_keep's launches: the kept-value forward over W's first
+// g.width0 rows, writing e and its maxima into keep, and the plain forward
+// over the rest, then one merge.
+flce_status forward_keep_into(const Geometry& g, const void* x, const void* W, const void* b,
+                              const int64_t* targets, int64_t N, int64_t H, int64_t V, int dtype, float eps, float s,
+                              int64_t ignore_index, int reduction, const flce_options& o, float* loss, float* lse,
+                              int64_t* n_valid, char* keep, char* ws, hipStream_t stream) {
+  const int64_t es = dtype == FLCE_F32 ? 4 : 2;
+  flce::FwdLaunch head{};
+  head.x = x; head.W = W; head.b = b; head.targets = targets;
+  head.N = (int)N; head.H = (int)H; head.V = (int)g.width0;
+  head.NT = g.NT; head.P = g.P0; head.VT = g.VT0;
+  head.ignore_index = ignore_index;
+  head.eps = eps;
+  head.eps_over_v = (float)((double)eps / (double)V);
+  head.s = s;
+  head.reduction = reduction;
+  head.logit_scale = o.logit_scale;
+  head.partials = ws + g.off_partials;
+  head.rowloss = (float*)(ws + g.off_rowloss);
+  head.rowzl = (float*)(ws + g.off_rowzl);
+  head.zloss = o.z_loss;
+  head.loss = loss; head.lse = lse; head.n_valid = n_valid;
+  head.ebuf = keep;
+  head.lde = g.slab_cols;
+  head.mref = (float*)(keep + g.off_kmref);
+  flce::FwdLaunch rest = head;
+  rest.V = (int)(V - g.width0);
+  if (rest.V > 0) {
+    rest.W = (const char*)W + g.width0 * H * es;
+    rest.b = b ? (const char*)b + g.width0 * es : nullptr;
+    rest.VT = g.VT - g.VT0;
+    rest.P = g.P1;
+    rest.vocab_start = g.width0;
+    rest.partials = ws + g.off_partials + (size_t)g.P0 * N * 16;
+    rest.ebuf = nullptr;
+    rest.mref = nullptr;
+  }
+  (void)hipGetLastError();
+  if (flce::launch_forward_keep(head, rest, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
+  return FLCE_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Static forward scratch (flce_forward_noalloc).  Each GPU holds its own copy
 // of this array at its own address for the life of the process; host code
@@ -354,6 +429,12 @@ flce_status scratch_on_stream_device(hipStream_t stream, char** out) {
   *out = g_scratch_ptr[cur];
   return FLCE_OK;
 }
+
+flce_status backward_impl(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N, int64_t H,
+                          int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                          flce_reduction reduction, const flce_options* opts, const float* lse, const int64_t* n_valid,
+                          const float* grad_loss, void* dx, void* dW, void* db, void* keep, size_t keep_bytes,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
 
@@ -441,6 +522,61 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
                              int64_t ignore_index, flce_reduction reduction, const flce_options* opts, const float* lse,
                              const int64_t* n_valid, const float* grad_loss, void* dx, void* dW, void* db,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction, opts,
+                       lse, n_valid, grad_loss, dx, dW, db, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+flce_status flce_keep_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
+                                     flce_reduction reduction, size_t* fwd_bytes, size_t* keep_bytes,
+                                     size_t* bwd_bytes) {
+  flce_status st = check_shape(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  st = check_options(0.f, 0.f, reduction);
+  if (st != FLCE_OK) return st;
+  const Geometry g = geometry(N, H, V, dtype, has_bias, true, true);
+  if (fwd_bytes) *fwd_bytes = g.fwd_total;
+  if (keep_bytes) *keep_bytes = g.keep_total;
+  if (bwd_bytes) *bwd_bytes = g.bwd_total;
+  return FLCE_OK;
+}
+
+flce_status flce_forward_keep(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                              int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                              int64_t ignore_index, flce_reduction reduction, const flce_options* opts, float* loss,
+                              float* lse, int64_t* n_valid, void* keep, size_t keep_bytes, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const flce_options o = opts ? *opts : default_options();
+  flce_status st = check_forward(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, reduction, o,
+                                 loss, lse, n_valid);
+  if (st != FLCE_OK) return st;
+  const Geometry g = geometry(N, H, V, dtype, b != nullptr, true, true);
+  if (workspace_bytes < g.fwd_total || keep_bytes < g.keep_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16) || !keep || !aligned(keep, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  return forward_keep_into(g, x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index,
+                           reduction, o, loss, lse, n_valid, (char*)keep, (char*)workspace, (hipStream_t)stream);
+}
+
+flce_status flce_backward_kept(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N,
+                               int64_t H, int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale,
+                               int64_t ignore_index, flce_reduction reduction, const flce_options* opts,
+                               const float* lse, const int64_t* n_valid, const float* grad_loss, void* keep,
+                               size_t keep_bytes, void* dx, void* dW, void* db, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (!keep) return FLCE_ERR_INVALID_ARGUMENT;
+  return backward_impl(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss_scale, ignore_index, reduction, opts,
+                       lse, n_valid, grad_loss, dx, dW, db, keep, keep_bytes, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// flce_backward_ex, and with keep != NULL flce_backward_kept.
+flce_status backward_impl(const void* x, const void* W, const void* b, const int64_t* targets, int64_t N, int64_t H,
+                          int64_t V, flce_dtype dtype, float label_smoothing, float z_loss_scale, int64_t ignore_index,
+                          flce_reduction reduction, const flce_options* opts, const float* lse, const int64_t* n_valid,
+                          const float* grad_loss, void* dx, void* dW, void* db, void* keep, size_t keep_bytes,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const flce_options o = opts ? *opts : default_options();
   if (!std::isfinite(o.logit_scale)) return FLCE_ERR_INVALID_ARGUMENT;
   flce_status st = check_shape(N, H, V, dtype);
@@ -451,9 +587,10 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   if (!aligned(lse, 4) || !aligned(n_valid, 8) || !aligned(grad_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   if ((dx && !aligned(dx, 16)) || (dW && !aligned(dW, 16))) return FLCE_ERR_INVALID_ARGUMENT;
   if (db && !aligned(db, dtype == FLCE_F32 ? 4 : 2)) return FLCE_ERR_INVALID_ARGUMENT;
-  const Geometry g = geometry(N, H, V, dtype, b != nullptr);
-  if (workspace_bytes < g.bwd_total) return FLCE_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace || !aligned(workspace, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  const bool kept = keep != nullptr;
+  const Geometry g = geometry(N, H, V, dtype, b != nullptr, true, kept);
+  if (workspace_bytes < g.bwd_total || (kept && keep_bytes < g.keep_total)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16) || (kept && !aligned(keep, 16))) return FLCE_ERR_INVALID_ARGUMENT;
   const bool want_db = b != nullptr && db != nullptr;
   if (!dx && !dW && !want_db) return FLCE_OK;
 
@@ -472,7 +609,7 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   a.lse = lse; a.n_valid = n_valid; a.grad = grad_loss;
   a.coef = ws + g.off_coef;
   a.yv = (int*)(ws + g.off_yv);
-  a.slab = ws + g.off_slab;
+  a.slab = kept ? (char*)keep : ws + g.off_slab;
   a.ldS = g.slab_cols;
   a.dx_acc = (float*)(ws + g.off_dxacc);
   a.dx_split = g.dx_split;
@@ -480,8 +617,13 @@ flce_status flce_backward_ex(const void* x, const void* W, const void* b, const 
   a.gscale = dtype == FLCE_F16 ? (float*)(ws + g.off_gscale) : nullptr;
   a.dx = dx; a.dW = dW; a.db = want_db ? db : nullptr;
 
-  return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream);
+  return run_backward(a, g, V, dtype, want_db, false, false, (hipStream_t)stream,
+                      kept ? (const float*)((char*)keep + g.off_kmref) : nullptr);
 }
+
+}  // namespace
+
+extern "C" {
 
 flce_status flce_fused_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
                                       int64_t chunk_tokens, int64_t* chunk_used, size_t* bytes) {

@@ -884,16 +884,22 @@ hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
 
 template <class T>
 static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int dx_mode, bool want_db,
-                                    hipStream_t st) {
+                                    bool dz_ready, hipStream_t st) {
   const int wpad = (width + 7) & ~7;
   const int TV = (width + kTile - 1) / kTile;
   const int TH = (a.H + kTile - 1) / kTile;
   const bool bias = a.b != nullptr;
   const dim3 blk(kThreads);
   const dim3 gdz(TV * a.NT < kPersistGrid ? TV * a.NT : kPersistGrid);
-  if (bias && want_db) hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
-  else if (bias) hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
-  else hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
+  if (dz_ready) {
+    // the slab already holds the dlogits (and the db partials are written)
+  } else if (bias && want_db) {
+    hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
+  } else if (bias) {
+    hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
+  } else {
+    hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
+  }
   if (a.dx) {
     // K split: each part takes kc slab columns (a multiple of the 64-deep copy block).
     const int parts = a.dx_split > 1 ? a.dx_split : 1;
@@ -914,10 +920,10 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
 }
 
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
-                           hipStream_t st) {
-  if (dtype == 1) return launch_bwd_slab_t<uint16_t>(a, vs, width, dx_mode, want_db, st);
-  if (dtype == 2) return launch_bwd_slab_t<_Float16>(a, vs, width, dx_mode, want_db, st);
-  return launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, st);
+                           bool dz_ready, hipStream_t st) {
+  if (dtype == 1) return launch_bwd_slab_t<uint16_t>(a, vs, width, dx_mode, want_db, dz_ready, st);
+  if (dtype == 2) return launch_bwd_slab_t<_Float16>(a, vs, width, dx_mode, want_db, dz_ready, st);
+  return launch_bwd_slab_t<float>(a, vs, width, dx_mode, want_db, dz_ready, st);
 }
 
 
@@ -1299,6 +1305,28 @@ hipError_t launch_fused_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
   if (dtype == 1) return launch_fused_forward_t<uint16_t>(a, st);
   if (dtype == 2) return launch_fused_forward_t<_Float16>(a, st);
   return launch_fused_forward_t<float>(a, st);
+}
+
+// Forward that keeps the first vocabulary slab's logits: the kept-value
+// schedule on W's rows [0, head.V), the plain forward on the rest (rest.V
+// rows from vocab_start head.V; none when rest.V is 0), each writing its own
+// phases' partials, then one merge of all head.P + rest.P phases.
+template <class T>
+static hipError_t launch_forward_keep_t(const FwdLaunch& head, const FwdLaunch& rest, hipStream_t st) {
+  if (sizeof(T) == 2 && head.P >= 4) launch_fused_fwd_order<T, true>(head, st);
+  else launch_fused_fwd_order<T, false>(head, st);
+  if (rest.V > 0) launch_fwd_lse<T>(rest, st);
+  FwdLaunch all = head;
+  all.P = head.P + (rest.V > 0 ? rest.P : 0);
+  hipLaunchKernelGGL(fwd_combine_kernel, dim3((all.N + 255) / 256), dim3(256), 0, st, all);
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, all);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_keep(const FwdLaunch& head, const FwdLaunch& rest, int dtype, hipStream_t st) {
+  if (dtype == 1) return launch_forward_keep_t<uint16_t>(head, rest, st);
+  if (dtype == 2) return launch_forward_keep_t<_Float16>(head, rest, st);
+  return launch_forward_keep_t<float>(head, rest, st);
 }
 
 template <class T>

@@ -73,8 +73,10 @@ hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st);
 // Merge of a.P shards' statistics (a.partials = float4 [P][N]) into lse, loss and the count.
 hipError_t launch_merge(const FwdLaunch& a, hipStream_t st);
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st);
+// dz_ready: the slab already holds the slab's dlogits (and, with want_db,
+// the db partials in a.dbp), so the recompute is skipped.
 hipError_t launch_bwd_slab(const BwdLaunch& a, int dtype, int vs, int width, int dx_mode, bool want_db,
-                           hipStream_t st);
+                           bool dz_ready, hipStream_t st);
 // dx = the sum of the a.dx_split fp32 accumulators (plus dx's old values when
 // a.accumulate), written in dx's dtype.
 hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st);
@@ -96,5 +98,10 @@ hipError_t launch_fused_products(const BwdLaunch& a, int dtype, bool first, hipS
 hipError_t launch_fused_db(const float* dbp, int rows, int64_t lde, float* dbacc, int V, bool first, bool last,
                            void* db, int dtype, bool accumulate, hipStream_t st);
 hipError_t launch_finalize(const FwdLaunch& a, hipStream_t st);
+// Forward keeping the first slab's logits (e values in head.ebuf, maxima in
+// head.mref) for the backward: head covers W's rows [0, head.V) with head.P
+// phases, rest the remaining rest.V rows (vocab_start = head.V) with rest.P
+// phases whose partials follow head's; then the merge and the final loss.
+hipError_t launch_forward_keep(const FwdLaunch& head, const FwdLaunch& rest, int dtype, hipStream_t st);
 
 }  // namespace flce

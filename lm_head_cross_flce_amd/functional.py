@@ -89,6 +89,12 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def flce_keep_workspace_size(N: int, H: int, V: int, dtype: torch.dtype, has_bias: bool,
+                             reduction: str = "mean") -> Tuple[int, int, int]:
+    """(forward bytes, keep bytes, backward bytes) of flce_forward_keep + flce_backward_kept."""
+    return _lib.flce_keep_workspace_size(N, H, V, _DTYPES[dtype], has_bias, _reduction_code(reduction))
+
+
 def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
                  label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
                  reduction: str = "mean", workspace: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
@@ -96,12 +102,37 @@ def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], ta
     """Returns (loss, lse, n_valid): loss float32 [1] (sum/mean) or [N] (none); with
     return_z_loss, (loss, lse, n_valid, z_loss), z_loss the s * lse^2 term alone,
     shaped like loss.  The logits are logit_scale * (x W^T + b)."""
+    return _forward(x, W, b, targets, label_smoothing, z_loss_scale, ignore_index, reduction, workspace,
+                    logit_scale, return_z_loss, None)
+
+
+def flce_forward_keep(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
+                      label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
+                      reduction: str = "mean", workspace: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
+                      return_z_loss: bool = False, keep: Optional[torch.Tensor] = None):
+    """flce_forward that also keeps the first vocabulary slab's logits for
+    flce_backward_kept: returns (loss, lse, n_valid, keep) (with return_z_loss,
+    z_loss last).  keep: a uint8 device buffer of at least the keep bytes of
+    flce_keep_workspace_size to fill (allocated when None)."""
+    return _forward(x, W, b, targets, label_smoothing, z_loss_scale, ignore_index, reduction, workspace,
+                    logit_scale, return_z_loss, keep if keep is not None else True)
+
+
+def _forward(x, W, b, targets, label_smoothing, z_loss_scale, ignore_index, reduction, workspace, logit_scale,
+             return_z_loss, keep):
     x, W, b, targets = _prep(x, W, b, targets)
     N, H = x.shape
     V = W.shape[0]
     dt, red = _dtype_code(x), _reduction_code(reduction)
     dev = x.device
-    fwd_bytes, _ = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    if keep is None:
+        fwd_bytes, _ = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    else:
+        fwd_bytes, keep_bytes, _ = _lib.flce_keep_workspace_size(N, H, V, dt, b is not None, red)
+        if keep is True:
+            keep = torch.empty(keep_bytes, dtype=torch.uint8, device=dev)
+        elif keep.dtype != torch.uint8 or keep.device != dev or not keep.is_contiguous() or keep.numel() < keep_bytes:
+            raise ValueError(f"keep must be a contiguous uint8 tensor of at least {keep_bytes} bytes on {dev}")
     if workspace is None or workspace.numel() < fwd_bytes:
         workspace = torch.empty(max(fwd_bytes, 1), dtype=torch.uint8, device=dev)
     loss = torch.empty(N if reduction == "none" else 1, dtype=torch.float32, device=dev)
@@ -110,7 +141,13 @@ def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], ta
     z_loss = torch.empty_like(loss) if return_z_loss else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        if logit_scale == 1.0 and not return_z_loss:
+        if keep is not None:
+            _lib.flce_forward_keep(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                                   float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                                   _lib.options(logit_scale, False, _ptr(z_loss)), loss.data_ptr(), lse.data_ptr(),
+                                   n_valid.data_ptr(), keep.data_ptr(), keep.numel(), workspace.data_ptr(),
+                                   workspace.numel(), stream)
+        elif logit_scale == 1.0 and not return_z_loss:
             _lib.flce_forward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
                               float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
                               loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), workspace.data_ptr(),
@@ -120,7 +157,8 @@ def flce_forward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], ta
                                  float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
                                  _lib.options(logit_scale, False, _ptr(z_loss)), loss.data_ptr(), lse.data_ptr(),
                                  n_valid.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
-    return (loss, lse, n_valid, z_loss) if return_z_loss else (loss, lse, n_valid)
+    out = (loss, lse, n_valid) if keep is None else (loss, lse, n_valid, keep)
+    return out + (z_loss,) if return_z_loss else out
 
 
 def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
@@ -131,6 +169,26 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
                   out: Optional[Tuple] = None, logit_scale: float = 1.0, accumulate: bool = False):
     """Returns (dx, dW, db) in the input dtype (None where not requested).  With
     accumulate, the gradients are added to the ``out`` tensors' contents."""
+    return _backward(x, W, b, targets, lse, n_valid, grad_loss, label_smoothing, z_loss_scale, ignore_index,
+                     reduction, need_dx, need_dW, need_db, workspace, out, logit_scale, accumulate, None)
+
+
+def flce_backward_kept(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], targets: torch.Tensor,
+                       lse: torch.Tensor, n_valid: torch.Tensor, grad_loss: torch.Tensor, keep: torch.Tensor,
+                       label_smoothing: float = 0.0, z_loss_scale: float = 0.0, ignore_index: int = -100,
+                       reduction: str = "mean", need_dx: bool = True, need_dW: bool = True,
+                       need_db: bool = True, workspace: Optional[torch.Tensor] = None,
+                       out: Optional[Tuple] = None, logit_scale: float = 1.0, accumulate: bool = False):
+    """flce_backward given the keep buffer that flce_forward_keep filled with
+    the same arguments; consumes it (a second backward needs a new forward)."""
+    if keep is None:
+        raise ValueError("keep is the buffer flce_forward_keep returned")
+    return _backward(x, W, b, targets, lse, n_valid, grad_loss, label_smoothing, z_loss_scale, ignore_index,
+                     reduction, need_dx, need_dW, need_db, workspace, out, logit_scale, accumulate, keep)
+
+
+def _backward(x, W, b, targets, lse, n_valid, grad_loss, label_smoothing, z_loss_scale, ignore_index, reduction,
+              need_dx, need_dW, need_db, workspace, out, logit_scale, accumulate, keep):
     H0 = x.shape[1] if x.dim() == 2 else -1
     x, W, b, targets = _prep(x, W, b, targets)
     N, H = x.shape
@@ -141,7 +199,12 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
     g = grad_loss.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
     if g.numel() != (N if reduction == "none" else 1):
         raise ValueError("grad_loss must have N entries for none and one otherwise")
-    _, bwd_bytes = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    if keep is None:
+        _, bwd_bytes = _lib.flce_workspace_size(N, H, V, dt, b is not None, red)
+    else:
+        _, keep_bytes, bwd_bytes = _lib.flce_keep_workspace_size(N, H, V, dt, b is not None, red)
+        if keep.dtype != torch.uint8 or keep.device != dev or not keep.is_contiguous() or keep.numel() < keep_bytes:
+            raise ValueError(f"keep must be the contiguous uint8 buffer flce_forward_keep filled ({keep_bytes} bytes)")
     if workspace is None or workspace.numel() < bwd_bytes:
         workspace = torch.empty(max(bwd_bytes, 1), dtype=torch.uint8, device=dev)
     if out is not None:
@@ -165,7 +228,13 @@ def flce_backward(x: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor], t
             torch.empty(V, H, dtype=x.dtype, device=dev) if dW is not None else None)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        if logit_scale == 1.0 and not accumulate:
+        if keep is not None:
+            _lib.flce_backward_kept(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
+                                    float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
+                                    _lib.options(logit_scale, accumulate, None), lse.data_ptr(), n_valid.data_ptr(),
+                                    g.data_ptr(), keep.data_ptr(), keep.numel(), _ptr(kx), _ptr(kW), _ptr(db),
+                                    workspace.data_ptr(), workspace.numel(), stream)
+        elif logit_scale == 1.0 and not accumulate:
             _lib.flce_backward(x.data_ptr(), W.data_ptr(), _ptr(b), targets.data_ptr(), N, H, V, dt,
                                float(label_smoothing), float(z_loss_scale), int(ignore_index), red,
                                lse.data_ptr(), n_valid.data_ptr(), g.data_ptr(), _ptr(kx), _ptr(kW), _ptr(db),
@@ -347,10 +416,18 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
-                z_loss_scale=0.0, reduction="mean", logit_scale=1.0):
-        loss, lse, n_valid = flce_forward(x, weight, bias, target, label_smoothing, z_loss_scale,
-                                          ignore_index, reduction, logit_scale=logit_scale)
+                z_loss_scale=0.0, reduction="mean", logit_scale=1.0, keep_first_slab=False):
+        # keep_first_slab: the forward keeps the first vocabulary slab's logits
+        # (flce_forward_keep) so the backward skips their recompute; the buffer
+        # (about N x 16384 x 2 bytes) lives until the backward.
+        if keep_first_slab:
+            loss, lse, n_valid, keep = flce_forward_keep(x, weight, bias, target, label_smoothing, z_loss_scale,
+                                                         ignore_index, reduction, logit_scale=logit_scale)
+        else:
+            (loss, lse, n_valid), keep = flce_forward(x, weight, bias, target, label_smoothing, z_loss_scale,
+                                                      ignore_index, reduction, logit_scale=logit_scale), None
         ctx.save_for_backward(x, target, weight, bias, lse, n_valid)
+        ctx.keep = keep
         ctx.opts = (ignore_index, label_smoothing, z_loss_scale, reduction, logit_scale)
         return loss if reduction == "none" else loss.reshape(())
 
@@ -358,28 +435,34 @@ class FusedLinearCrossEntropyFunction(torch.autograd.Function):
     def backward(ctx, grad):
         x, target, weight, bias, lse, n_valid = ctx.saved_tensors
         ignore_index, eps, s, reduction, logit_scale = ctx.opts
-        dx, dW, db = flce_backward(x, weight, bias, target, lse, n_valid, grad, eps, s, ignore_index,
-                                   reduction, need_dx=ctx.needs_input_grad[0],
-                                   need_dW=ctx.needs_input_grad[2],
-                                   need_db=bias is not None and ctx.needs_input_grad[3], logit_scale=logit_scale)
-        return dx, None, dW, db, None, None, None, None, None
+        keep, ctx.keep = ctx.keep, None   # consumed: a second backward recomputes every slab
+        args = (x, weight, bias, target, lse, n_valid, grad)
+        kw = dict(label_smoothing=eps, z_loss_scale=s, ignore_index=ignore_index, reduction=reduction,
+                  need_dx=ctx.needs_input_grad[0], need_dW=ctx.needs_input_grad[2],
+                  need_db=bias is not None and ctx.needs_input_grad[3], logit_scale=logit_scale)
+        if keep is not None:
+            dx, dW, db = flce_backward_kept(*args, keep, **kw)
+        else:
+            dx, dW, db = flce_backward(*args, **kw)
+        return dx, None, dW, db, None, None, None, None, None, None
 
 
 def fused_linear_cross_entropy_loss(x, target, weight, bias=None, ignore_index=-100, label_smoothing=0.0,
-                                    z_loss_scale=0.0, reduction="mean", logit_scale=1.0):
+                                    z_loss_scale=0.0, reduction="mean", logit_scale=1.0, keep_first_slab=False):
     """Functional form: x [N, H], target [N], weight [V, H], bias [V] or None."""
     return FusedLinearCrossEntropyFunction.apply(x, target, weight, bias, ignore_index, label_smoothing,
-                                                 z_loss_scale, reduction, logit_scale)
+                                                 z_loss_scale, reduction, logit_scale, keep_first_slab)
 
 
 class FusedLinearCrossEntropyLoss(torch.nn.Module):
     """Module form; x may be [..., H] and target [...]; they are flattened."""
 
     def __init__(self, ignore_index: int = -100, label_smoothing: float = 0.0, z_loss_scale: float = 0.0,
-                 reduction: str = "mean", logit_scale: float = 1.0):
+                 reduction: str = "mean", logit_scale: float = 1.0, keep_first_slab: bool = False):
         super().__init__()
         _reduction_code(reduction)
         self.logit_scale = logit_scale
+        self.keep_first_slab = keep_first_slab
         self.ignore_index = ignore_index
         self.label_smoothing = label_smoothing
         self.z_loss_scale = z_loss_scale
@@ -388,4 +471,4 @@ class FusedLinearCrossEntropyLoss(torch.nn.Module):
     def forward(self, x, target, weight, bias=None):
         return fused_linear_cross_entropy_loss(x.reshape(-1, x.shape[-1]), target.reshape(-1), weight, bias,
                                                self.ignore_index, self.label_smoothing, self.z_loss_scale,
-                                               self.reduction, self.logit_scale)
+                                               self.reduction, self.logit_scale, self.keep_first_slab)

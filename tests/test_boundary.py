@@ -371,3 +371,69 @@ def _ffb(lib, **over):
 ])
 def test_fused_validation(lib, over, code):
     assert _ffb(lib, **over) == code
+
+
+def test_keep_workspace_sizes(lib):
+    # keep: the first slab [N][slab] in the input dtype and its maxima
+    # [N][slab / 256][2] fp32; the backward's workspace is the recompute's less
+    # the slab; the forward's partials cover both of its launches' phases.
+    for N, H, V, dt, bias in ((8192, 4096, 128256, 1, True), (4096, 2048, 32000, 1, False),
+                              (16384, 1024, 256000, 1, False), (64, 128, 1000, 0, True), (600, 328, 2083, 2, True)):
+        es = 4 if dt == 0 else 2
+        slab = _lib.flce_backward_slab_cols(N, H, V, dt)
+        f, b = _lib.flce_workspace_size(N, H, V, dt, bias, 2)
+        fk, k, bk = _lib.flce_keep_workspace_size(N, H, V, dt, bias, 2)
+        slab_bytes = -(-N * slab * es // 256) * 256
+        assert bk == b - slab_bytes
+        assert slab_bytes + N * (slab // 256) * 8 <= k <= slab_bytes + N * (slab // 256) * 8 + 256
+        assert f <= fk <= f + 256 * 16 * N
+    # the Llama-3-sized head: peak extra memory (keep + backward workspace) stays
+    # under 10% of the fp32 logits
+    fk, k, bk = _lib.flce_keep_workspace_size(8192, 4096, 128256, 1, True, 2)
+    assert max(fk, bk) + k < 0.1 * 8192 * 128256 * 4
+
+
+def _fk(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100, red=2,
+                opts=None, loss=P2, lse=P2, nv=P2, keep=P2, keepb=1 << 30, ws=P2, wsb=1 << 30, stream=None)
+    args.update(over)
+    return lib.flce_forward_keep(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"], args["V"],
+                                 args["dtype"], args["eps"], args["s"], args["ign"], args["red"], args["opts"],
+                                 args["loss"], args["lse"], args["nv"], args["keep"], args["keepb"], args["ws"],
+                                 args["wsb"], args["stream"])
+
+
+def _bk(lib, **over):
+    args = dict(x=P, W=P, b=None, targets=P, N=64, H=128, V=1000, dtype=0, eps=0.0, s=0.0, ign=-100, red=2,
+                opts=None, lse=P2, nv=P2, g=P2, keep=P2, keepb=1 << 30, dx=P2, dW=P2, db=None, ws=P2, wsb=1 << 30,
+                stream=None)
+    args.update(over)
+    return lib.flce_backward_kept(args["x"], args["W"], args["b"], args["targets"], args["N"], args["H"],
+                                  args["V"], args["dtype"], args["eps"], args["s"], args["ign"], args["red"],
+                                  args["opts"], args["lse"], args["nv"], args["g"], args["keep"], args["keepb"],
+                                  args["dx"], args["dW"], args["db"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=12), 2), (dict(dtype=5), 2), (dict(eps=1.5), 1), (dict(s=-1.0), 1), (dict(red=4), 1),
+    (dict(x=None), 1), (dict(x=P + 8), 1), (dict(loss=None), 1), (dict(lse=P2 + 2), 1),
+    (dict(keep=None), 1), (dict(keep=P2 + 8), 1), (dict(keepb=1000), 3),
+    (dict(wsb=16), 3), (dict(ws=None), 1),
+])
+def test_forward_keep_validation(lib, over, code):
+    assert _fk(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), 1), (dict(H=20), 2), (dict(eps=2.0), 1), (dict(red=9), 1),
+    (dict(lse=None), 1), (dict(nv=None), 1), (dict(g=None), 1), (dict(x=None), 1),
+    (dict(dx=P2 + 4), 1), (dict(dW=P2 + 8), 1),
+    (dict(keep=None), 1), (dict(keep=P2 + 8), 1), (dict(keepb=1000), 3),
+    (dict(wsb=100), 3), (dict(ws=None), 1),
+])
+def test_backward_kept_validation(lib, over, code):
+    assert _bk(lib, **over) == code
+
+
+def test_backward_kept_with_nothing_requested_is_a_no_op(lib):
+    assert _bk(lib, dx=None, dW=None, db=None) == 0
