@@ -384,14 +384,23 @@ __device__ __forceinline__ void gemm_tile_f32(Acc& acc, const Opnd<float>& A, in
 //
 // M-contiguous operand, one block = 64 k x 256 m in its global layout: LDS
 // rows (one per k) of 512 bytes; chunk p of row k holds logical chunk
-// p ^ (4 (k & 3)).  Fragments are read with ds_read_b64_tr_b16, which within
+// p ^ mswz(k).  Fragments are read with ds_read_b64_tr_b16, which within
 // each 16-lane group hands lane l element l % 4 of the 8-byte pieces
 // addressed by lanes 4 e + l / 4 (e = 0..3): lane j of group G addresses row
 // k = 8 G + 4 h + j / 4 (plus 32 in a block's second stage) at columns
 // m0 + 4 (j % 4) .. + 3, so lane l receives column m0 + l % 16 at
 // k = 8 G + 4 h + e, the K order of a 16-byte read of a K-contiguous row; two
-// reads (h = 0, 1) give the lane its 8 values.
+// reads (h = 0, 1) give the lane its 8 values.  The LDS serves such a read
+// 32 lanes (two groups, 256 bytes over its 64 banks) per cycle: within a
+// group, 4 (k & 3) spreads the four rows' 32-byte runs over the 256 bytes;
+// 2 ((k >> 3) & 1) moves the odd group's runs to the other 16-byte chunks, so
+// the two groups of a cycle do not share banks.  (With 4 (k & 3) alone they
+// did: every such read took two extra cycles, which the LDS bank-conflict
+// counter showed as one per MFMA in the weight-gradient product.)
 // ---------------------------------------------------------------------------
+
+// Chunk swizzle of row k of an M-contiguous operand's LDS block.
+__device__ __forceinline__ constexpr int mswz(int k) { return (4 * (k & 3)) | (2 * ((k >> 3) & 1)); }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_t* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -460,7 +469,7 @@ template <> struct Dma<false> {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = 2 * (4 * q + wave) + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (row & 3));
+      const int c = (lane & 31) ^ mswz(row);
       off[q] = (m0 + 8 * c < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
@@ -501,7 +510,7 @@ template <> struct FragAddr<false> {
       for (int i = 0; i < 8; ++i) {
         const int k = 8 * G + 4 * h + (j >> 2);
         const int m = wbase + 16 * i + 4 * (j & 3);
-        a[h][i] = k * 512 + 16 * ((m >> 3) ^ (4 * (k & 3))) + 2 * (m & 7);
+        a[h][i] = k * 512 + 16 * ((m >> 3) ^ mswz(k)) + 2 * (m & 7);
       }
   }
   // Read H of block i: elements 2H, 2H + 1 of the fragment's dwords.  The
