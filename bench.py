@@ -85,8 +85,8 @@ def parse():
     p.add_argument("--no-fused-line", action="store_true",
                    help="leave the fused schedule's comparison out of the recompute line")
     p.add_argument("--no-kernel-times", action="store_true",
-                   help="leave out the per-kernel timing calls (counter runs); roofline falls back to the "
-                        "forward call")
+                   help="leave out the library's launch timing log (counter runs); roofline falls back to "
+                        "the forward call")
     return p.parse_args()
 
 
@@ -126,6 +126,28 @@ def recorded_traffic(kernel, workload):
     return float(t.group(1))
 
 
+def recorded_trace(kernel, workload):
+    """The committed kernel trace of this workload, if it was taken from the
+    current kernel sources: {"file", "avg_us"} for ``kernel`` (its average
+    launch duration over every launch of the traced run), else None."""
+    rel_path = os.path.join("profiles", f"flce_step_{workload}_kernel_trace.md")
+    path = os.path.join(ROOT, rel_path)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Source hash `([0-9a-f]+)`", text)
+    names = [k.strip() for k in kernel.split("+")]
+    avgs = []
+    for k in names:
+        a = re.search(r"kernel_avg_us: " + re.escape(k) + r" ([0-9.]+) over (\d+) launches", text)
+        if not a:
+            return None
+        avgs.append(float(a.group(1)))
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    return {"file": rel_path, "avg_us": sum(avgs)}
+
+
 def _kernel_rows(d):
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     rows = []
@@ -156,6 +178,15 @@ def summarize_trace(d):
         t, n = sum(v), len(v)
         warm = (t - v[0]) / (n - 1) if n > 1 else t
         print(f"| `{k}` | {n} | {t / n / 1e3:.1f} | {warm / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.1f}% |")
+    # Per kernel over all its template instances: the average launch duration
+    # that the benchmark's roofline compares with its live figure.
+    fam = {}
+    for k, v in agg.items():
+        f = k.replace("flce::", "").split("<")[0]
+        fam.setdefault(f, []).extend(v)
+    print()
+    for f, v in sorted(fam.items(), key=lambda kv: -sum(kv[1])):
+        print(f"kernel_avg_us: {f} {sum(v) / len(v) / 1e3:.2f} over {len(v)} launches")
 
 
 def summarize_alloc(d):
@@ -388,11 +419,17 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if not args.no_kernel_times:
+        _lib.flce_timing_start(128 * args.steps + 64)   # HIP events between the library's launches
     t0 = time.perf_counter()
     for k in range(args.steps):
         loss = step(events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if not args.no_kernel_times:
+        _lib.flce_timing_stop()
+        launch_log = _lib.flce_timing_log()
+        _lib.flce_timing_clear()
     # Measured extra memory: the allocator's peak over the warmup and timed steps, less
     # the inputs and the gradient outputs (dx, dW, db): the workspaces plus the
     # per-call loss, lse and count.
@@ -414,20 +451,19 @@ def main():
 
     if args.no_kernel_times:
         tf = 2.0 * N * H * V / (fwd_avg * 1e-3) / 1e12
-        kernels = {"fwd_lse_kernel": {"avg_us": fwd_avg * 1e3, "launches_per_step": 1, "ms_per_step": fwd_avg,
-                                      "flops_per_launch": 2.0 * N * H * V, "tflops": tf, "frac": tf / peak,
-                                      "method": "flops per launch / average launch duration from HIP events on "
-                                                "the launch stream: forward call (one launch) / 1"}}
+        kernels = {"forward call": {"avg_us": fwd_avg * 1e3, "launches_per_step": 1, "ms_per_step": fwd_avg,
+                                    "flops_per_launch": 2.0 * N * H * V, "tflops": tf, "frac": tf / peak,
+                                    "method": "2NHV / the forward call's average duration from HIP events on "
+                                              "the launch stream (no launch timing log)"}}
     else:
-        del ws_b, kbuf
-        ws_b = kbuf = None
-        torch.cuda.empty_cache()
-        kernels = kernel_times(F, w, (x, W, b, tg, g), (dx, dW, db), fwd_avg, peak, max(3, args.steps // 2),
-                               keep_mode)
-    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        code = {"bf16": _lib.FLCE_BF16, "f16": _lib.FLCE_F16, "f32": _lib.FLCE_F32}[w.dtype]
+        slab = _lib.flce_backward_slab_cols(N, H, V, code)
+        kernels = kernel_figures(launch_log, args.steps, N, H, V, min(slab, V) if keep_mode else 0, peak)
+    gemms = {k: v for k, v in kernels.items() if "frac" in v}
+    dominant = max(gemms, key=lambda k: gemms[k]["ms_per_step"])
     kd = kernels[dominant]
-    print(f"[bench] per kernel: " + ", ".join(f"{k} {v['avg_us']:.1f} us x {v['launches_per_step']} "
-                                              f"({100 * v['frac']:.1f}%)" for k, v in kernels.items()),
+    print(f"[bench] per kernel: " + ", ".join(f"{k} {v['avg_us']:.1f} us x {v['launches_per_step']:g} "
+                                              f"({100 * v['frac']:.1f}%)" for k, v in gemms.items()),
           file=sys.stderr, flush=True)
 
     out = {
@@ -457,7 +493,7 @@ def main():
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": kd["tflops"], "peak": peak,
                      "unit": "TFLOP/s", "frac": kd["frac"], "traffic": recorded_traffic(dominant, name),
                      "avg_launch_us": kd["avg_us"], "flops_per_launch": kd["flops_per_launch"],
-                     "note": kd["method"]},
+                     "note": kd["method"], "profile": profile_figure(dominant, name, kd, peak)},
         "kernels": kernels,
     }
     if not args.no_fused_line:
@@ -476,6 +512,17 @@ def main():
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, rows)
     print(json.dumps(out), flush=True)
+
+
+def profile_figure(kernel, workload, kd, peak):
+    """The roofline figure recomputed from the committed trace of the same
+    sources (its average launch duration), beside the live one; None without
+    such a trace.  A kernel named "a + b" is one call of both kernels."""
+    t = recorded_trace(kernel, workload)
+    if t is None:
+        return None
+    tf = kd["flops_per_launch"] / (t["avg_us"] * 1e-6) / 1e12
+    return {"file": t["file"], "avg_launch_us": t["avg_us"], "achieved": tf, "frac": tf / peak}
 
 
 def fused_bench(F, w, inputs, outs, chunk, warmup, steps):
@@ -510,84 +557,34 @@ def fused_bench(F, w, inputs, outs, chunk, warmup, steps):
             "method": "flce_fused_forward_backward, HIP events on the launch stream over the timed steps"}
 
 
-def kernel_times(F, w, inputs, outs, fwd_avg_ms, peak, reps, keep_mode):
-    """Average launch duration of each GEMM kernel, from HIP events recorded on
-    the launch stream around public calls that isolate them.
-
-    The backward runs, per vocabulary slab, the recompute (bwd_dz_kernel),
-    the dx product and the dW product; a backward asked for dx only runs the
-    recompute and dx, one asked for dW only the recompute and dW, and one
-    asked for db only (with a bias) the recompute and a small column-sum
-    kernel.  So, per slab, from flce_backward calls (every slab recomputed):
-    bwd_dz = the db-only call (with a bias) or dx-only + dW-only - full
-    (without); bwd_dx = full - dW-only; bwd_dw = full - dx-only.  Each call
-    also runs the O(N) coefficient kernel.  The forward: fwd_lse_kernel from
-    the flce_forward call (one launch plus two O(N) kernels of a few
-    microseconds).  With keep_mode the step runs the recompute on every slab
-    but the first, and its forward call (fwd_avg_ms) is the kept-value
-    kernel on the first slab plus fwd_lse_kernel on the rest (one kernel,
-    fused_fwd_kernel, when the vocabulary fits in one slab)."""
-    import torch
-    from lm_head_cross_flce_amd import _lib
-
-    x, W, b, tg, g = inputs
-    dx, dW, db = outs
-    N, H, V = w.N, w.H, w.V
-    code = {"bf16": _lib.FLCE_BF16, "f16": _lib.FLCE_F16, "f32": _lib.FLCE_F32}[w.dtype]
-    slab = _lib.flce_backward_slab_cols(N, H, V, code)
-    nslab = -(-V // slab)
-    fb, bb = F.flce_workspace_size(N, H, V, x.dtype, b is not None, w.reduction)
-    ws_f = torch.empty(fb, dtype=torch.uint8, device=x.device)
-    ws_b = torch.empty(bb, dtype=torch.uint8, device=x.device)
-    stream = torch.cuda.current_stream()
-
-    def timed(call):
-        call()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e0, e1 in ev:
-            e0.record(stream)
-            call()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
-
-    def fwd():
-        return F.flce_forward(x, W, b, tg, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
-                              workspace=ws_f)
-
-    loss, lse, nv = fwd()
-
-    def bwd(out):
-        return lambda: F.flce_backward(x, W, b, tg, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                                       w.reduction, workspace=ws_b, out=out)
-
-    t_full = timed(bwd((dx, dW, db)))
-    t_dx = timed(bwd((dx, None, None)))
-    t_dw = timed(bwd((None, dW, None)))
-    if b is not None:
-        t_dz, how = timed(bwd((None, None, db))), "db-only backward call / slabs"
-    else:
-        t_dz, how = t_dx + t_dw - t_full, "(dx-only + dW-only - full backward call) / slabs"
-    per_slab = 2.0 * N * H * V / nslab
-    rows = {}
-    if keep_mode:
-        fname = "fused_fwd_kernel" if nslab == 1 else "fused_fwd_kernel + fwd_lse_kernel"
-        rows[fname] = (fwd_avg_ms, 1, 2.0 * N * H * V, "flce_forward_keep call (its GEMM launches) / 1")
-    else:
-        rows["fwd_lse_kernel"] = (timed(fwd), 1, 2.0 * N * H * V, "forward call (one launch) / 1")
-    if not keep_mode or nslab > 1:
-        rows["bwd_dz_kernel"] = (t_dz / nslab, nslab - 1 if keep_mode else nslab, per_slab, how)
-    rows["bwd_dx_kernel"] = ((t_full - t_dw) / nslab, nslab, per_slab, "(full - dW-only backward call) / slabs")
-    rows["bwd_dw_kernel"] = ((t_full - t_dx) / nslab, nslab, per_slab, "(full - dx-only backward call) / slabs")
+def kernel_figures(log, steps, N, H, V, kept_cols, peak):
+    """Per GEMM kernel, from the library's launch timing log over the timed
+    steps (a HIP event on the launch stream before and after every launch):
+    launches per step, average launch duration, and flops per launch = the
+    kernel's flops per step / its launches per step.  Flops per step: the
+    forward product 2NH(V - kept) (fwd_lse_kernel; kept = the first slab's
+    columns when the forward keeps them, else 0), the kept-value forward
+    2NH kept (fused_fwd_kernel), the recompute 2NH(V - kept) (bwd_dz_kernel),
+    dx and dW 2NHV each.  The other kernels are listed with their time only."""
+    gemm = {"fwd_lse_kernel": 2.0 * N * H * (V - kept_cols), "fused_fwd_kernel": 2.0 * N * H * kept_cols,
+            "bwd_dz_kernel": 2.0 * N * H * (V - kept_cols), "bwd_dx_kernel": 2.0 * N * H * V,
+            "bwd_dw_kernel": 2.0 * N * H * V}
+    times = {}
+    for name, ms in log:
+        times.setdefault(name.strip("() ").split("<")[0].strip(), []).append(ms)
     out = {}
-    for k, (ms, n, fl, method) in rows.items():
-        tf = fl / (ms * 1e-3) / 1e12
-        out[k] = {"avg_us": ms * 1e3, "launches_per_step": n, "ms_per_step": ms * n, "flops_per_launch": fl,
-                  "tflops": tf, "frac": tf / peak,
-                  "method": "flops per launch / average launch duration from HIP events on the launch "
-                            f"stream: {method}"}
-    del ws_f, ws_b
-    torch.cuda.empty_cache()
+    for k, v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
+        n = len(v) / steps
+        avg = sum(v) / len(v)
+        row = {"avg_us": avg * 1e3, "launches_per_step": n, "ms_per_step": sum(v) / steps}
+        if k in gemm and gemm[k] > 0:
+            fl = gemm[k] / n
+            tf = fl / (avg * 1e-3) / 1e12
+            row.update({"flops_per_launch": fl, "tflops": tf, "frac": tf / peak,
+                        "method": "flops per launch / average launch duration; durations from HIP events the "
+                                  "library records on the launch stream around each launch (flce_timing_*) "
+                                  "over the timed steps"})
+        out[k] = row
     return out
 
 

@@ -376,6 +376,29 @@ flce_status flce_shard_backward(const void* x, const void* W_shard, const void* 
 /* A static, human-readable name for a status code. */
 const char* flce_status_string(flce_status status);
 
+/*
+ * Launch timing, for measurement (the per-kernel figures a benchmark reports
+ * beside a profiler's trace).  flce_timing_start(capacity) discards the
+ * calling thread's previous log, creates `capacity` HIP events (2 to 2^20)
+ * and turns logging on: from then on the thread's entry-point calls record an
+ * event on their stream before their first kernel and after each kernel
+ * launch (hipEventRecord only: no synchronisation, no device memory), until
+ * the events are used up or flce_timing_stop.  The events skip the
+ * system-scope fence (hipEventDisableSystemFence), so a record writes back no
+ * caches between kernels.  flce_timing_count gives the
+ * number of kernel launches logged; flce_timing_read(i, &kernel, &ms) waits
+ * for launch i's closing event and gives the launch's kernel (a static
+ * string: the kernel and its template arguments as the source names them)
+ * and the time from the event before it to the one after it.
+ * flce_timing_clear destroys the events.  With logging off (the default) the
+ * entry points record nothing.  Not one of the pages' operations.
+ */
+flce_status flce_timing_start(int capacity);
+flce_status flce_timing_stop(void);
+int64_t flce_timing_count(void);
+flce_status flce_timing_read(int64_t index, const char** kernel, float* ms);
+flce_status flce_timing_clear(void);
+
 /* Vocabulary slab width (columns of dlogits held at once) the backward uses
  * for this problem; pure host arithmetic.  Returns 0 on invalid arguments. */
 int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, flce_dtype dtype);

@@ -32,6 +32,7 @@ REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_forward_ex", "flce_backward_ex",
            "flce_forward_noalloc", "flce_fused_workspace_size", "flce_fused_forward_backward",
            "flce_keep_workspace_size", "flce_forward_keep", "flce_backward_kept",
+           "flce_timing_start", "flce_timing_stop", "flce_timing_count", "flce_timing_read", "flce_timing_clear",
            "flce_status_string",
            "flce_backward_slab_cols", "flce_shard_workspace_size", "flce_shard_forward", "flce_shard_merge",
            "flce_shard_backward")
@@ -97,6 +98,16 @@ def load() -> ctypes.CDLL:
         lib.flce_backward_kept.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, f32, f32, i64, c_int, opt,
                                            vp, vp, vp, vp, sz, vp, vp, vp, vp, sz, vp]
         lib.flce_backward_kept.restype = c_int
+        lib.flce_timing_start.argtypes = [c_int]
+        lib.flce_timing_start.restype = c_int
+        lib.flce_timing_stop.argtypes = []
+        lib.flce_timing_stop.restype = c_int
+        lib.flce_timing_count.argtypes = []
+        lib.flce_timing_count.restype = i64
+        lib.flce_timing_read.argtypes = [i64, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(f32)]
+        lib.flce_timing_read.restype = c_int
+        lib.flce_timing_clear.argtypes = []
+        lib.flce_timing_clear.restype = c_int
         lib.flce_status_string.argtypes = [c_int]
         lib.flce_status_string.restype = ctypes.c_char_p
         lib.flce_backward_slab_cols.argtypes = [i64, i64, i64, c_int]
@@ -269,3 +280,31 @@ def flce_backward_kept(x, W, b, targets, N, H, V, dtype, label_smoothing, z_loss
                                      lse, n_valid, grad_loss, keep or None, keep_bytes, dx or None, dW or None,
                                      db or None, workspace, workspace_bytes, stream or None),
            "flce_backward_kept")
+
+
+def flce_timing_start(capacity: int) -> None:
+    _check(load().flce_timing_start(int(capacity)), "flce_timing_start")
+
+
+def flce_timing_stop() -> None:
+    _check(load().flce_timing_stop(), "flce_timing_stop")
+
+
+def flce_timing_clear() -> None:
+    _check(load().flce_timing_clear(), "flce_timing_clear")
+
+
+def flce_timing_log():
+    """[(kernel, ms)] of the launches logged since flce_timing_start (waits for them)."""
+    lib = load()
+    out = []
+    for i in range(int(lib.flce_timing_count())):
+        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        _check(lib.flce_timing_read(i, ctypes.byref(name), ctypes.byref(ms)), "flce_timing_read")
+        out.append((name.value.decode(), float(ms.value)))
+    return out
+
+
+def kernel_family(name: str) -> str:
+    """"(bwd_dx_kernel<T, kDxFirst, false>)" -> "bwd_dx_kernel"."""
+    return name.strip("() ").split("<")[0].strip()

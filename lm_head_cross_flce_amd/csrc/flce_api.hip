@@ -6,6 +6,7 @@
 #include <cstring>
 #include <mutex>
 #include <numeric>
+#include <vector>
 
 #include "flce.h"
 #include "flce_launch.hpp"
@@ -266,6 +267,7 @@ flce_status check_inputs(const void* x, const void* W, const void* b, const int6
 flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int dtype, bool want_db,
                          bool dx_out_fp32, bool accumulate, hipStream_t s, const float* kmref = nullptr) {
   (void)hipGetLastError();
+  flce::mark_launch(s, nullptr);
   if (flce::launch_bwd_prepare(a, s) != hipSuccess) return FLCE_ERR_HIP;
   if (kmref) {
     flce::FusedDz fd{};
@@ -347,6 +349,7 @@ flce_status forward_into(const Geometry& g, const void* x, const void* W, const 
   a.zloss = o.z_loss;
   a.loss = loss; a.lse = lse; a.n_valid = n_valid;
   (void)hipGetLastError();
+  flce::mark_launch(stream, nullptr);
   if (flce::launch_forward(a, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
   return FLCE_OK;
 }
@@ -390,8 +393,32 @@ flce_status forward_keep_into(const Geometry& g, const void* x, const void* W, c
     rest.mref = nullptr;
   }
   (void)hipGetLastError();
+  flce::mark_launch(stream, nullptr);
   if (flce::launch_forward_keep(head, rest, dtype, stream) != hipSuccess) return FLCE_ERR_HIP;
   return FLCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch timing log (flce_timing_*).  Per host thread: a fixed set of events
+// created by flce_timing_start, recorded in order by mark_launch until the
+// set is used up.
+// ---------------------------------------------------------------------------
+struct TimingLog {
+  bool on = false;
+  size_t used = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> tag;
+  std::vector<int> launch_mark;   // mark index that ends each logged launch
+};
+thread_local TimingLog g_tlog;
+
+void timing_clear(TimingLog& t) {
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.tag.clear();
+  t.launch_mark.clear();
+  t.used = 0;
+  t.on = false;
 }
 
 // ---------------------------------------------------------------------------
@@ -438,7 +465,61 @@ flce_status backward_impl(const void* x, const void* W, const void* b, const int
 
 }  // namespace
 
+namespace flce {
+void mark_launch(hipStream_t st, const char* kernel) {
+  TimingLog& t = g_tlog;
+  if (!t.on || t.used >= t.ev.size()) return;
+  if (hipEventRecord(t.ev[t.used], st) != hipSuccess) {
+    t.on = false;
+    return;
+  }
+  t.tag[t.used] = kernel;
+  if (kernel && t.used > 0) t.launch_mark.push_back((int)t.used);
+  ++t.used;
+}
+}  // namespace flce
+
 extern "C" {
+
+flce_status flce_timing_start(int capacity) {
+  if (capacity < 2 || capacity > (1 << 20)) return FLCE_ERR_INVALID_ARGUMENT;
+  TimingLog& t = g_tlog;
+  timing_clear(t);
+  t.ev.resize((size_t)capacity, nullptr);
+  t.tag.assign((size_t)capacity, nullptr);
+  for (int i = 0; i < capacity; ++i) {
+    // timing only: no system-scope fence (cache writeback) at each record
+    if (hipEventCreateWithFlags(&t.ev[(size_t)i], hipEventDisableSystemFence) != hipSuccess) {
+      t.ev.resize((size_t)i);
+      timing_clear(t);
+      return FLCE_ERR_HIP;
+    }
+  }
+  t.on = true;
+  return FLCE_OK;
+}
+
+flce_status flce_timing_stop(void) {
+  g_tlog.on = false;
+  return FLCE_OK;
+}
+
+int64_t flce_timing_count(void) { return (int64_t)g_tlog.launch_mark.size(); }
+
+flce_status flce_timing_read(int64_t index, const char** kernel, float* ms) {
+  const TimingLog& t = g_tlog;
+  if (index < 0 || index >= (int64_t)t.launch_mark.size() || !kernel || !ms) return FLCE_ERR_INVALID_ARGUMENT;
+  const int j = t.launch_mark[(size_t)index];
+  if (hipEventSynchronize(t.ev[(size_t)j]) != hipSuccess) return FLCE_ERR_HIP;
+  if (hipEventElapsedTime(ms, t.ev[(size_t)j - 1], t.ev[(size_t)j]) != hipSuccess) return FLCE_ERR_HIP;
+  *kernel = t.tag[(size_t)j];
+  return FLCE_OK;
+}
+
+flce_status flce_timing_clear(void) {
+  timing_clear(g_tlog);
+  return FLCE_OK;
+}
 
 const char* flce_status_string(flce_status status) {
   switch (status) {
@@ -673,6 +754,7 @@ flce_status flce_fused_forward_backward(const void* x, const void* W, const void
   base.logit_scale = o.logit_scale;
   base.n_valid = n_valid;
   (void)hipGetLastError();
+  flce::mark_launch(stream, nullptr);
   // The mean's count is needed by the first chunk's dlogits.
   flce::FwdLaunch cnt = base;
   cnt.targets = targets;
@@ -783,6 +865,7 @@ flce_status flce_shard_forward(const void* x, const void* W_shard, const void* b
   a.partials = ws + g.off_partials;
   a.stats = stats;
   (void)hipGetLastError();
+  flce::mark_launch((hipStream_t)stream, nullptr);
   if (flce::launch_shard_forward(a, dtype, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
   return FLCE_OK;
 }
@@ -815,6 +898,7 @@ flce_status flce_shard_merge(const float* stats, int64_t num_shards, const int64
   a.rowloss = (float*)workspace;
   a.loss = loss; a.lse = lse; a.n_valid = n_valid;
   (void)hipGetLastError();
+  flce::mark_launch((hipStream_t)stream, nullptr);
   if (flce::launch_merge(a, (hipStream_t)stream) != hipSuccess) return FLCE_ERR_HIP;
   return FLCE_OK;
 }

@@ -305,10 +305,10 @@ template <class T, bool XFIRST>
 static void launch_fwd_lse_order(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
-  if (bias && smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (bias) hipLaunchKernelGGL((fwd_lse_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (smooth) hipLaunchKernelGGL((fwd_lse_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((fwd_lse_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  if (bias && smooth) FLCE_LAUNCH((fwd_lse_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) FLCE_LAUNCH((fwd_lse_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) FLCE_LAUNCH((fwd_lse_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else FLCE_LAUNCH((fwd_lse_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
 }
 
 template <class T>
@@ -324,8 +324,8 @@ static void launch_fwd_lse(const FwdLaunch& a, hipStream_t st) {
 template <class T>
 static hipError_t launch_forward_t(const FwdLaunch& a, hipStream_t st) {
   launch_fwd_lse<T>(a, st);
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  FLCE_LAUNCH(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  FLCE_LAUNCH(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
@@ -338,7 +338,7 @@ hipError_t launch_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
 template <class T>
 static hipError_t launch_shard_forward_t(const FwdLaunch& a, hipStream_t st) {
   launch_fwd_lse<T>(a, st);
-  hipLaunchKernelGGL(fwd_stats_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  FLCE_LAUNCH(fwd_stats_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -349,8 +349,8 @@ hipError_t launch_shard_forward(const FwdLaunch& a, int dtype, hipStream_t st) {
 }
 
 hipError_t launch_merge(const FwdLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  FLCE_LAUNCH(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  FLCE_LAUNCH(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
@@ -858,14 +858,14 @@ hipError_t launch_bwd_dx_finalize(const BwdLaunch& a, int dtype, hipStream_t st)
   if (blocks > 4 * kPersistGrid) blocks = 4 * kPersistGrid;
   const dim3 grid((unsigned)blocks), blk(256);
   if (dtype == 1) {
-    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<uint16_t, false>), grid, blk, 0, st, a);
+    if (a.accumulate) FLCE_LAUNCH((bwd_dx_finalize_kernel<uint16_t, true>), grid, blk, 0, st, a);
+    else FLCE_LAUNCH((bwd_dx_finalize_kernel<uint16_t, false>), grid, blk, 0, st, a);
   } else if (dtype == 2) {
-    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<_Float16, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<_Float16, false>), grid, blk, 0, st, a);
+    if (a.accumulate) FLCE_LAUNCH((bwd_dx_finalize_kernel<_Float16, true>), grid, blk, 0, st, a);
+    else FLCE_LAUNCH((bwd_dx_finalize_kernel<_Float16, false>), grid, blk, 0, st, a);
   } else {
-    if (a.accumulate) hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dx_finalize_kernel<float, false>), grid, blk, 0, st, a);
+    if (a.accumulate) FLCE_LAUNCH((bwd_dx_finalize_kernel<float, true>), grid, blk, 0, st, a);
+    else FLCE_LAUNCH((bwd_dx_finalize_kernel<float, false>), grid, blk, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -877,8 +877,8 @@ __global__ void __launch_bounds__(256) bwd_db_kernel(BwdLaunch a, int vs, int wi
 }
 
 hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
-  if (a.gscale) hipLaunchKernelGGL(bwd_scale_kernel, dim3(1), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(bwd_coef_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  if (a.gscale) FLCE_LAUNCH(bwd_scale_kernel, dim3(1), dim3(1024), 0, st, a);
+  FLCE_LAUNCH(bwd_coef_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -894,11 +894,11 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   if (dz_ready) {
     // the slab already holds the dlogits (and the db partials are written)
   } else if (bias && want_db) {
-    hipLaunchKernelGGL((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
+    FLCE_LAUNCH((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
   } else if (bias) {
-    hipLaunchKernelGGL((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
+    FLCE_LAUNCH((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
   } else {
-    hipLaunchKernelGGL((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
+    FLCE_LAUNCH((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   }
   if (a.dx) {
     // K split: each part takes kc slab columns (a multiple of the 64-deep copy block).
@@ -906,16 +906,16 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
     const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
     const dim3 gdx(TH * a.NT * parts);
     const bool acc = a.accumulate != 0;
-    if (dx_mode == kDxFirst) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxAccum) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxLast && !acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxLast) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (!acc) hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxLast && !acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else if (!acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    else FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
   }
-  if (a.dW && a.accumulate) hipLaunchKernelGGL((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
-  else if (a.dW) hipLaunchKernelGGL((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
-  else if (want_db) hipLaunchKernelGGL((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
+  if (a.dW && a.accumulate) FLCE_LAUNCH((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  else if (a.dW) FLCE_LAUNCH((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
+  else if (want_db) FLCE_LAUNCH((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
   return hipGetLastError();
 }
 
@@ -1279,7 +1279,7 @@ __global__ void __launch_bounds__(256) fused_db_kernel(const float* dbp, int row
 }
 
 hipError_t launch_fused_count(const FwdLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL(fused_count_kernel, dim3(1), dim3(1024), 0, st, a);
+  FLCE_LAUNCH(fused_count_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1287,17 +1287,17 @@ template <class T, bool XFIRST>
 static void launch_fused_fwd_order(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
-  if (bias && smooth) hipLaunchKernelGGL((fused_fwd_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (bias) hipLaunchKernelGGL((fused_fwd_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (smooth) hipLaunchKernelGGL((fused_fwd_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((fused_fwd_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  if (bias && smooth) FLCE_LAUNCH((fused_fwd_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) FLCE_LAUNCH((fused_fwd_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  else FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
 }
 
 template <class T>
 static hipError_t launch_fused_forward_t(const FwdLaunch& a, hipStream_t st) {
   if (sizeof(T) == 2 && a.P >= 4) launch_fused_fwd_order<T, true>(a, st);
   else launch_fused_fwd_order<T, false>(a, st);
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
+  FLCE_LAUNCH(fwd_combine_kernel, dim3((a.N + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1318,8 +1318,8 @@ static hipError_t launch_forward_keep_t(const FwdLaunch& head, const FwdLaunch& 
   if (rest.V > 0) launch_fwd_lse<T>(rest, st);
   FwdLaunch all = head;
   all.P = head.P + (rest.V > 0 ? rest.P : 0);
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3((all.N + 255) / 256), dim3(256), 0, st, all);
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, all);
+  FLCE_LAUNCH(fwd_combine_kernel, dim3((all.N + 255) / 256), dim3(256), 0, st, all);
+  FLCE_LAUNCH(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, all);
   return hipGetLastError();
 }
 
@@ -1332,8 +1332,8 @@ hipError_t launch_forward_keep(const FwdLaunch& head, const FwdLaunch& rest, int
 template <class T>
 static hipError_t launch_fused_dz_t(const FusedDz& f, hipStream_t st) {
   const dim3 grid((unsigned)((f.VT * kTile + 2047) / 2048), (unsigned)((f.N + kTile - 1) / kTile));
-  if (f.dbp) hipLaunchKernelGGL((fused_dz_kernel<T, true>), grid, dim3(256), 0, st, f);
-  else hipLaunchKernelGGL((fused_dz_kernel<T, false>), grid, dim3(256), 0, st, f);
+  if (f.dbp) FLCE_LAUNCH((fused_dz_kernel<T, true>), grid, dim3(256), 0, st, f);
+  else FLCE_LAUNCH((fused_dz_kernel<T, false>), grid, dim3(256), 0, st, f);
   return hipGetLastError();
 }
 
@@ -1358,18 +1358,18 @@ static hipError_t launch_fused_products_t(const BwdLaunch& a, bool first, hipStr
     const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
     const dim3 gdx(TH * a.NT * parts);
     if (parts > 1) {
-      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+      FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
       if (launch_bwd_dx_finalize(a, sizeof(T) == 4 ? 0 : (IsF16<T>::value ? 2 : 1), st) != hipSuccess)
         return hipGetLastError();
     } else if (acc) {
-      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+      FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
     } else {
-      hipLaunchKernelGGL((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
+      FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, 0, width, wpad, TH, kc);
     }
   }
   if (a.dW) {
-    if (first && !acc) hipLaunchKernelGGL((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
-    else hipLaunchKernelGGL((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
+    if (first && !acc) FLCE_LAUNCH((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
+    else FLCE_LAUNCH((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, 0, width, wpad, TH, TV);
   }
   return hipGetLastError();
 }
@@ -1384,16 +1384,16 @@ hipError_t launch_fused_db(const float* dbp, int rows, int64_t lde, float* dbacc
                            void* db, int dtype, bool accumulate, hipStream_t st) {
   const dim3 grid((unsigned)((V + 255) / 256)), blk(256);
   if (dtype == 1)
-    hipLaunchKernelGGL((fused_db_kernel<uint16_t>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+    FLCE_LAUNCH((fused_db_kernel<uint16_t>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
   else if (dtype == 2)
-    hipLaunchKernelGGL((fused_db_kernel<_Float16>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+    FLCE_LAUNCH((fused_db_kernel<_Float16>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
   else
-    hipLaunchKernelGGL((fused_db_kernel<float>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
+    FLCE_LAUNCH((fused_db_kernel<float>), grid, blk, 0, st, dbp, rows, lde, dbacc, V, (int)first, (int)last, db, (int)accumulate);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FwdLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  FLCE_LAUNCH(fwd_finalize_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

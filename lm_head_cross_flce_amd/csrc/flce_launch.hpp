@@ -6,6 +6,19 @@
 
 namespace flce {
 
+// Launch timing: while the calling thread's timing log is on (the C-ABI's
+// flce_timing_start), records a HIP event on st and tags it with `kernel`,
+// the kernel just launched (null: the start of an entry point's launches).
+// Does nothing otherwise.
+void mark_launch(hipStream_t st, const char* kernel);
+
+// Every kernel launch of the library: the launch, then its timing mark.
+#define FLCE_LAUNCH(kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                      \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);    \
+    ::flce::mark_launch(stream, #kernel);                                   \
+  } while (0)
+
 enum Reduction { kNone = 0, kSum = 1, kMean = 2 };
 enum DxMode { kDxFirst = 0, kDxAccum = 1, kDxLast = 2, kDxOnly = 3 };
 

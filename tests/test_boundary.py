@@ -437,3 +437,18 @@ def test_backward_kept_validation(lib, over, code):
 
 def test_backward_kept_with_nothing_requested_is_a_no_op(lib):
     assert _bk(lib, dx=None, dW=None, db=None) == 0
+
+
+def test_timing_log_validation(lib):
+    # no log yet on this thread: nothing to read; bad capacities are rejected
+    # before any HIP call
+    assert lib.flce_timing_count() == 0
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    assert lib.flce_timing_read(0, ctypes.byref(name), ctypes.byref(ms)) == 1
+    assert lib.flce_timing_read(-1, ctypes.byref(name), ctypes.byref(ms)) == 1
+    assert lib.flce_timing_start(1) == 1
+    assert lib.flce_timing_start(-5) == 1
+    assert lib.flce_timing_start(1 << 21) == 1
+    assert lib.flce_timing_stop() == 0 and lib.flce_timing_clear() == 0
+    assert _lib.kernel_family("(bwd_dx_kernel<T, kDxFirst, false>)") == "bwd_dx_kernel"
+    assert _lib.kernel_family("fwd_combine_kernel") == "fwd_combine_kernel"
