@@ -1182,28 +1182,33 @@ __global__ void __launch_bounds__(1024) fused_count_kernel(FwdLaunch a) {
 // past V, stored in T, and with DB the fp32 column sums of dz over each block
 // of 256 tokens.  For fp16 the coefficients carry the slab scale S (as in the
 // recompute schedule), so the stored values are dz S and the column sums are
-// multiplied by 1/S (exact: a power of two).  Thread t of block (bx, by) takes the 8
-// columns 2048 bx + 8 t .. + 7 (one half tile: one m_h per token) of tokens
-// 256 by .. 256 by + 255, eight rows at a time.
+// multiplied by 1/S (exact: a power of two).  Block (bx, by) has 1024 threads
+// (16 waves per CU keep enough loads in flight for this HBM-bound pass):
+// thread t takes the 8 columns 2048 bx + 8 (t % 256) .. + 7 (one half tile:
+// one m_h per token) of the 64 tokens 256 by + 64 (t / 256) .. + 63, eight
+// rows at a time (four for fp32).  With DB the four quarters' column sums are added in LDS,
+// in quarter order.
 template <class T, bool DB>
-__global__ void __launch_bounds__(256) fused_dz_kernel(FusedDz f) {
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (c >= f.VT * kTile) return;   // no barriers below
+__global__ void __launch_bounds__(1024) fused_dz_kernel(FusedDz f) {
+  __shared__ float qsum[DB ? 3 : 1][256][8];
+  const int tx = threadIdx.x & 255, qr = threadIdx.x >> 8;
+  const int c = (blockIdx.x * 256 + tx) * 8;
+  const bool active = c < f.VT * kTile;   // no early return: the DB sum below has a barrier
   const int vt = c >> 8, h = (c >> 7) & 1;
-  const int n0 = blockIdx.y * kTile;
-  const int n1 = min(n0 + kTile, f.N);
+  const int n0 = blockIdx.y * kTile + 64 * qr;
+  const int n1 = min(n0 + 64, f.N);
   const float inv_s = (IsF16<T>::value && f.gscale) ? f.gscale[1] : 1.f;
   const f32x4* coef = (const f32x4*)f.coef;
   float cs[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) cs[k] = 0.f;
-  constexpr int kRows = 8;
-  for (int nb = n0; nb < n1; nb += kRows) {
+  constexpr int kRows = sizeof(T) == 2 ? 8 : 4;   // fp32: half the rows per batch fits 128 VGPRs
+  for (int nb = n0; active && nb < n1; nb += kRows) {
     float v[kRows][8];
     float mr[kRows];
 #pragma unroll
     for (int q = 0; q < kRows; ++q) {
-      const int n = min(nb + q, n1 - 1);   // rows past the block repeat the last (not stored, not summed)
+      const int n = min(nb + q, n1 - 1);   // rows past the quarter repeat the last (not stored, not summed)
       const int64_t base = (int64_t)n * f.lde + c;
       if constexpr (sizeof(T) == 2) {
         const u32x4 u = *(const u32x4*)((const T*)f.ebuf + base);
@@ -1250,9 +1255,18 @@ __global__ void __launch_bounds__(256) fused_dz_kernel(FusedDz f) {
     }
   }
   if (DB) {
-    float* o = f.dbp + (int64_t)blockIdx.y * f.lde + c;
-    *(f32x4*)o = f32x4{cs[0], cs[1], cs[2], cs[3]} * inv_s;
-    *(f32x4*)(o + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]} * inv_s;
+    if (qr > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qsum[qr - 1][tx][k] = cs[k];
+    }
+    __syncthreads();
+    if (qr == 0 && active) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cs[k] = ((cs[k] + qsum[0][tx][k]) + qsum[1][tx][k]) + qsum[2][tx][k];
+      float* o = f.dbp + (int64_t)blockIdx.y * f.lde + c;
+      *(f32x4*)o = f32x4{cs[0], cs[1], cs[2], cs[3]} * inv_s;
+      *(f32x4*)(o + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]} * inv_s;
+    }
   }
 }
 
@@ -1332,8 +1346,8 @@ hipError_t launch_forward_keep(const FwdLaunch& head, const FwdLaunch& rest, int
 template <class T>
 static hipError_t launch_fused_dz_t(const FusedDz& f, hipStream_t st) {
   const dim3 grid((unsigned)((f.VT * kTile + 2047) / 2048), (unsigned)((f.N + kTile - 1) / kTile));
-  if (f.dbp) FLCE_LAUNCH((fused_dz_kernel<T, true>), grid, dim3(256), 0, st, f);
-  else FLCE_LAUNCH((fused_dz_kernel<T, false>), grid, dim3(256), 0, st, f);
+  if (f.dbp) FLCE_LAUNCH((fused_dz_kernel<T, true>), grid, dim3(1024), 0, st, f);
+  else FLCE_LAUNCH((fused_dz_kernel<T, false>), grid, dim3(1024), 0, st, f);
   return hipGetLastError();
 }
 
