@@ -6,7 +6,9 @@ or off, label smoothing, z-loss, any reduction, a random share of ignored
 rows (all of them sometimes), a logit scale, and uniform or Zipf targets.
 The shapes are ragged in every dimension, and most of them split the
 input-gradient product along K (few output tiles) or run several vocabulary
-slabs.  Bar: loss relative error <= 1e-3 (relative 2-norm for reduction
+slabs.  Every case runs through both schedules: flce_forward +
+flce_backward, and the kept-slab pair (half of those cases with 512-column
+slabs, so the kept slab is one of several).  Bar: loss relative error <= 1e-3 (relative 2-norm for reduction
 none), lse <= 1e-5, gradients <= 1e-2 (bf16, fp16) or 1e-5 (fp32) relative
 Frobenius error; exact zeros where the oracle's result is zero.  fp16
 gradients are compared with the exact result rounded to fp16: with means over
@@ -52,24 +54,46 @@ def draw_case(k):
     return w, scale
 
 
+_oracle_cache = {}
+
+
+def _oracle(k, inp, w, scale):
+    if k not in _oracle_cache:
+        _oracle_cache.clear()   # the two schedules of one case run back to back
+        x64, W64, b64 = inp.as_f64("x"), inp.as_f64("W"), inp.as_f64("b")
+        f = O.forward(x64, W64, b64, inp.targets, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                      logit_scale=scale)
+        bw = O.backward(x64, W64, b64, inp.targets, inp.grad, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                        w.reduction, logit_scale=scale)
+        _oracle_cache[k] = (f, bw)
+    return _oracle_cache[k]
+
+
+@pytest.mark.parametrize("schedule", ["recompute", "keep"])
 @pytest.mark.parametrize("k", range(N_CASES))
-def test_sweep(k):
+def test_sweep(k, schedule, monkeypatch):
+    # keep: the kept-slab pair (flce_forward_keep + flce_backward_kept); on
+    # even cases with 512-column slabs, so the kept slab is one of several.
     w, scale = draw_case(k)
-    print(f"[gpu] sweep {k}: N={w.N} H={w.H} V={w.V} {w.dtype} bias={w.b_std is not None} "
+    if schedule == "keep" and k % 2 == 0:
+        monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
+    print(f"[gpu] sweep {k} {schedule}: N={w.N} H={w.H} V={w.V} {w.dtype} bias={w.b_std is not None} "
           f"eps={w.label_smoothing} s={w.z_loss_scale} {w.reduction} ignored={w.n_ignored} scale={scale}",
           flush=True)
     inp = synth.make_inputs(w)
     x, W, b, t, g = device_inputs(inp)
-    loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
-                                   logit_scale=scale)
-    dx, dW, db = F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                                 w.reduction, logit_scale=scale)
+    if schedule == "keep":
+        loss, lse, nv, keep = F.flce_forward_keep(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                                  w.reduction, logit_scale=scale)
+        dx, dW, db = F.flce_backward_kept(x, W, b, t, lse, nv, g, keep, w.label_smoothing, w.z_loss_scale,
+                                          w.ignore_index, w.reduction, logit_scale=scale)
+    else:
+        loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                                       logit_scale=scale)
+        dx, dW, db = F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                     w.reduction, logit_scale=scale)
     torch.cuda.synchronize()
-    x64, W64, b64 = inp.as_f64("x"), inp.as_f64("W"), inp.as_f64("b")
-    f = O.forward(x64, W64, b64, inp.targets, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
-                  logit_scale=scale)
-    bw = O.backward(x64, W64, b64, inp.targets, inp.grad, w.label_smoothing, w.z_loss_scale, w.ignore_index,
-                    w.reduction, logit_scale=scale)
+    f, bw = _oracle(k, inp, w, scale)
     tol = GRAD_RTOL[w.dtype]
     assert int(nv.item()) == f.n_valid
     got_loss = loss.cpu().numpy().astype(np.float64)
