@@ -6,9 +6,10 @@ or off, label smoothing, z-loss, any reduction, a random share of ignored
 rows (all of them sometimes), a logit scale, and uniform or Zipf targets.
 The shapes are ragged in every dimension, and most of them split the
 input-gradient product along K (few output tiles) or run several vocabulary
-slabs.  Every case runs through both schedules: flce_forward +
-flce_backward, and the kept-slab pair (half of those cases with 512-column
-slabs, so the kept slab is one of several).  Bar: loss relative error <= 1e-3 (relative 2-norm for reduction
+slabs.  Every case runs through all three schedules: flce_forward +
+flce_backward, the kept-slab pair (half of those cases with 512-column
+slabs, so the kept slab is one of several), and the fused schedule in
+256-token chunks.  Bar: loss relative error <= 1e-3 (relative 2-norm for reduction
 none), lse <= 1e-5, gradients <= 1e-2 (bf16, fp16) or 1e-5 (fp32) relative
 Frobenius error; exact zeros where the oracle's result is zero.  fp16
 gradients are compared with the exact result rounded to fp16: with means over
@@ -59,7 +60,7 @@ _oracle_cache = {}
 
 def _oracle(k, inp, w, scale):
     if k not in _oracle_cache:
-        _oracle_cache.clear()   # the two schedules of one case run back to back
+        _oracle_cache.clear()   # the schedules of one case run back to back
         x64, W64, b64 = inp.as_f64("x"), inp.as_f64("W"), inp.as_f64("b")
         f = O.forward(x64, W64, b64, inp.targets, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
                       logit_scale=scale)
@@ -69,11 +70,12 @@ def _oracle(k, inp, w, scale):
     return _oracle_cache[k]
 
 
-@pytest.mark.parametrize("schedule", ["recompute", "keep"])
+@pytest.mark.parametrize("schedule", ["recompute", "keep", "fused"])
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_sweep(k, schedule, monkeypatch):
     # keep: the kept-slab pair (flce_forward_keep + flce_backward_kept); on
     # even cases with 512-column slabs, so the kept slab is one of several.
+    # fused: flce_fused_forward_backward in chunks of 256 tokens.
     w, scale = draw_case(k)
     if schedule == "keep" and k % 2 == 0:
         monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
@@ -82,7 +84,11 @@ def test_sweep(k, schedule, monkeypatch):
           flush=True)
     inp = synth.make_inputs(w)
     x, W, b, t, g = device_inputs(inp)
-    if schedule == "keep":
+    if schedule == "fused":
+        loss, lse, nv, dx, dW, db = F.flce_fused_forward_backward(x, W, b, t, g, w.label_smoothing, w.z_loss_scale,
+                                                                  w.ignore_index, w.reduction, chunk_tokens=256,
+                                                                  logit_scale=scale)
+    elif schedule == "keep":
         loss, lse, nv, keep = F.flce_forward_keep(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index,
                                                   w.reduction, logit_scale=scale)
         dx, dW, db = F.flce_backward_kept(x, W, b, t, lse, nv, g, keep, w.label_smoothing, w.z_loss_scale,
