@@ -1182,7 +1182,8 @@ __global__ void __launch_bounds__(1024) fused_count_kernel(FwdLaunch a) {
 // past V, stored in T, and with DB the fp32 column sums of dz over each block
 // of 256 tokens.  For fp16 the coefficients carry the slab scale S (as in the
 // recompute schedule), so the stored values are dz S and the column sums are
-// multiplied by 1/S (exact: a power of two).  Block (bx, by) has 1024 threads
+// multiplied by 1/S (exact: a power of two).  Block bx + CB by (CB = the
+// column blocks; one grid dimension, so any N fits) has 1024 threads
 // (16 waves per CU keep enough loads in flight for this HBM-bound pass):
 // thread t takes the 8 columns 2048 bx + 8 (t % 256) .. + 7 (one half tile:
 // one m_h per token) of the 64 tokens 256 by + 64 (t / 256) .. + 63, eight
@@ -1192,10 +1193,12 @@ template <class T, bool DB>
 __global__ void __launch_bounds__(1024) fused_dz_kernel(FusedDz f) {
   __shared__ float qsum[DB ? 3 : 1][256][8];
   const int tx = threadIdx.x & 255, qr = threadIdx.x >> 8;
-  const int c = (blockIdx.x * 256 + tx) * 8;
+  const unsigned CB = (unsigned)((f.VT * kTile + 2047) / 2048);
+  const unsigned bx = blockIdx.x % CB, by = blockIdx.x / CB;
+  const int c = (bx * 256 + tx) * 8;
   const bool active = c < f.VT * kTile;   // no early return: the DB sum below has a barrier
   const int vt = c >> 8, h = (c >> 7) & 1;
-  const int n0 = blockIdx.y * kTile + 64 * qr;
+  const int n0 = (int)by * kTile + 64 * qr;
   const int n1 = min(n0 + 64, f.N);
   const float inv_s = (IsF16<T>::value && f.gscale) ? f.gscale[1] : 1.f;
   const f32x4* coef = (const f32x4*)f.coef;
@@ -1263,7 +1266,7 @@ __global__ void __launch_bounds__(1024) fused_dz_kernel(FusedDz f) {
     if (qr == 0 && active) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) cs[k] = ((cs[k] + qsum[0][tx][k]) + qsum[1][tx][k]) + qsum[2][tx][k];
-      float* o = f.dbp + (int64_t)blockIdx.y * f.lde + c;
+      float* o = f.dbp + (int64_t)by * f.lde + c;
       *(f32x4*)o = f32x4{cs[0], cs[1], cs[2], cs[3]} * inv_s;
       *(f32x4*)(o + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]} * inv_s;
     }
@@ -1345,7 +1348,7 @@ hipError_t launch_forward_keep(const FwdLaunch& head, const FwdLaunch& rest, int
 
 template <class T>
 static hipError_t launch_fused_dz_t(const FusedDz& f, hipStream_t st) {
-  const dim3 grid((unsigned)((f.VT * kTile + 2047) / 2048), (unsigned)((f.N + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((f.VT * kTile + 2047) / 2048) * (unsigned)((f.N + kTile - 1) / kTile));
   if (f.dbp) FLCE_LAUNCH((fused_dz_kernel<T, true>), grid, dim3(1024), 0, st, f);
   else FLCE_LAUNCH((fused_dz_kernel<T, false>), grid, dim3(1024), 0, st, f);
   return hipGetLastError();

@@ -272,3 +272,42 @@ def test_keep_full_size_dense(name):
         check_close(got_db, _out(d.db, w.dtype), tol, "db")
     if w.dtype == "f16":
         assert rel(got_dx, d.dx) <= 2 * tol and rel(got_dW, d.dW_cols) <= 2 * tol
+
+
+@pytest.mark.timeout(600)
+def test_keep_more_token_tiles_than_one_grid_dimension_holds():
+    # 65537 token tiles of 256 (N = 16,777,472) with H = 8 and V = 300: the
+    # in-place dlogits pass and every token-tiled launch take more blocks than
+    # a second grid dimension allows (65535).  Reduction none makes each row's
+    # loss, lse and dx a function of that row alone, so the oracle checks
+    # sampled rows: the first and last tokens, both sides of tile boundaries
+    # near the start, the middle and the 65535th/65536th tiles, and random rows.
+    N = 65537 * 256
+    w = synth.scaled(synth.WORKLOADS["n16384_h1024_v256000"], "keep_many_tiles", N=N, H=8, V=300)
+    inp = synth.make_inputs(w)
+    print(f"[gpu] keep with {N} tokens (65537 token tiles)", flush=True)
+    x, W, b, t, g = device_inputs(inp)
+    loss, lse, nv, keep = F.flce_forward_keep(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index,
+                                              w.reduction)
+    dx, dW, db = F.flce_backward_kept(x, W, b, t, lse, nv, g, keep, w.label_smoothing, w.z_loss_scale,
+                                      w.ignore_index, w.reduction)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == O.count_valid(inp.targets, w.ignore_index)
+    assert bool(torch.isfinite(dW.float()).all())
+    rows = np.unique(np.concatenate([
+        [0, 1, 255, 256, 257, N // 2 - 1, N // 2, 65535 * 256 - 1, 65535 * 256, 65536 * 256 - 1, 65536 * 256,
+         N - 2, N - 1], O.sample_rows(N, 40, seed=77)]))
+    idx = torch.from_numpy(rows).to(x.device)
+    got_loss = loss[idx].cpu().numpy().astype(np.float64)
+    got_lse = lse[idx].cpu().numpy().astype(np.float64)
+    got_dx = to_f64(dx[idx])
+    del x, W, b, t, g, keep, dx, dW, db, loss, lse, nv
+    torch.cuda.empty_cache()
+    x64 = synth.bf16_bits_to_f64(inp.x[rows])
+    W64 = inp.as_f64("W")
+    f = O.forward(x64, W64, None, inp.targets[rows], w.label_smoothing, w.z_loss_scale, w.ignore_index, "none")
+    bw = O.backward(x64, W64, None, inp.targets[rows], inp.grad[rows], w.label_smoothing, w.z_loss_scale,
+                    w.ignore_index, "none")
+    assert rel(got_loss, f.loss) <= LOSS_RTOL
+    check_close(got_lse, f.lse, LSE_RTOL, "lse")
+    check_close(got_dx, bw.dx, GRAD_RTOL["bf16"], "dx rows")
