@@ -6,6 +6,7 @@
     python bench.py --summarize-pmc DIR         # markdown table from a rocprofv3 --pmc run
     python bench.py --summarize-alloc DIR       # device allocations from a --memory-allocation-trace run
     python bench.py --shards P                  # the vocabulary-shard path: P shards in sequence
+    python bench.py --hbm-activity              # HBM-side activity of the FLCE calls (amdsmi)
 
 A step is one pass of the whole hot path over one batch: flce_forward_keep
 (logits GEMM with the online log-sum-exp epilogue, combine, reduction; the
@@ -74,6 +75,8 @@ def parse():
     p.add_argument("--summarize-trace", default=None, metavar="DIR")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR")
     p.add_argument("--summarize-alloc", default=None, metavar="DIR")
+    p.add_argument("--hbm-activity", action="store_true",
+                   help="memory-controller activity (amdsmi) while calibration loops and the FLCE calls run")
     p.add_argument("--shards", type=int, default=0, metavar="P",
                    help="time the vocabulary-shard entry points: W split into P shards run one after another")
     p.add_argument("--schedule", choices=("keep", "recompute", "fused"), default="keep",
@@ -234,6 +237,140 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copy_probe_bytes_written": b.numel() * 4}))
 
 
+def refresh_window_activity(refreshes):
+    """Average memory-controller busy percentage over consecutive refreshes of
+    the gpu metrics table.  ``refreshes``: (system_clock_counter ns,
+    mem_activity_acc) per refresh, in order, every one seen after the loop
+    started and before it ended.  The window ending at the first refresh began
+    before the loop, so only the windows between refreshes count.  Returns
+    (percent or None, windows, their total length in ms)."""
+    pairs = list(zip(refreshes, refreshes[1:]))
+    acc = sum(b[1] - a[1] for a, b in pairs)
+    span_ms = sum(b[0] - a[0] for a, b in pairs) * 1e-6
+    return (acc / span_ms if span_ms > 0 else None), len(pairs), span_ms
+
+
+def hbm_activity(F, w, x, W, b, tg, g, seconds=4.0):
+    """Memory-controller activity while loops of known HBM traffic run, then
+    while the FLCE calls run.
+
+    The L2 fetch counters count every L2 miss, including those that the 256 MB
+    last-level cache in front of HBM serves.  The SMU's gpu metrics table
+    (amdsmi) sees only the memory controllers: `mem_activity_acc` adds their
+    busy percentage every millisecond, and the table is refreshed about once a
+    second together with `system_clock_counter` (ns).  Each phase keeps its
+    loop on the GPU for ``seconds`` and averages the refresh windows that lie
+    wholly inside it: percent = sum of acc deltas / sum of clock deltas (ms).
+    A read-only loop over 2 GiB (larger than that cache) gives percent per
+    TB/s; a loop re-reading 128 MiB (which fits it) is the control.  Each phase
+    prints one JSON line; the FLCE calls add the HBM bytes per call that the
+    read calibration implies."""
+    import threading
+    import torch
+    import amdsmi
+
+    amdsmi.amdsmi_init()
+    try:
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        dev = x.device
+        N, H, V = w.N, w.H, w.V
+
+        def table():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            return (m["system_clock_counter"], m["mem_activity_acc"], m["average_umc_activity"],
+                    m["current_gfxclk"])
+
+        def phase(name, fn, nbytes=None):
+            print(f"[hbm-activity] {name}", file=sys.stderr, flush=True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fn()
+            e0.record()
+            for _ in range(3):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            iters = max(4, int(seconds * 1e3 / (e0.elapsed_time(e1) / 3)))
+            seen, stop = [], threading.Event()
+            base = table()[0]
+
+            def poll():
+                last = base
+                while not stop.is_set():
+                    t = table()
+                    if t[0] != last:   # a refresh: (host time seen, clock, acc, average, gfxclk)
+                        seen.append((time.perf_counter(),) + t)
+                        last = t[0]
+                    time.sleep(0.02)
+
+            th = threading.Thread(target=poll)
+            th.start()
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t_end = time.perf_counter()
+            stop.set()
+            th.join()
+            ms = e0.elapsed_time(e1) / iters
+            inside = [s for s in seen if s[0] < t_end - 0.05]
+            pct, windows, span_ms = refresh_window_activity([(s[1], s[2]) for s in inside])
+            r = {"phase": name, "iters": iters, "ms_per_iter": ms, "windows": windows, "window_ms": span_ms,
+                 "umc_activity_pct": pct, "average_umc_activity": [s[3] for s in inside[1:]],
+                 "gfxclk_mhz": [s[4] for s in inside[1:]]}
+            if nbytes:
+                r["bytes_per_iter"] = nbytes
+                r["tb_per_s"] = nbytes / (ms * 1e-3) / 1e12
+            return r
+
+        def emit(r):
+            print(json.dumps(r), flush=True)
+
+        emit(phase("idle", lambda: torch.cuda._sleep(20_000_000)))
+        big = torch.ones((2 << 30) // 4, dtype=torch.float32, device=dev)
+        cal = phase("read 2 GiB", lambda: torch.sum(big), big.numel() * 4)
+        emit(cal)
+        small = big[: (128 << 20) // 4]
+        emit(phase("read 128 MiB (fits the last-level cache)", lambda: torch.sum(small), small.numel() * 4))
+        dst = torch.empty_like(big)
+        emit(phase("copy 2 GiB", lambda: dst.copy_(big), 2 * big.numel() * 4))
+        del big, small, dst
+        torch.cuda.empty_cache()
+        pct_per_tbps = cal["umc_activity_pct"] / cal["tb_per_s"]
+
+        fb, kb, bb = F.flce_keep_workspace_size(N, H, V, x.dtype, b is not None, w.reduction)
+        rfb, rbb = F.flce_workspace_size(N, H, V, x.dtype, b is not None, w.reduction)
+        ws_f = torch.empty(max(fb, rfb), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(max(bb, rbb), dtype=torch.uint8, device=dev)
+        kbuf = torch.empty(kb, dtype=torch.uint8, device=dev)
+        outs = (torch.empty_like(x), torch.empty_like(W), torch.empty_like(b) if b is not None else None)
+        args = (w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+        _, lse, nv = F.flce_forward(x, W, b, tg, *args, workspace=ws_f)
+        algo_fwd = (N * H + V * H) * x.element_size() + (V * b.element_size() if b is not None else 0) + N * 8
+
+        def keep_step():
+            _, lse_k, nv_k, _ = F.flce_forward_keep(x, W, b, tg, *args, workspace=ws_f, keep=kbuf)
+            F.flce_backward_kept(x, W, b, tg, lse_k, nv_k, g, kbuf, *args, workspace=ws_b, out=outs)
+
+        calls = [
+            ("forward, every vocabulary column (flce_forward)",
+             lambda: F.flce_forward(x, W, b, tg, *args, workspace=ws_f), algo_fwd),
+            ("backward, every slab recomputed (flce_backward)",
+             lambda: F.flce_backward(x, W, b, tg, lse, nv, g, *args, workspace=ws_b, out=outs), None),
+            ("step, first slab kept (flce_forward_keep + flce_backward_kept)", keep_step, None),
+        ]
+        for name, fn, algo in calls:
+            r = phase(name, fn)
+            if r["umc_activity_pct"] is not None:
+                r["hbm_bytes_per_iter_est"] = r["umc_activity_pct"] / pct_per_tbps * 1e12 * r["ms_per_iter"] * 1e-3
+            if algo:
+                r["algorithmic_bytes"] = algo
+            emit(r)
+        emit({"workload": f"N={N} H={H} V={V}", "calibration_pct_per_tb_per_s": pct_per_tbps})
+    finally:
+        amdsmi.amdsmi_shut_down()
+
+
 def cpu_baseline(inp, rows):
     """Time the fp64 oracle (as it stands) on the first ``rows`` tokens."""
     import numpy as np
@@ -370,6 +507,11 @@ def main():
     db = torch.empty_like(b) if b is not None else None
     stream = torch.cuda.current_stream(dev)
 
+    if args.hbm_activity:
+        del ws_f, ws_b, kbuf
+        torch.cuda.empty_cache()
+        hbm_activity(F, w, x, W, b, tg, g)
+        return
     if args.shards > 0:
         shard_bench(args, w, x, W, b, tg, g, name)
         return
