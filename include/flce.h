@@ -108,12 +108,16 @@ typedef FLCE_ENUM(flce_dtype) {
  * partial statistics for each of P vocabulary phases (P x N x 16 bytes, P =
  * min(V/256 rounded up, max(8, 256 / (N/256 rounded up)))) and per-row losses.
  * The backward figure includes one
- * vocabulary slab of dlogits [N, slab] in the input dtype and an fp32 [N, H]
- * accumulator for dx, plus O(N) and O(N/256 * V) fp32 scratch (and, for fp16,
- * 256 bytes for the slab's scale).  When the dx
- * product has too few 256 x 256 output tiles to fill the GPU (at most half
- * of its 256 CUs), each slab's columns are split into P <= 8 parts, each with
- * its own fp32 [N, H] accumulator (P x N x H x 4 bytes, at most about 64 MB).
+ * vocabulary slab of dlogits [N, slab] in the input dtype, plus O(N) and
+ * O(N/256 * V) fp32 scratch (and, for fp16, 256 bytes for the slab's scale),
+ * and what dx accumulates in over the slabs.  dx sums in fp32: with several
+ * slabs, fp32 inputs accumulate in dx itself, and 16-bit inputs keep each
+ * fp32 value's high 16 bits in dx (so dx holds no result until the call
+ * ends) and its low 16 bits in an [N, H] 16-bit workspace array; one slab
+ * needs neither.  When the dx product has too few 256 x 256 output tiles to
+ * fill the GPU (at most half of its 256 CUs), each slab's columns are split
+ * into P <= 8 parts instead, each with its own fp32 [N, H] accumulator in the
+ * workspace (P x N x H x 4 bytes, at most about 64 MB).
  */
 flce_status flce_workspace_size(int64_t N, int64_t H, int64_t V, flce_dtype dtype, int has_bias,
                                 flce_reduction reduction, size_t* fwd_bytes, size_t* bwd_bytes);

@@ -95,6 +95,19 @@ int dx_split(int64_t N, int64_t H, int64_t slab_cols) {
   return p < 2 ? 1 : (int)p;
 }
 
+// Where the backward accumulates dx over the slabs.  Several K parts: one
+// fp32 [N][H] accumulator each, summed once at the end.  One part and several
+// slabs: fp32 inputs accumulate in dx itself; 16-bit inputs keep each fp32
+// value's high half in dx and its low half in an [N][H] 16-bit array (exact:
+// the value is the two halves' bits).  One slab: no accumulator.
+bool dx_in_place(int64_t V, int64_t slab_cols, int parts) { return parts <= 1 && cdiv(V, slab_cols) > 1; }
+
+size_t dx_acc_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t slab_cols, int parts) {
+  if (parts > 1) return (size_t)parts * N * H * 4;
+  if (!dx_in_place(V, slab_cols, parts) || dtype == FLCE_F32) return 0;
+  return (size_t)N * H * 2;
+}
+
 // Forward phases for NT token tiles: enough that the grid (token tiles x
 // phases) fills the CUs, and at least 8 (see geometry), at most VT.
 int fwd_phases(int NT, int VT) {
@@ -141,7 +154,7 @@ Geometry geometry(int64_t N, int64_t H, int64_t V, int dtype, int has_bias, bool
   g.off_slab = off;
   if (!kept) off = align_up(off + (size_t)N * g.slab_cols * es);
   g.off_dxacc = off;
-  if (with_dx_acc) off = align_up(off + (size_t)g.dx_split * N * H * 4);
+  if (with_dx_acc) off = align_up(off + dx_acc_bytes(N, H, V, dtype, g.slab_cols, g.dx_split));
   g.off_dbp = off;
   if (has_bias) off = align_up(off + (size_t)g.NT * g.slab_cols * 4);
   g.off_coef = off;
@@ -281,12 +294,18 @@ flce_status run_backward(flce::BwdLaunch& a, const Geometry& g, int64_t V, int d
   }
   const int64_t cols = g.slab_cols;
   const int64_t nslab = cdiv(V, cols);
+  // dx accumulated in place (see dx_acc_bytes): fp32 dx is its own
+  // accumulator, which the caller's-buffer modes below handle.
+  const bool in_place = !dx_out_fp32 && a.dx && dx_in_place(V, cols, a.dx_split);
+  const bool fp32_in_place = in_place && dtype == FLCE_F32;
+  if (fp32_in_place) a.dx_acc = (float*)a.dx;
+  a.split_acc = in_place && dtype != FLCE_F32;
   for (int64_t k = 0; k < nslab; ++k) {
     const int64_t vs = k * cols;
     const int64_t width = (V - vs) < cols ? (V - vs) : cols;
     int mode = flce::kDxAccum;
-    if (dx_out_fp32) {
-      if (k == 0 && !accumulate) mode = flce::kDxFirst;
+    if (dx_out_fp32 || fp32_in_place) {
+      if (k == 0 && !(accumulate || (fp32_in_place && a.accumulate))) mode = flce::kDxFirst;
     } else if (a.dx_split > 1) {
       mode = k == 0 ? flce::kDxFirst : flce::kDxAccum;   // the parts' sum is written below
     } else if (nslab == 1) {

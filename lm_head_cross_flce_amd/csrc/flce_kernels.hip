@@ -774,9 +774,16 @@ __device__ __forceinline__ f32x4 load4_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
 // [p kc, (p + 1) kc) of part p = b / G into accumulator p, in the First or
 // Accum mode; a part past the slab's columns reads only zeros (its operands'
 // valid K is 0), so it still writes or keeps its accumulator.
-template <class T, int MODE, bool ACC>
+//
+// SPLIT (16-bit T, one part): the accumulator is split as a.split_acc
+// describes, high halves in dx, low halves in a.dx_acc; an fp32 value is
+// exactly (high << 16) | low, so nothing is rounded before the last slab.
+// With ACC, dx's old values are added in the First mode, before the first
+// high halves overwrite them.
+template <class T, int MODE, bool ACC, bool SPLIT = false>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs, int width, int wpad, int TM,
                                                              int kc) {
+  static_assert(!SPLIT || sizeof(T) == 2, "split accumulators hold fp32 values in two 16-bit halves");
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int G = TM * a.NT;
@@ -796,7 +803,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   constexpr bool kRead = MODE == kDxAccum || MODE == kDxLast;
   constexpr bool kAcc = MODE == kDxFirst || MODE == kDxAccum;   // write the fp32 accumulator
   // Descriptors start at token row n0, so offsets stay below 256 * H * 4 bytes.
-  const __amdgpu_buffer_rsrc_t racc = make_rsrc(a.dx_acc + (int64_t)part * a.N * a.H + (int64_t)n0 * a.H);
+  const __amdgpu_buffer_rsrc_t racc =
+      SPLIT ? make_rsrc((const uint16_t*)a.dx_acc + (int64_t)n0 * a.H)
+            : make_rsrc(a.dx_acc + (int64_t)part * a.N * a.H + (int64_t)n0 * a.H);
   const __amdgpu_buffer_rsrc_t rdx = make_rsrc((const T*)a.dx + (int64_t)n0 * a.H);
   const int g = lane >> 4;
   // Byte offset of block b = 8 j + i (row n = n0 + nl, columns h .. h + 3)
@@ -813,26 +822,104 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dx_kernel(BwdLaunch a, int vs
   // one CU's share of HBM bandwidth needs while every CU makes its
   // read-modify-write at the same moment.
   constexpr int kAhead = 12;
-  constexpr bool kOld = ACC && !kAcc;   // read the dx being added to
-  f32x4 old[kAhead + 1], oldx[kAhead + 1];
+  if constexpr (SPLIT) {
+    // Pairs of blocks 2q, 2q + 1 (columns h and h + 16 of one token).
+    // v_permlane16_swap trades value r of block 2q held by lane groups
+    // g = 1, 3 for value r of block 2q + 1 held by groups g = 0, 2 (lanes 16
+    // apart, same token), after which a lane holds eight consecutive columns:
+    // block 2q's from 4g (g even) or block 2q + 1's from 16 + 4(g - 1) (g odd).
+    // Each half of the accumulator then moves in one 16-byte access.
+    constexpr int kAheadP = kAhead / 2;
+    constexpr bool kOld = ACC && MODE == kDxFirst;   // dx's old values, before its first overwrite
+    auto poff = [&](int q) -> uint32_t {
+      const int i = (2 * q) & 7, j = (2 * q) >> 3;
+      const int nl = wn * kWaveTile + 16 * j + (lane & 15);
+      const int h = h0 + wm * kWaveTile + 16 * i + 4 * (g & 2) + 16 * (g & 1);
+      return (n0 + nl < a.N && h < a.H) ? (uint32_t)(nl * a.H + h) * 2u : kOOB;   // H % 8 == 0: all 8 or none
+    };
+    u32x4 hi[kAheadP + 1], lo[kAheadP + 1], ox[kAheadP + 1];
+    auto fetch = [&](int q) {
+      const uint32_t off = poff(q);
+      if (kRead) {
+        hi[q % (kAheadP + 1)] = __builtin_bit_cast(u32x4, buf_load16(rdx, off));
+        lo[q % (kAheadP + 1)] = __builtin_bit_cast(u32x4, buf_load16(racc, off));
+      }
+      if (kOld) ox[q % (kAheadP + 1)] = __builtin_bit_cast(u32x4, buf_load16(rdx, off));
+    };
 #pragma unroll
-  for (int b = 0; b < kAhead; ++b) {
-    if (kRead) old[b] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b, 4u)));
-    if (kOld) oldx[b] = load4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)));
-  }
+    for (int q = 0; q < kAheadP; ++q) fetch(q);
 #pragma unroll
-  for (int b = 0; b < 64; ++b) {
-    const int bn = b + kAhead;
-    if (kRead && bn < 64) old[bn % (kAhead + 1)] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn, 4u)));
-    if (kOld && bn < 64) oldx[bn % (kAhead + 1)] = load4_buf<T>(rdx, boff(bn, (uint32_t)sizeof(T)));
-    f32x4 v = acc_read4(acc[b & 7][b >> 3]);
-    if constexpr (IsF16<T>::value) v *= inv;
-    if (kRead) v += old[b % (kAhead + 1)];
-    if (kOld) v += oldx[b % (kAhead + 1)];
-    if (kAcc) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(b, 4u), 0, 0);
-    } else {
-      store4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)), v);
+    for (int q = 0; q < 32; ++q) {
+      if (q + kAheadP < 32) fetch(q + kAheadP);
+      const int i = (2 * q) & 7, j = (2 * q) >> 3;
+      f32x4 v0 = acc_read4(acc[i][j]), v1 = acc_read4(acc[i + 1][j]);
+      if constexpr (IsF16<T>::value) {
+        v0 *= inv;
+        v1 *= inv;
+      }
+      float w[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0[r]), __float_as_uint(v1[r]), false, false);
+        w[r] = __uint_as_float(sw[0]);
+        w[4 + r] = __uint_as_float(sw[1]);
+      }
+      if (kRead) {
+        // element 2k's bits: the low halves of word k of each part; 2k + 1's: the high halves
+        const u32x4 h = hi[q % (kAheadP + 1)], l = lo[q % (kAheadP + 1)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w[2 * k] += __uint_as_float((h[k] << 16) | (l[k] & 0xffffu));
+          w[2 * k + 1] += __uint_as_float((h[k] & 0xffff0000u) | (l[k] >> 16));
+        }
+      }
+      if (kOld) {
+        const u32x4 o = ox[q % (kAheadP + 1)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w[2 * k] += h16_to_f32<T>(o[k]);
+          w[2 * k + 1] += h16_to_f32<T>(o[k] >> 16);
+        }
+      }
+      const uint32_t off = poff(q);
+      if (kAcc) {
+        u32x4 hw, lw;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t u0 = __float_as_uint(w[2 * k]), u1 = __float_as_uint(w[2 * k + 1]);
+          hw[k] = (u0 >> 16) | (u1 & 0xffff0000u);
+          lw[k] = (u0 & 0xffffu) | (u1 << 16);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(hw, rdx, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(lw, racc, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack2<T>(w[0], w[1]), pack2<T>(w[2], w[3]), pack2<T>(w[4], w[5]), pack2<T>(w[6], w[7])}, rdx, off,
+            0, 0);
+      }
+    }
+  } else {
+    constexpr bool kOld = ACC && !kAcc;   // read the dx being added to
+    f32x4 old[kAhead + 1], oldx[kAhead + 1];
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) {
+      if (kRead) old[b] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(b, 4u)));
+      if (kOld) oldx[b] = load4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)));
+    }
+#pragma unroll
+    for (int b = 0; b < 64; ++b) {
+      const int bn = b + kAhead;
+      if (kRead && bn < 64) old[bn % (kAhead + 1)] = __builtin_bit_cast(f32x4, buf_load16(racc, boff(bn, 4u)));
+      if (kOld && bn < 64) oldx[bn % (kAhead + 1)] = load4_buf<T>(rdx, boff(bn, (uint32_t)sizeof(T)));
+      f32x4 v = acc_read4(acc[b & 7][b >> 3]);
+      if constexpr (IsF16<T>::value) v *= inv;
+      if (kRead) v += old[b % (kAhead + 1)];
+      if (kOld) v += oldx[b % (kAhead + 1)];
+      if (kAcc) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), racc, boff(b, 4u), 0, 0);
+      } else {
+        store4_buf<T>(rdx, boff(b, (uint32_t)sizeof(T)), v);
+      }
     }
   }
 }
@@ -906,7 +993,19 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
     const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
     const dim3 gdx(TH * a.NT * parts);
     const bool acc = a.accumulate != 0;
-    if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+      if (a.split_acc) {
+        done = true;
+        if (dx_mode == kDxFirst && acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, true, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+        else if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+        else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+        else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+        else return hipErrorInvalidValue;   // one slab needs no accumulator
+      }
+    }
+    if (done) {
+    } else if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
     else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
     else if (dx_mode == kDxLast && !acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
     else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);

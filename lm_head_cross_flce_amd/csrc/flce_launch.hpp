@@ -61,8 +61,12 @@ struct BwdLaunch {
   void* coef;             // float4 [N]
   int* yv;                // [N]
   void* slab; int64_t ldS;
-  float* dx_acc;          // [dx_split][N][H]
+  float* dx_acc;          // [dx_split][N][H] fp32; with split_acc, uint16 [N][H]
   int dx_split;           // input-gradient K split: parts of each slab's columns, one accumulator each
+  // 16-bit inputs, one part, several slabs: each fp32 accumulator value is
+  // held as its high 16 bits in dx itself and its low 16 bits in dx_acc (the
+  // last slab writes the rounded result over the high halves).
+  int split_acc;
   float* dbp;             // [NT][ldS]: per token tile db partials of the current slab; null if no db
   float* gscale;          // fp16 inputs: {S, 1/S}, the dlogits slab's power-of-two scale; null otherwise
   void* dx; void* dW; void* db;

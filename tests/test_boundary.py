@@ -64,7 +64,8 @@ def test_workspace_size_arithmetic(lib):
     assert f >= P * 8192 * 16 + 8192 * 4
     slab = _lib.flce_backward_slab_cols(8192, 4096, 128256, _lib.FLCE_BF16)
     assert slab % 256 == 0 and slab >= 256
-    need = 8192 * slab * 2 + 8192 * 4096 * 4 + NT * slab * 4 + 8192 * 20
+    # the dx accumulator keeps only its low 16-bit halves here (the high halves live in dx)
+    need = 8192 * slab * 2 + 8192 * 4096 * 2 + NT * slab * 4 + 8192 * 20
     assert need <= b <= need + 8 * 256
     # extra memory at the Llama-3-sized head stays under 10% of the fp32 logits
     assert f + b < 0.1 * 8192 * 128256 * 4
@@ -84,6 +85,23 @@ def test_fp16_workspace_adds_the_slab_scale(lib):
     fs, ms, bs = _lib.flce_shard_workspace_size(8192, 4096, 16032, _lib.FLCE_F16, True)
     _, _, bs16 = _lib.flce_shard_workspace_size(8192, 4096, 16032, _lib.FLCE_BF16, True)
     assert bs == bs16 + 256
+
+
+def test_dx_accumulator_bytes_by_dtype_and_slab_count(lib):
+    # one K part and several slabs: fp32 inputs accumulate in dx itself, 16-bit
+    # inputs hold the fp32 low halves in the workspace; one slab: nothing
+    N, H, V = 8192, 4096, 128256
+    slab = _lib.flce_backward_slab_cols(N, H, V, _lib.FLCE_BF16)
+    _, b16 = _lib.flce_workspace_size(N, H, V, _lib.FLCE_BF16, False, 2)
+    _, b32 = _lib.flce_workspace_size(N, H, V, _lib.FLCE_F32, False, 2)
+    slab32 = _lib.flce_backward_slab_cols(N, H, V, _lib.FLCE_F32)
+    tail = N * 20
+    assert N * slab * 2 + N * H * 2 + tail <= b16 <= N * slab * 2 + N * H * 2 + tail + 8 * 256
+    assert N * slab32 * 4 + tail <= b32 <= N * slab32 * 4 + tail + 8 * 256
+    # a vocabulary within one slab: no accumulator (N = 8192, H = 4096 never splits K)
+    V1 = slab
+    _, b1 = _lib.flce_workspace_size(N, H, V1, _lib.FLCE_BF16, False, 2)
+    assert N * slab * 2 + tail <= b1 <= N * slab * 2 + tail + 8 * 256
 
 
 def test_workspace_holds_one_dx_accumulator_per_k_part(lib):
@@ -246,7 +264,12 @@ def test_shard_workspace_sizes(lib):
     ff, bb = _lib.flce_workspace_size(8192, 4096, 16032, _lib.FLCE_BF16, True, 2)
     assert f == ff                                   # same forward partials
     assert m >= 8192 * 4                             # per-row losses of the merge
-    assert b == bb - 8192 * 4096 * 4                 # no dx accumulator: the caller's fp32 buffer
+    assert b == bb                                   # 16032 rows fit one slab: no dx accumulator in either
+    # several slabs: the plain backward holds the accumulator's low halves, the
+    # shard backward none (it accumulates in the caller's fp32 buffer)
+    _, _, b4 = _lib.flce_shard_workspace_size(8192, 4096, 64128, _lib.FLCE_BF16, True)
+    _, bb4 = _lib.flce_workspace_size(8192, 4096, 64128, _lib.FLCE_BF16, True, 2)
+    assert b4 == bb4 - 8192 * 4096 * 2
     assert _sbwd(lib, dx=None, dW=None, db=None) == 0   # nothing requested: no launch, OK
 
 
@@ -334,7 +357,7 @@ def test_fused_workspace_and_default_chunk(lib):
         if bigger is not None:
             bigger = -(-bigger // 256) * 256
             assert _lib.flce_fused_workspace_size(N, H, V, _lib.FLCE_BF16, bias, bigger)[0] > f + b
-    assert _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 0)[1] == 1280
+    assert _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 0)[1] == 1024
     # explicit chunk: the kept logits [chunk][V rounded up to 256] in bf16 dominate
     fb, chunk = _lib.flce_fused_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 1024)
     assert chunk == 1024

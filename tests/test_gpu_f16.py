@@ -98,6 +98,32 @@ def test_f16_forced_slabs_and_k_split(monkeypatch):
         check(name, run(inputs(name)))
 
 
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_f16_split_dx_accumulator(monkeypatch, accumulate):
+    # 256-column slabs give one K part, so dx accumulates over nine slabs as
+    # fp32 values split in two: the high halves in dx itself, the low halves in
+    # the workspace.  With accumulate, dx's old values are added on the first
+    # slab, before its high halves replace them.
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "256")
+    name = "c3_f16"
+    inp = inputs(name)
+    w = inp.w
+    print(f"[gpu] f16 split dx accumulator, accumulate={accumulate}", flush=True)
+    if not accumulate:
+        check(name, run(inp))
+        return
+    f, bw = oracle(name)
+    x, W, b, t, g = device_inputs(inp)
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    dx0 = (torch.randn(x.shape, generator=gen, dtype=torch.float64) * float(np.std(bw.dx))).to(x.dtype).to(x.device)
+    out = (dx0.clone(), None, None)
+    loss, lse, nv = F.flce_forward(x, W, b, t, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction)
+    F.flce_backward(x, W, b, t, lse, nv, g, w.label_smoothing, w.z_loss_scale, w.ignore_index, w.reduction,
+                    need_dW=False, need_db=False, out=out, accumulate=True)
+    torch.cuda.synchronize()
+    assert rel(to_f64(out[0]), to_f64(dx0) + bw.dx) <= GRAD_RTOL["f16"]
+
+
 def test_f16_all_ignored_gives_exact_zeros():
     w = _case("n8192_h4096_v128256", "f16_all_ignored", N=300, H=64, V=700, n_ignored=300)
     print("[gpu] f16 all ignored", flush=True)

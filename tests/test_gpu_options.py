@@ -78,10 +78,12 @@ def test_z_loss_term_alone(red):
 
 
 @pytest.mark.parametrize("name,slab", [("c3_small", None), ("c3_small", "512"), ("c3_small", "1024"),
-                                       ("f32_none", None)])
+                                       ("f32_none", None), ("f32_none", "256")])
 def test_accumulate_into_existing_gradients(monkeypatch, name, slab):
-    # one slab and several (dx through the fp32 accumulators; with no override
-    # and with 1024 columns these shapes split each slab's columns in K parts)
+    # one slab and several (with no override and with 1024 columns these
+    # shapes split each slab's columns in K parts, each with an fp32
+    # accumulator; with 512 or 256 columns dx is its own accumulator: bf16
+    # holds the fp32 values' high halves, fp32 the values themselves)
     if slab:
         monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", slab)
     inp = inputs(name)
