@@ -404,7 +404,14 @@ flce_status flce_timing_read(int64_t index, const char** kernel, float* ms);
 flce_status flce_timing_clear(void);
 
 /* Vocabulary slab width (columns of dlogits held at once) the backward uses
- * for this problem; pure host arithmetic.  Returns 0 on invalid arguments. */
+ * for this problem; pure host arithmetic.  Returns 0 on invalid arguments.
+ * The environment variable FLCE_SLAB_COLS, a positive multiple of 256 (other
+ * values are ignored), overrides the automatic width (capped at V rounded up
+ * to 256): narrower slabs take less workspace and keep buffer, and more
+ * recompute launches.  At N=8192, H=4096, V=128256, 8192 columns hold all
+ * extra memory under 10% of the bf16 logits (206.8 MB with the first slab
+ * kept) for about 3% more time per step.  It is read on every call, so it must
+ * not change between a workspace query and the calls that use its answer. */
 int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, flce_dtype dtype);
 
 #ifdef __cplusplus

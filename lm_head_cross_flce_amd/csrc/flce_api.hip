@@ -59,14 +59,16 @@ flce_status check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
 // as more of the slab is still cached when dx and dW read it).  (b) gives the
 // Llama-3-sized head (N=8192, H=4096, V=128256) 16384 columns, with all extra
 // memory at 9.7% of its fp32 logits.
-// FLCE_DEBUG_SLAB_COLS (a positive multiple of 256) overrides it; the tests
-// use it to force many slabs.
+// FLCE_SLAB_COLS (a positive multiple of 256; the caller's memory knob) or
+// else FLCE_DEBUG_SLAB_COLS (the tests force many slabs with it) overrides it.
 int64_t slab_cols(int64_t N, int64_t H, int64_t V, int dtype) {
   const int64_t es = dtype == FLCE_F32 ? 4 : 2;
   const int64_t vmax = cdiv(V, kTile) * kTile;
-  if (const char* env = std::getenv("FLCE_DEBUG_SLAB_COLS")) {
-    const long long c = std::atoll(env);
-    if (c > 0 && c % kTile == 0) return c < vmax ? c : vmax;
+  for (const char* name : {"FLCE_SLAB_COLS", "FLCE_DEBUG_SLAB_COLS"}) {
+    if (const char* env = std::getenv(name)) {
+      const long long c = std::atoll(env);
+      if (c > 0 && c % kTile == 0) return c < vmax ? c : vmax;
+    }
   }
   const int64_t th = cdiv(H, kTile);
   const bool small_acc = (size_t)N * (size_t)H * 4 < (size_t(128) << 20);

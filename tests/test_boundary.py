@@ -133,6 +133,21 @@ def test_slab_width_heuristic(lib):
     assert _lib.flce_backward_slab_cols(64, 12, 1000, 0) == 0         # H % 8 != 0
 
 
+def test_slab_cols_knob_trades_memory(lib, monkeypatch):
+    # FLCE_SLAB_COLS narrows the slabs; 8192 columns keep the Llama-3-sized head's
+    # extra memory (kept slab) under 10% of its bf16 logits
+    monkeypatch.delenv("FLCE_DEBUG_SLAB_COLS", raising=False)
+    base = sum(_lib.flce_keep_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 2))
+    monkeypatch.setenv("FLCE_SLAB_COLS", "8192")
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
+    narrow = sum(_lib.flce_keep_workspace_size(8192, 4096, 128256, _lib.FLCE_BF16, True, 2))
+    assert narrow < 0.1 * 8192 * 128256 * 2 < base
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")   # the documented knob wins
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 8192
+    monkeypatch.setenv("FLCE_SLAB_COLS", "1000")          # not a multiple of 256: ignored
+    assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 512
+
+
 def test_slab_debug_override(lib, monkeypatch):
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
     assert _lib.flce_backward_slab_cols(8192, 4096, 128256, 1) == 512
