@@ -49,6 +49,12 @@ CASES = {
     # H not a multiple of 8: the binding pads x and W with zero columns
     "bf16_h100": _case("n8192_h4096_v128256", "bf16_h100", N=130, H=100, V=700, n_ignored=5, seed=14),
     "f32_h13": _case("tiny_f32", "f32_h13", N=40, H=13, V=300, seed=15),
+    # extreme aspect ratios: a million-row vocabulary (3907 vocabulary tiles over 256 phases of one token tile),
+    # a hidden size past 8192 that is no multiple of the 64-deep K block or the 256-wide output tile, and
+    # 20000 tokens (79 token tiles, the last 32 rows) against a tiny head
+    "bf16_v1m": _case("n8192_h4096_v128256", "bf16_v1m", N=64, H=64, V=1_000_003, n_ignored=2, seed=16),
+    "bf16_h8200": _case("n8192_h4096_v128256", "bf16_h8200", N=300, H=8200, V=1500, n_ignored=4, seed=17),
+    "bf16_n20000": _case("n8192_h4096_v128256", "bf16_n20000", N=20000, H=64, V=700, n_ignored=100, seed=18),
 }
 
 _oracle_cache = {}
