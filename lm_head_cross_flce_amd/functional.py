@@ -390,8 +390,9 @@ def flce_shard_backward(x: torch.Tensor, W_shard: torch.Tensor, b_shard: Optiona
     if g.numel() != (N if reduction == "none" else 1):
         raise ValueError("grad_loss must have N entries for none and one otherwise")
     if dx_partial is not None:
-        if dx_partial.shape != (N, H) or dx_partial.dtype != torch.float32 or not dx_partial.is_contiguous():
-            raise ValueError("dx_partial must be a contiguous float32 [N, H] tensor")
+        if (dx_partial.shape != (N, H) or dx_partial.dtype != torch.float32 or not dx_partial.is_contiguous()
+                or dx_partial.device != dev):
+            raise ValueError(f"dx_partial must be a contiguous float32 [N, H] tensor on {dev}")
     elif need_dx:
         if accumulate_dx:
             raise ValueError("accumulate_dx needs dx_partial")
