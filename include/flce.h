@@ -410,8 +410,11 @@ flce_status flce_timing_clear(void);
  * to 256): narrower slabs take less workspace and keep buffer, and more
  * recompute launches.  At N=8192, H=4096, V=128256, 8192 columns hold all
  * extra memory under 10% of the bf16 logits (206.8 MB with the first slab
- * kept) for about 3% more time per step.  It is read on every call, so it must
- * not change between a workspace query and the calls that use its answer. */
+ * kept) for about 3% more time per step.  Below 256 x 256 / ceil(H / 256)
+ * columns a slab's dW product has fewer output tiles than the GPU's 256 CUs:
+ * at N=16384, H=1024, V=256000, 8192 columns cost 17%.  It is read on every
+ * call, so it must not change between a workspace query and the calls that
+ * use its answer. */
 int64_t flce_backward_slab_cols(int64_t N, int64_t H, int64_t V, flce_dtype dtype);
 
 #ifdef __cplusplus
