@@ -650,7 +650,7 @@ def main():
         del x, W, b, dx, dW, db
         ws_f = ws_b = kbuf = None
         torch.cuda.empty_cache()
-        rows = args.cpu_rows or max(8, min(N, int(1.0e13 // (8.0 * H * V))))
+        rows = args.cpu_rows or max(8, min(N, int(1.8e13 // (8.0 * H * V))))   # ~15 s on 16 host threads
         print(f"[bench] cpu oracle on {rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, rows)
     print(json.dumps(out), flush=True)
