@@ -55,6 +55,9 @@ CASES = {
     "bf16_v1m": _case("n8192_h4096_v128256", "bf16_v1m", N=64, H=64, V=1_000_003, n_ignored=2, seed=16),
     "bf16_h8200": _case("n8192_h4096_v128256", "bf16_h8200", N=300, H=8200, V=1500, n_ignored=4, seed=17),
     "bf16_n20000": _case("n8192_h4096_v128256", "bf16_n20000", N=20000, H=64, V=700, n_ignored=100, seed=18),
+    # fp32 inputs over several ragged tiles in every dimension (6 x 3 x 20), with bias, smoothing and z-loss
+    "f32_mid": _case("tiny_f32", "f32_mid", N=1300, H=520, V=5003, n_ignored=40, label_smoothing=0.1,
+                     z_loss_scale=1e-4, seed=19),
 }
 
 _oracle_cache = {}
