@@ -969,6 +969,34 @@ hipError_t launch_bwd_prepare(const BwdLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The dx product of one slab.  K split: each part takes kc slab columns (a
+// multiple of the 64-deep copy block).  A split accumulator (several slabs,
+// one part) runs the First, Accum and Last modes only; false for any other.
+template <class T>
+static bool launch_dx(const BwdLaunch& a, int vs, int width, int wpad, int TH, int dx_mode, hipStream_t st) {
+  const int parts = a.dx_split > 1 ? a.dx_split : 1;
+  const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
+  const dim3 gdx(TH * a.NT * parts), blk(kThreads);
+  const bool acc = a.accumulate != 0;
+  if constexpr (sizeof(T) == 2) {
+    if (a.split_acc) {
+      if (dx_mode == kDxFirst && acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, true, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+      else if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+      else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+      else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+      else return false;
+      return true;
+    }
+  }
+  if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  else if (dx_mode == kDxLast && !acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  else if (!acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  else FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
+  return true;
+}
+
 template <class T>
 static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int dx_mode, bool want_db,
                                     bool dz_ready, hipStream_t st) {
@@ -987,31 +1015,7 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   } else {
     FLCE_LAUNCH((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
   }
-  if (a.dx) {
-    // K split: each part takes kc slab columns (a multiple of the 64-deep copy block).
-    const int parts = a.dx_split > 1 ? a.dx_split : 1;
-    const int kc = parts > 1 ? (((wpad + parts - 1) / parts + 63) / 64) * 64 : wpad;
-    const dim3 gdx(TH * a.NT * parts);
-    const bool acc = a.accumulate != 0;
-    bool done = false;
-    if constexpr (sizeof(T) == 2) {
-      if (a.split_acc) {
-        done = true;
-        if (dx_mode == kDxFirst && acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, true, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-        else if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-        else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-        else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-        else return hipErrorInvalidValue;   // one slab needs no accumulator
-      }
-    }
-    if (done) {
-    } else if (dx_mode == kDxFirst) FLCE_LAUNCH((bwd_dx_kernel<T, kDxFirst, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxAccum) FLCE_LAUNCH((bwd_dx_kernel<T, kDxAccum, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxLast && !acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (dx_mode == kDxLast) FLCE_LAUNCH((bwd_dx_kernel<T, kDxLast, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else if (!acc) FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, false>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-    else FLCE_LAUNCH((bwd_dx_kernel<T, kDxOnly, true>), gdx, blk, 0, st, a, vs, width, wpad, TH, kc);
-  }
+  if (a.dx && !launch_dx<T>(a, vs, width, wpad, TH, dx_mode, st)) return hipErrorInvalidValue;
   if (a.dW && a.accumulate) FLCE_LAUNCH((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
   else if (a.dW) FLCE_LAUNCH((bwd_dw_kernel<T, false>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
   else if (want_db) FLCE_LAUNCH((bwd_db_kernel<T>), dim3(TV), blk, 0, st, a, vs, width);
