@@ -82,6 +82,17 @@ def test_keep_forced_small_slabs(monkeypatch, cols):
         check_keep(CASES[name], got, f, bw)
 
 
+def test_slab_cols_knob(monkeypatch):
+    # The documented FLCE_SLAB_COLS narrows the slabs for both calls and the
+    # workspace queries the binding makes: 256 columns give c3_small nine slabs,
+    # the kept slab and dx accumulated in place over the other eight.
+    monkeypatch.setenv("FLCE_SLAB_COLS", "256")
+    print("[gpu] FLCE_SLAB_COLS=256 keep", flush=True)
+    got = run_keep(inputs("c3_small"))
+    f, bw = oracle("c3_small")
+    check_keep(CASES["c3_small"], got, f, bw)
+
+
 @pytest.mark.parametrize("red", ["none", "sum", "mean"])
 def test_keep_all_reductions(red, monkeypatch):
     monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
