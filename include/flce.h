@@ -112,8 +112,10 @@ typedef FLCE_ENUM(flce_dtype) {
  * O(N/256 * V) fp32 scratch (and, for fp16, 256 bytes for the slab's scale),
  * and what dx accumulates in over the slabs.  dx sums in fp32: with several
  * slabs, fp32 inputs accumulate in dx itself, and 16-bit inputs keep each
- * fp32 value's high 16 bits in dx (so dx holds no result until the call
- * ends) and its low 16 bits in an [N, H] 16-bit workspace array; one slab
+ * fp32 value's high 16 bits in dx (so dx holds no result until the call's
+ * launches complete, and its contents are unspecified after an error return,
+ * old values included when accumulating) and its low 16 bits in an [N, H]
+ * 16-bit workspace array; one slab
  * needs neither.  When the dx product has too few 256 x 256 output tiles to
  * fill the GPU (at most half of its 256 CUs), each slab's columns are split
  * into P <= 8 parts instead, each with its own fp32 [N, H] accumulator in the
