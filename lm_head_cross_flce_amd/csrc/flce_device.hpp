@@ -223,6 +223,14 @@ __device__ __forceinline__ f32x4 acc_read4(const f32x4& blk) {
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[3]) : "a"(blk[3]));
   return z;
 }
+// Value R of one block's accumulators (an epilogue that walks output rows
+// takes one value from each of eight blocks at a time).
+template <int R>
+__device__ __forceinline__ float acc_read1(const f32x4& blk) {
+  float z;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z) : "a"(blk[R]));
+  return z;
+}
 
 // ---------------------------------------------------------------------------
 // fp32 operands: register-staged copies and v_mfma_f32_16x16x4_f32
@@ -426,15 +434,24 @@ __device__ __forceinline__ constexpr int tile_row_perm(int t) {
   return (t & 0xE3) | ((t & 0x0C) << 1) | ((t & 0x10) >> 2);
 }
 
+// Tile row t of an operand copied with permuted columns holds global row
+// m0 + tile_col_perm(t): within each half of 128 rows, row 16 j + c (the
+// MFMA output column c of block j) holds row 8 c + j, so a lane's values in
+// the eight blocks of one output row are eight consecutive global rows.
+__device__ __forceinline__ constexpr int tile_col_perm(int t) {
+  return (t & 0x80) | ((t & 0x0F) << 3) | ((t & 0x70) >> 4);
+}
+
 // K-contiguous: instruction idx fills rows 8 idx .. 8 idx + 7; lane l takes
 // row 8 idx + l / 8 and LDS chunk l % 8, which holds global chunk
-// (l % 8) ^ (l / 8).  PERM: tile rows hold permuted global rows.
+// (l % 8) ^ (l / 8).  perm: tile rows hold permuted global rows, 1 by
+// tile_row_perm, 2 by tile_col_perm.
 template <> struct Dma<true> {
   uint32_t off[8];
   const uint16_t* base;
   int wave;
   template <class E>
-  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, bool perm = false) {
+  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, int perm = 0) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = (const uint16_t*)o.p + (int64_t)m0 * o.ld;
@@ -442,7 +459,7 @@ template <> struct Dma<true> {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int t = 8 * (4 * q + wave) + (lane >> 3);
-      const int row = perm ? tile_row_perm(t) : t;
+      const int row = perm == 1 ? tile_row_perm(t) : perm == 2 ? tile_col_perm(t) : t;
       off[q] = (m0 + row < o.mext) ? (uint32_t)(((int64_t)row * o.ld + 8 * c) * 2) : kOOB;
     }
   }
@@ -461,7 +478,7 @@ template <> struct Dma<false> {
   int64_t ld;
   int wave;
   template <class E>
-  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, bool = false) {
+  __device__ __forceinline__ void init(const Opnd<E>& o, int m0, int tid, int = 0) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     base = (const uint16_t*)o.p + m0;
@@ -643,16 +660,17 @@ __device__ __forceinline__ void stage_last_half(Acc& acc, const Frag& P) {
 // block into buffer 0; it may run while the previous tile's epilogue is still
 // working, as long as every wave has finished that tile's mainloop (whose
 // last barrier follows its last fragment read and the completion of its
-// copies).  perm_a: A's tile rows hold permuted rows (tile_row_perm; A must
-// be K-contiguous).
+// copies).  perm_a: A's tile rows hold permuted rows (tile_row_perm); perm_b:
+// B's hold permuted columns (tile_col_perm).  A permuted operand must be
+// K-contiguous.
 template <bool AK, bool BK> struct TileCopy {
   Dma<AK> da;
   Dma<BK> db;
   template <class E>
   __device__ __forceinline__ void start(const Opnd<E>& A, int m0, const Opnd<E>& B, int n0,
-                                        const Lds& L, int tid, bool perm_a = false) {
-    da.init(A, m0, tid, perm_a);
-    db.init(B, n0, tid);
+                                        const Lds& L, int tid, bool perm_a = false, bool perm_b = false) {
+    da.init(A, m0, tid, perm_a ? 1 : 0);
+    db.init(B, n0, tid, perm_b ? 2 : 0);
     const int lane = tid & 63;
     // Copies past K read zeros (out-of-range offsets), so the stage bodies
     // need no branches.

@@ -636,6 +636,109 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   }
 }
 
+// One tile of the recompute kernel for 16-bit inputs, with the product's
+// operands the other way round: rows are tokens (A = x) and columns are
+// vocabulary rows (B = W, copied with permuted columns, tile_col_perm), so a
+// lane holds, for each of its 32 tokens (blocks i, rows r), eight consecutive
+// vocabulary rows 8 c .. 8 c + 7 of its wave's half (c = lane % 16) across
+// the blocks j.  One 16-byte store then covers those rows of one token, and a
+// wave instruction writes 4 tokens x 256 bytes (whole lines) instead of 16
+// tokens x 64 bytes.  Used without db partials only (no bias, or db not
+// requested): with them (in rs[8] over the lane's 32 tokens) the compiler
+// spilled about 50 VGPRs and the launch ran 8% slower at N=8192, H=4096,
+// V=128256.  Without them the recompute runs 0.7-1.9% faster than dz_tile's
+// at N=16384, H=1024, V=256000 and N=4096, H=2048, V=32000 (same-box A/Bs,
+// bit-identical dlogits).
+template <class T, bool BIAS, int EXTRA>
+__device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
+                                          const Lds& L, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
+                                          int tid) {
+  static_assert(sizeof(T) == 2, "16-bit inputs");
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const Opnd<T> A{(const T*)a.x, a.H, a.N, a.H};
+  const Opnd<T> B{(const T*)a.W, a.H, a.V, a.H};
+  const int g = lane >> 4, c = lane & 15;
+  int tm, tn;
+  tile_coords(t, G, TM, a.NT, tm, tn);
+  const int v0 = vs + tm * kTile, n0 = tn * kTile;
+  TokenTile tt;
+  tt.fetch(a, n0, tid);
+  BiasTile<T> bt;
+  if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
+  Acc acc;
+  gemm_tile_bf16_run<true, true, EXTRA, true>(acc, A, B, a.H, L, tid, tc);
+  const int tnext = t + gridDim.x;
+  if (tnext < G) {
+    int tm2, tn2;
+    tile_coords(tnext, G, TM, a.NT, tm2, tn2);
+    tc.start(A, tn2 * kTile, B, vs + tm2 * kTile, L, tid, false, true);
+  }
+  tt.publish(ltok, lyv, tid);
+  if (BIAS) bt.publish(L.bias, tid);
+  lds_barrier();
+  acc_drain();
+  const int vleft = a.V - v0;
+  const bool ragged = vleft < kTile;   // wave-uniform
+  const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
+  const float sl2e = a.logit_scale * kLog2e;
+  const int vl0 = wn * kWaveTile + 8 * c;   // this lane's vocabulary rows vl0 .. vl0 + 7 (tile-relative)
+  // Store offset of token row lane_row + tr: the lane's part in the vector
+  // offset, the row's (16 i + r, the same for every lane) in the scalar one.
+  // The slab is at most 1 GiB, so rows before N stay below 2^30 bytes; rows
+  // at or past N take kOOB (dropped) and a scalar offset of 0.
+  const uint32_t rowbytes = (uint32_t)(a.ldS * (int64_t)sizeof(T));
+  const int lane_row = wm * kWaveTile + 4 * g;
+  const int rows_left = a.N - n0;
+  const uint32_t vbase = (uint32_t)lane_row * rowbytes + (uint32_t)((v0 - vs + vl0) * (int)sizeof(T));
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+  if (BIAS) {
+    b0 = read_bias4(L.bias, vl0);
+    b1 = read_bias4(L.bias, vl0 + 4);
+  }
+  auto row_dz = [&](int i, auto rr, float (&dz)[8], const f32x4& cf) {
+    constexpr int R = decltype(rr)::value;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float bj = j < 4 ? b0[j] : b1[j - 4];
+      const float z = acc_read1<R>(acc[i][j]);
+      const float av = BIAS ? z + bj : z;
+      dz[j] = fmaf(cf[0], fast_exp2(fmaf(av, sl2e, -cf[3])), -cf[1]);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nl = wm * kWaveTile + 16 * i + 4 * g + r;   // token within the tile
+      const f32x4 cf = ltok[nl];
+      const int y = lyv[nl];
+      float dz[8];
+      if (r == 0) row_dz(i, std::integral_constant<int, 0>{}, dz, cf);
+      else if (r == 1) row_dz(i, std::integral_constant<int, 1>{}, dz, cf);
+      else if (r == 2) row_dz(i, std::integral_constant<int, 2>{}, dz, cf);
+      else row_dz(i, std::integral_constant<int, 3>{}, dz, cf);
+      const int tg = y - (v0 + vl0);
+      if (__ballot((unsigned)tg < 8u)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (tg == k) dz[k] -= cf[2];
+      }
+      if (ragged) {
+        const int lim = vleft - vl0;   // rows of this lane inside the vocabulary
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k >= lim) dz[k] = 0.f;
+      }
+      const int tr = 16 * i + r;
+      const uint32_t voff = lane_row + tr < rows_left ? vbase : kOOB;
+      const int soff = tr < rows_left ? (int)((uint32_t)tr * rowbytes) : 0;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]), pack2<T>(dz[6], dz[7])},
+          rslab, voff, soff, kSlabPolicy);
+    }
+  }
+}
+
 // Persistent over the slab's tiles (TM vocabulary tiles x NT token tiles): a
 // workgroup takes logical tiles blockIdx.x, + gridDim.x, ..., so the tiles in
 // flight together are the ones a one-tile-per-workgroup launch would run
@@ -653,7 +756,14 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   const int G = TM * a.NT;
   TileCopy<true, true> tc;
   int t = blockIdx.x;
-  if constexpr (sizeof(T) == 2) {
+  constexpr bool kTransposed = sizeof(T) == 2 && !DB;   // dz_tile_t: x rows, W columns
+  if constexpr (kTransposed) {
+    const Opnd<T> A{(const T*)a.x, a.H, a.N, a.H};
+    const Opnd<T> B{(const T*)a.W, a.H, a.V, a.H};
+    int tm, tn;
+    tile_coords(t, G, TM, a.NT, tm, tn);
+    tc.start(A, tn * kTile, B, vs + tm * kTile, L, tid, false, true);
+  } else if constexpr (sizeof(T) == 2) {
     const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
     const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
     int tm, tn;
@@ -667,9 +777,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   constexpr int kStoresVm = 32;
   lds_f32x4* ltok = (lds_f32x4*)tok_s;
   __attribute__((address_space(3))) int* lyv = (__attribute__((address_space(3))) int*)yv_s;
-  dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
-  for (t += gridDim.x; t < G; t += gridDim.x)
-    dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+  if constexpr (kTransposed) {
+    dz_tile_t<T, BIAS, kLoadsVm>(a, vs, TM, G, t, tc, L, ltok, lyv, tid);
+    for (t += gridDim.x; t < G; t += gridDim.x)
+      dz_tile_t<T, BIAS, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, ltok, lyv, tid);
+  } else {
+    dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+    for (t += gridDim.x; t < G; t += gridDim.x)
+      dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+  }
 }
 
 // db[vs + c] = sum over token tiles of the slab's db partials (fixed order),
