@@ -469,9 +469,8 @@ struct TokenTile {
   }
 };
 
-// One tile of the recompute kernel.  EXTRA: the vector-memory instructions
-// every wave has issued since this tile's copies started (see
-// gemm_tile_bf16_run).  bf16 tiles copy W with permuted rows
+// First tile row of lane group g's four rows in MFMA block i, W's rows
+// being the tile rows.  16-bit tiles copy W with permuted rows
 // (tile_row_perm), so a lane's values in blocks 2s and 2s + 1 of a token
 // column are eight consecutive vocabulary rows; fp32 tiles keep the MFMA row
 // order (two runs of four rows, 16 apart).
@@ -480,10 +479,14 @@ __device__ __forceinline__ constexpr int dz_row(int i, int g) {
   return sizeof(T) == 2 ? 32 * (i >> 1) + 8 * g + 4 * (i & 1) : 16 * i + 4 * g;
 }
 
+// One tile of the recompute kernel for fp32 inputs, W's rows as the tile
+// rows.  EXTRA is unused: fp32 tiles copy through registers.
+
 template <class T, bool BIAS, bool DB, int EXTRA>
 __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
                                         const Lds& L, lds_f32* red, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
                                         int tid) {
+  static_assert(sizeof(T) == 4, "16-bit inputs use dz_tile_t");
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
   const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
@@ -496,17 +499,8 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   BiasTile<T> bt;
   if (BIAS) bt.fetch((const T*)a.b, a.V, v0, tid);
   Acc acc;
-  if constexpr (sizeof(T) == 2) {
-    gemm_tile_bf16_run<true, true, EXTRA>(acc, A, B, a.H, L, tid, tc);
-    const int tnext = t + gridDim.x;
-    if (tnext < G) {
-      int tm2, tn2;
-      tile_coords(tnext, G, TM, a.NT, tm2, tn2);
-      tc.start(A, vs + tm2 * kTile, B, tn2 * kTile, L, tid, true);
-    }
-  } else {
-    gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
-  }
+  (void)tc;
+  gemm_tile<T, true, true>(acc, A, v0, B, n0, a.H, L, tid);
   tt.publish(ltok, lyv, tid);
   if (BIAS) bt.publish(L.bias, tid);
   lds_barrier();
@@ -519,8 +513,6 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // times W's zero rows would give NaN.  Only the vocabulary's last tile is
   // ragged (vleft < 256), so the mask is a wave-uniform branch.
   const int vleft = a.V - v0;
-  // Slab rows of this tile's tokens, from token n0 on.
-  const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
   const float sl2e = a.logit_scale * kLog2e;   // p = 2^((scale (z + b)) log2 e - lse log2 e)
   // Bands s of 32 wave rows (blocks 2s, 2s + 1), token blocks j within them:
   // dlogits of the lane's token (16 j + l % 16) at its rows r0 .. r0 + 3 and
@@ -529,19 +521,9 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // done, so few stay live.
   float dbs[4];
   const bool ragged = vleft < kTile;   // wave-uniform
-  // Byte offset of each of this lane's token rows in the slab, kOOB past N
-  // (a column offset below 2^31 added to kOOB stays out of range, so stores
-  // past N are dropped without a select).
-  uint32_t rowoff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int nl = wn * kWaveTile + 16 * j + (lane & 15);
-    rowoff[j] = n0 + nl < a.N ? (uint32_t)((int64_t)nl * a.ldS * (int64_t)sizeof(T)) : kOOB;
-  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r0 = wm * kWaveTile + dz_row<T>(2 * s, g), r1 = wm * kWaveTile + dz_row<T>(2 * s + 1, g);
-    const uint32_t coff = (uint32_t)((v0 - vs + r0) * (int)sizeof(T));
     const f32x4 bias0 = BIAS ? read_bias4(L.bias, r0) : f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 bias1 = BIAS ? read_bias4(L.bias, r1) : f32x4{0.f, 0.f, 0.f, 0.f};
     float rs[8];
@@ -564,15 +546,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
         dz[r] = fmaf(cf[0], fast_exp2(fmaf(a0, sl2e, -cf[3])), -cf[1]);
         dz[4 + r] = fmaf(cf[0], fast_exp2(fmaf(a1, sl2e, -cf[3])), -cf[1]);
       }
-      if constexpr (sizeof(T) == 2) {
-        // r1 = r0 + 4: the lane's rows are r0 .. r0 + 7.
-        const int t = y - (v0 + r0);
-        if (__ballot((unsigned)t < 8u)) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (t == k) dz[k] -= cf[2];
-        }
-      } else {
+      {
         const int t0 = y - (v0 + r0), t1 = y - (v0 + r1);
         if (__ballot((unsigned)t0 < 4u || (unsigned)t1 < 4u)) {
 #pragma unroll
@@ -594,20 +568,10 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
 #pragma unroll
         for (int e = 0; e < 8; ++e) rs[e] += dz[e];
       }
-      if constexpr (sizeof(T) == 2) {
-        // Sixteen contiguous bytes; a wave instruction writes 16 tokens x 64
-        // bytes.
-        const uint32_t off = rowoff[j] + coff;
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]),
-                  pack2<T>(dz[6], dz[7])},
-            rslab, off, 0, kSlabPolicy);
-      } else {
-        if (n0 + nl < a.N) {
-          T* row = (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs);
-          store4<T>(row + r0, dz[0], dz[1], dz[2], dz[3]);
-          store4<T>(row + r1, dz[4], dz[5], dz[6], dz[7]);
-        }
+      if (n0 + nl < a.N) {
+        T* row = (T*)a.slab + (int64_t)(n0 + nl) * a.ldS + (v0 - vs);
+        store4<T>(row + r0, dz[0], dz[1], dz[2], dz[3]);
+        store4<T>(row + r1, dz[4], dz[5], dz[6], dz[7]);
       }
     }
     if (DB) dbs[s] = group_sum8(rs, lane);
@@ -637,22 +601,24 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
 }
 
 // One tile of the recompute kernel for 16-bit inputs, with the product's
-// operands the other way round: rows are tokens (A = x) and columns are
-// vocabulary rows (B = W, copied with permuted columns, tile_col_perm), so a
-// lane holds, for each of its 32 tokens (blocks i, rows r), eight consecutive
-// vocabulary rows 8 c .. 8 c + 7 of its wave's half (c = lane % 16) across
-// the blocks j.  One 16-byte store then covers those rows of one token, and a
-// wave instruction writes 4 tokens x 256 bytes (whole lines) instead of 16
-// tokens x 64 bytes.  Used without db partials only (no bias, or db not
-// requested): with them (in rs[8] over the lane's 32 tokens) the compiler
-// spilled about 50 VGPRs and the launch ran 8% slower at N=8192, H=4096,
-// V=128256.  Without them the recompute runs 0.7-1.9% faster than dz_tile's
-// at N=16384, H=1024, V=256000 and N=4096, H=2048, V=32000 (same-box A/Bs,
-// bit-identical dlogits).
-template <class T, bool BIAS, int EXTRA>
+// operands the other way round from the forward's: rows are tokens (A = x)
+// and columns vocabulary rows (B = W, copied with permuted columns,
+// tile_col_perm), so a lane holds, for each of its 32 tokens (blocks i, rows
+// r), eight consecutive vocabulary rows 8 c .. 8 c + 7 of its wave's half
+// (c = lane % 16) across the blocks j.  One 16-byte store then covers those
+// rows of one token, and a wave instruction writes 4 tokens x 256 bytes
+// (whole lines) instead of 16 tokens x 64 bytes.  The db row sums accumulate
+// over the lane's tokens in fixed-order adds (as plain += the compiler
+// restructured them and spilled about 50 VGPRs) and are reduced once per
+// tile.  Same-box A/Bs against the forward's orientation: recompute -1.9%
+// without db partials (N=8192, H=4096, V=128256, first slab kept), -0.7% to
+// -1.9% at N=16384, H=1024 and N=4096, H=2048; with them (the same shapes
+// with a bias) -1.3% to -1.6%, and -2.1% at N=32768, H=2048, V=128000;
+// bit-identical dlogits.
+template <class T, bool BIAS, bool DB, int EXTRA>
 __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
-                                          const Lds& L, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
-                                          int tid) {
+                                          const Lds& L, lds_f32* red, lds_f32x4* ltok,
+                                          __attribute__((address_space(3))) int* lyv, int tid) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const Opnd<T> A{(const T*)a.x, a.H, a.N, a.H};
@@ -695,6 +661,9 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
     b0 = read_bias4(L.bias, vl0);
     b1 = read_bias4(L.bias, vl0 + 4);
   }
+  float rs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rs[j] = 0.f;
   auto row_dz = [&](int i, auto rr, float (&dz)[8], const f32x4& cf) {
     constexpr int R = decltype(rr)::value;
 #pragma unroll
@@ -729,12 +698,44 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
         for (int k = 0; k < 8; ++k)
           if (k >= lim) dz[k] = 0.f;
       }
+      if (DB) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("v_add_f32 %0, %0, %1" : "+v"(rs[k]) : "v"(dz[k]));
+      }
       const int tr = 16 * i + r;
       const uint32_t voff = lane_row + tr < rows_left ? vbase : kOOB;
       const int soff = tr < rows_left ? (int)((uint32_t)tr * rowbytes) : 0;
       __builtin_amdgcn_raw_buffer_store_b128(
           u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]), pack2<T>(dz[6], dz[7])},
           rslab, voff, soff, kSlabPolicy);
+
+    }
+  }
+  if (DB) {
+    // Lanes c, c + 16, c + 32, c + 48 hold the same rows; then the two waves
+    // sharing rows (wm = 0, 1) add through LDS.  The next tile's mainloop
+    // barriers keep this tile's reads of red ahead of the next tile's writes.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rs[k] += __shfl_xor(rs[k], 16);
+      rs[k] += __shfl_xor(rs[k], 32);
+    }
+    if (wm == 1 && g == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) red[vl0 + k] = rs[k];
+    }
+    lds_barrier();
+    // Columns past V (inside the slab's padded width) get exact zeros, which
+    // the db sums never read.
+    if (wm == 0 && g == 0) {
+      const __amdgpu_buffer_rsrc_t rdb = make_rsrc(a.dbp + (int64_t)tn * a.ldS + (v0 - vs));
+      const f32x4 r0 = read_bias4(red, vl0), r1 = read_bias4(red, vl0 + 4);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, f32x4{rs[0] + r0[0], rs[1] + r0[1], rs[2] + r0[2], rs[3] + r0[3]}), rdb,
+          (uint32_t)vl0 * 4u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, f32x4{rs[4] + r1[0], rs[5] + r1[1], rs[6] + r1[2], rs[7] + r1[3]}), rdb,
+          (uint32_t)(vl0 + 4) * 4u, 0, 0);
     }
   }
 }
@@ -756,19 +757,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   const int G = TM * a.NT;
   TileCopy<true, true> tc;
   int t = blockIdx.x;
-  constexpr bool kTransposed = sizeof(T) == 2 && !DB;   // dz_tile_t: x rows, W columns
-  if constexpr (kTransposed) {
+  if constexpr (sizeof(T) == 2) {   // dz_tile_t: x rows, W columns (permuted)
     const Opnd<T> A{(const T*)a.x, a.H, a.N, a.H};
     const Opnd<T> B{(const T*)a.W, a.H, a.V, a.H};
     int tm, tn;
     tile_coords(t, G, TM, a.NT, tm, tn);
     tc.start(A, tn * kTile, B, vs + tm * kTile, L, tid, false, true);
-  } else if constexpr (sizeof(T) == 2) {
-    const Opnd<T> A{(const T*)a.W, a.H, a.V, a.H};
-    const Opnd<T> B{(const T*)a.x, a.H, a.N, a.H};
-    int tm, tn;
-    tile_coords(t, G, TM, a.NT, tm, tn);
-    tc.start(A, vs + tm * kTile, B, tn * kTile, L, tid, true);
   }
   // Vector-memory instructions every wave issues between starting a tile's
   // copies and its mainloop: the per-token loads (2) and the bias fetch, plus,
@@ -777,10 +771,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   constexpr int kStoresVm = 32;
   lds_f32x4* ltok = (lds_f32x4*)tok_s;
   __attribute__((address_space(3))) int* lyv = (__attribute__((address_space(3))) int*)yv_s;
-  if constexpr (kTransposed) {
-    dz_tile_t<T, BIAS, kLoadsVm>(a, vs, TM, G, t, tc, L, ltok, lyv, tid);
+  if constexpr (sizeof(T) == 2) {
+    dz_tile_t<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
     for (t += gridDim.x; t < G; t += gridDim.x)
-      dz_tile_t<T, BIAS, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, ltok, lyv, tid);
+      dz_tile_t<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
   } else {
     dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
     for (t += gridDim.x; t < G; t += gridDim.x)
