@@ -482,7 +482,7 @@ __device__ __forceinline__ constexpr int dz_row(int i, int g) {
 // One tile of the recompute kernel for fp32 inputs, W's rows as the tile
 // rows.  EXTRA is unused: fp32 tiles copy through registers.
 
-template <class T, bool BIAS, bool DB, int EXTRA>
+template <class T, bool BIAS, bool DB, bool RAGGED, int EXTRA>
 __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
                                         const Lds& L, lds_f32* red, lds_f32x4* ltok, __attribute__((address_space(3))) int* lyv,
                                         int tid) {
@@ -520,7 +520,7 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
   // A band's row sums are reduced over the lane group as soon as the band is
   // done, so few stay live.
   float dbs[4];
-  const bool ragged = vleft < kTile;   // wave-uniform
+  const bool ragged = RAGGED && vleft < kTile;   // wave-uniform
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int r0 = wm * kWaveTile + dz_row<T>(2 * s, g), r1 = wm * kWaveTile + dz_row<T>(2 * s + 1, g);
@@ -615,7 +615,13 @@ __device__ __forceinline__ void dz_tile(const BwdLaunch& a, int vs, int TM, int 
 // -1.9% at N=16384, H=1024 and N=4096, H=2048; with them (the same shapes
 // with a bias) -1.3% to -1.6%, and -2.1% at N=32768, H=2048, V=128000;
 // bit-identical dlogits.
-template <class T, bool BIAS, bool DB, int EXTRA>
+//
+// RAGGED: the launch holds a partial vocabulary tile (the slab's width not a
+// multiple of 256) or partial token tiles (N not a multiple of 256).  Without
+// it every tile is whole and the row masks and token checks compile away: the
+// compiler hoisted the mask's eight compares per token row out of their
+// wave-uniform branch, one VALU operation per dlogit in every tile.
+template <class T, bool BIAS, bool DB, bool RAGGED, int EXTRA>
 __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, int G, int t, TileCopy<true, true>& tc,
                                           const Lds& L, lds_f32* red, lds_f32x4* ltok,
                                           __attribute__((address_space(3))) int* lyv, int tid) {
@@ -644,7 +650,7 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
   lds_barrier();
   acc_drain();
   const int vleft = a.V - v0;
-  const bool ragged = vleft < kTile;   // wave-uniform
+  const bool ragged = RAGGED && vleft < kTile;   // wave-uniform
   const __amdgpu_buffer_rsrc_t rslab = make_rsrc((const T*)a.slab + (int64_t)n0 * a.ldS);
   const float sl2e = a.logit_scale * kLog2e;
   const int vl0 = wn * kWaveTile + 8 * c;   // this lane's vocabulary rows vl0 .. vl0 + 7 (tile-relative)
@@ -703,8 +709,8 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
         for (int k = 0; k < 8; ++k) asm volatile("v_add_f32 %0, %0, %1" : "+v"(rs[k]) : "v"(dz[k]));
       }
       const int tr = 16 * i + r;
-      const uint32_t voff = lane_row + tr < rows_left ? vbase : kOOB;
-      const int soff = tr < rows_left ? (int)((uint32_t)tr * rowbytes) : 0;
+      const uint32_t voff = !RAGGED || lane_row + tr < rows_left ? vbase : kOOB;
+      const int soff = !RAGGED || tr < rows_left ? (int)((uint32_t)tr * rowbytes) : 0;
       __builtin_amdgcn_raw_buffer_store_b128(
           u32x4{pack2<T>(dz[0], dz[1]), pack2<T>(dz[2], dz[3]), pack2<T>(dz[4], dz[5]), pack2<T>(dz[6], dz[7])},
           rslab, voff, soff, kSlabPolicy);
@@ -746,7 +752,7 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
 // together (same XCD mapping), and each tile's first copies are issued while
 // the previous tile's epilogue runs.  The first tile is peeled: only later
 // tiles start with the previous tile's slab stores still in flight.
-template <class T, bool BIAS, bool DB>
+template <class T, bool BIAS, bool DB, bool RAGGED>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs, int TM) {
   FLCE_LDS(L, T);
   __shared__ __attribute__((aligned(16))) float red_s[kTile];       // db: the two waves sharing rows
@@ -772,13 +778,13 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dz_kernel(BwdLaunch a, int vs
   lds_f32x4* ltok = (lds_f32x4*)tok_s;
   __attribute__((address_space(3))) int* lyv = (__attribute__((address_space(3))) int*)yv_s;
   if constexpr (sizeof(T) == 2) {
-    dz_tile_t<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+    dz_tile_t<T, BIAS, DB, RAGGED, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
     for (t += gridDim.x; t < G; t += gridDim.x)
-      dz_tile_t<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+      dz_tile_t<T, BIAS, DB, RAGGED, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
   } else {
-    dz_tile<T, BIAS, DB, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+    dz_tile<T, BIAS, DB, RAGGED, kLoadsVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
     for (t += gridDim.x; t < G; t += gridDim.x)
-      dz_tile<T, BIAS, DB, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
+      dz_tile<T, BIAS, DB, RAGGED, kLoadsVm + kStoresVm>(a, vs, TM, G, t, tc, L, red, ltok, lyv, tid);
   }
 }
 
@@ -1116,14 +1122,19 @@ static hipError_t launch_bwd_slab_t(const BwdLaunch& a, int vs, int width, int d
   const bool bias = a.b != nullptr;
   const dim3 blk(kThreads);
   const dim3 gdz(TV * a.NT < kPersistGrid ? TV * a.NT : kPersistGrid);
+  // A partial vocabulary tile (only in the last slab) or partial token tiles.
+  const bool ragged = width % kTile != 0 || a.N % kTile != 0;
   if (dz_ready) {
     // the slab already holds the dlogits (and the db partials are written)
   } else if (bias && want_db) {
-    FLCE_LAUNCH((bwd_dz_kernel<T, true, true>), gdz, blk, 0, st, a, vs, TV);
+    if (ragged) FLCE_LAUNCH((bwd_dz_kernel<T, true, true, true>), gdz, blk, 0, st, a, vs, TV);
+    else FLCE_LAUNCH((bwd_dz_kernel<T, true, true, false>), gdz, blk, 0, st, a, vs, TV);
   } else if (bias) {
-    FLCE_LAUNCH((bwd_dz_kernel<T, true, false>), gdz, blk, 0, st, a, vs, TV);
+    if (ragged) FLCE_LAUNCH((bwd_dz_kernel<T, true, false, true>), gdz, blk, 0, st, a, vs, TV);
+    else FLCE_LAUNCH((bwd_dz_kernel<T, true, false, false>), gdz, blk, 0, st, a, vs, TV);
   } else {
-    FLCE_LAUNCH((bwd_dz_kernel<T, false, false>), gdz, blk, 0, st, a, vs, TV);
+    if (ragged) FLCE_LAUNCH((bwd_dz_kernel<T, false, false, true>), gdz, blk, 0, st, a, vs, TV);
+    else FLCE_LAUNCH((bwd_dz_kernel<T, false, false, false>), gdz, blk, 0, st, a, vs, TV);
   }
   if (a.dx && !launch_dx<T>(a, vs, width, wpad, TH, dx_mode, st)) return hipErrorInvalidValue;
   if (a.dW && a.accumulate) FLCE_LAUNCH((bwd_dw_kernel<T, true>), dim3(TH * TV), blk, 0, st, a, vs, width, wpad, TH, TV);
