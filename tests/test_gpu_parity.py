@@ -36,6 +36,7 @@ CASES = {
     "c3_small": _case("n8192_h4096_v128256", "c3_small", N=600, H=328, V=2083, n_ignored=30),
     "c4_small": _case("n32768_h2048_v128000", "c4_small", N=1024, H=264, V=4000),
     "c5_small": _case("n16384_h1024_v256000", "c5_small", N=777, H=128, V=5003),
+    "c5_whole": _case("n16384_h1024_v256000", "c5_whole", N=512, H=128, V=5003),
     "sum_bias": _case("n8192_h4096_v128256", "sum_bias", N=300, H=200, V=1500, n_ignored=7,
                       reduction="sum", grad="scalar_normal", seed=7),
     "f32_none": _case("tiny_f32", "f32_none", N=300, H=136, V=1100, n_ignored=11, label_smoothing=0.1,
@@ -129,6 +130,20 @@ def test_forced_small_slabs(monkeypatch, cols):
         got = run(inputs(name))
         f, bw = oracle(name)
         check(name, got, f, bw)
+
+
+@pytest.mark.parametrize("cols", ["512", "1024"])
+@pytest.mark.parametrize("name", ["c4_small", "c5_whole"])
+def test_whole_tile_slabs_then_a_ragged_one(monkeypatch, cols, name):
+    # N a multiple of 256 and slabs of whole tiles: every slab but the last
+    # (4000 or 5003 columns) runs the recompute instance without the
+    # partial-tile masks and token checks, the last one the instance with them.
+    # c4_small has a bias (db partials), c5_whole none.
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", cols)
+    print(f"[gpu] whole-tile slabs {cols} {name}", flush=True)
+    got = run(inputs(name))
+    f, bw = oracle(name)
+    check(name, got, f, bw)
 
 
 @pytest.mark.parametrize("need", [(True, False, False), (False, True, False), (False, False, True),
