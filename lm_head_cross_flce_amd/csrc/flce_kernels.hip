@@ -120,7 +120,12 @@ __device__ __forceinline__ void lse_column(const Acc& acc, int j, const f32x4 (&
 // was 0.7% slower with 2 phases (16 token tiles per XCD sharing each W tile).
 // The launch takes x first with at least 4 phases, which the phase rule
 // (at least 8 when the vocabulary has 8 tiles) makes the usual case.
-template <class T, bool BIAS, bool SMOOTH, bool XFIRST>
+//
+// RAGGED: V or N may not be a multiple of 256, so some tile may be partial.
+// Without it the partial-tile epilogue is not compiled in: the compiler
+// computed its 32 row compares in every tile and held them in 64 scalar
+// registers.
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED>
 __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -182,7 +187,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_lse_kernel(FwdLaunch a) {
       for (int i = 0; i < 8; ++i) bias[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int rb = v0 + rloc;
-    const bool full = v0 + kTile <= a.V;
+    const bool full = !RAGGED || v0 + kTile <= a.V;
     const bool unit = !BIAS && a.logit_scale == 1.f;   // logits are the accumulators themselves
     acc_drain();
 #pragma unroll
@@ -301,14 +306,22 @@ __global__ void __launch_bounds__(1024) fwd_finalize_kernel(FwdLaunch a) {
   }
 }
 
+// Launches without a bias whose tiles are all whole (V and N multiples of
+// 256) take the instance without the partial-tile code.  With a bias that
+// instance spilled 87-103 VGPRs (the branch had been bounding the compiler's
+// scheduling), so biased launches, and fp32 inputs, keep the other one.
 template <class T, bool XFIRST>
 static void launch_fwd_lse_order(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
-  if (bias && smooth) FLCE_LAUNCH((fwd_lse_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (bias) FLCE_LAUNCH((fwd_lse_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (smooth) FLCE_LAUNCH((fwd_lse_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else FLCE_LAUNCH((fwd_lse_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  const bool whole = sizeof(T) == 2 && a.V % kTile == 0 && a.N % kTile == 0;
+  constexpr bool kW = sizeof(T) != 2;   // RAGGED of the whole-tile instance (fp32: none)
+  if (bias && smooth) FLCE_LAUNCH((fwd_lse_kernel<T, true, true, XFIRST, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) FLCE_LAUNCH((fwd_lse_kernel<T, true, false, XFIRST, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth && whole) FLCE_LAUNCH((fwd_lse_kernel<T, false, true, XFIRST, kW>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) FLCE_LAUNCH((fwd_lse_kernel<T, false, true, XFIRST, true>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (whole) FLCE_LAUNCH((fwd_lse_kernel<T, false, false, XFIRST, kW>), dim3(G), dim3(kThreads), 0, st, a);
+  else FLCE_LAUNCH((fwd_lse_kernel<T, false, false, XFIRST, true>), dim3(G), dim3(kThreads), 0, st, a);
 }
 
 template <class T>
