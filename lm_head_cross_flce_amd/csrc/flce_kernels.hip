@@ -47,6 +47,19 @@ constexpr int kSlabPolicy = 3;
 // four consecutive ones in each of the 8 row blocks.
 // ---------------------------------------------------------------------------
 
+// acc += x as one v_add_f32 the compiler cannot reorder or merge, for sums
+// whose adds the compiler otherwise restructured (and spilled).  x must not
+// come straight from a transcendental: use add_pinned_after_trans for that.
+__device__ __forceinline__ void add_pinned(float& acc, float x) {
+  asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(x));
+}
+// The same for x straight from a transcendental (v_exp_f32): a VALU
+// instruction that reads such a result needs one wait state first, which the
+// compiler does not insert before inline assembly, so the s_nop supplies it.
+__device__ __forceinline__ void add_pinned_after_trans(float& acc, float x) {
+  asm volatile("s_nop 0\n\tv_add_f32 %0, %0, %1" : "+v"(acc) : "v"(x));
+}
+
 __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2) {
   const float mn = fmaxf(m, m2);
   float r = 0.f;
@@ -719,7 +732,7 @@ __device__ __forceinline__ void dz_tile_t(const BwdLaunch& a, int vs, int TM, in
       }
       if (DB) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) asm volatile("v_add_f32 %0, %0, %1" : "+v"(rs[k]) : "v"(dz[k]));
+        for (int k = 0; k < 8; ++k) add_pinned(rs[k], dz[k]);
       }
       const int tr = 16 * i + r;
       const uint32_t voff = !RAGGED || lane_row + tr < rows_left ? vbase : kOOB;
@@ -1185,7 +1198,7 @@ constexpr int kFusedStoresVm = 40;
 // itself would put |z| 2^-9 into the exponent).  16-bit tiles copy W with
 // permuted rows (tile_row_perm), so a lane's values in blocks 2s and 2s + 1
 // of a token column are eight consecutive vocabulary rows: one 16-byte store.
-template <class T, bool BIAS, bool SMOOTH, bool XFIRST, int EXTRA>
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED, int EXTRA>
 __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n0, TileCopy<true, true>& tc,
                                                const Lds& L, const int (&ycol)[8], float (&m)[8], float (&d)[8],
                                                float (&sz)[8], float (&zy)[8], __amdgpu_buffer_rsrc_t re,
@@ -1211,7 +1224,7 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
   acc_drain();
   const int rw = wm * kWaveTile;
   const int vleft = a.V - v0;          // rows of this tile inside the vocabulary
-  const bool ragged = vleft < kTile;   // the vocabulary's last tile (wave-uniform)
+  const bool ragged = RAGGED && vleft < kTile;   // the vocabulary's last tile (wave-uniform)
   const float sc = a.logit_scale;
   auto logit = [&](float v, float bv, int row) -> float {
     const float z = fmaf(v, sc, bv);
@@ -1249,7 +1262,7 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
   for (int j = 0; j < 8; ++j) {
     const int nl = wn * kWaveTile + 16 * j + (lane & 15);
     const uint32_t off =
-        (g == 0 && n0 + nl < a.N) ? (uint32_t)(((int64_t)nl * 2 * a.VT + 2 * vt + wm) * 4) : kOOB;
+        (g == 0 && (!RAGGED || n0 + nl < a.N)) ? (uint32_t)(((int64_t)nl * 2 * a.VT + 2 * vt + wm) * 4) : kOOB;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mh[j]), rm, off, 0, 0);
   }
   // Pass 2: kept values, sums and the target logit.
@@ -1280,8 +1293,15 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         e[k] = live ? fast_exp2(fmaf(z[k], kLog2e, nml)) : 0.f;
-        se[j] += e[k];
-        if (SMOOTH) zs[j] += (!ragged || z[k] != -INFINITY) ? z[k] : 0.f;
+        if (RAGGED) {
+          se[j] += e[k];
+          if (SMOOTH) zs[j] += (!ragged || z[k] != -INFINITY) ? z[k] : 0.f;
+        } else {
+          // The same adds in the same order, pinned: as plain += the compiler
+          // restructured the sums and spilled.
+          add_pinned_after_trans(se[j], e[k]);
+          if (SMOOTH) add_pinned(zs[j], z[k]);
+        }
       }
       // Target logit by selects: a branch here (as in the other epilogues)
       // makes the compiler keep this pass's values live across it and spill.
@@ -1292,7 +1312,7 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
         zy[j] = t1 == r ? z[4 + r] : zy[j];
       }
       if constexpr (sizeof(T) == 2) {
-        const uint32_t off = n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.lde + v0 + r0) * 2) : kOOB;
+        const uint32_t off = !RAGGED || n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.lde + v0 + r0) * 2) : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7])}, re,
             off, 0, 0);
@@ -1322,7 +1342,8 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
 // Chunk forward: the forward kernel's schedule (persistent over token tile and
 // vocabulary phase, one workgroup per CU) with fused_fwd_tile's epilogue;
 // writes the same per-phase partials, which fwd_combine_kernel merges.
-template <class T, bool BIAS, bool SMOOTH, bool XFIRST>
+// RAGGED as for fwd_lse_kernel.
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED>
 __global__ void __launch_bounds__(kThreads, 1) fused_fwd_kernel(FwdLaunch a) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -1362,11 +1383,11 @@ __global__ void __launch_bounds__(kThreads, 1) fused_fwd_kernel(FwdLaunch a) {
   // The first tile is peeled: later tiles start with the previous tile's
   // kept-value stores still in flight (counted in the mainloop's first wait).
   if (vt < a.VT) {
-    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, BIAS ? 1 : 0>(a, vt, n0, tc, L, ycol, m, d, sz, zy, re, rm, tid);
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, BIAS ? 1 : 0>(a, vt, n0, tc, L, ycol, m, d, sz, zy, re, rm, tid);
     vt += a.P;
   }
   for (; vt < a.VT; vt += a.P)
-    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, (BIAS ? 1 : 0) + kFusedStoresVm>(a, vt, n0, tc, L, ycol, m, d, sz, zy,
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, (BIAS ? 1 : 0) + kFusedStoresVm>(a, vt, n0, tc, L, ycol, m, d, sz, zy,
                                                                              re, rm, tid);
   // Merge the four lanes of a token, then the two waves, as the forward does.
 #pragma unroll
@@ -1537,14 +1558,22 @@ hipError_t launch_fused_count(const FwdLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class T, bool XFIRST>
-static void launch_fused_fwd_order(const FwdLaunch& a, hipStream_t st) {
+template <class T, bool XFIRST, bool RAGGED>
+static void launch_fused_fwd_inst(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
-  if (bias && smooth) FLCE_LAUNCH((fused_fwd_kernel<T, true, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (bias) FLCE_LAUNCH((fused_fwd_kernel<T, true, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (smooth) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
-  else FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST>), dim3(G), dim3(kThreads), 0, st, a);
+  if (bias && smooth) FLCE_LAUNCH((fused_fwd_kernel<T, true, true, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) FLCE_LAUNCH((fused_fwd_kernel<T, true, false, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
+  else FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
+}
+
+// Whole tiles only (V and N multiples of 256, 16-bit inputs): the instance
+// without the partial-tile masks and token checks.
+template <class T, bool XFIRST>
+static void launch_fused_fwd_order(const FwdLaunch& a, hipStream_t st) {
+  if (sizeof(T) == 2 && a.V % kTile == 0 && a.N % kTile == 0) launch_fused_fwd_inst<T, XFIRST, sizeof(T) != 2>(a, st);
+  else launch_fused_fwd_inst<T, XFIRST, true>(a, st);
 }
 
 template <class T>
