@@ -1198,7 +1198,7 @@ constexpr int kFusedStoresVm = 40;
 // itself would put |z| 2^-9 into the exponent).  16-bit tiles copy W with
 // permuted rows (tile_row_perm), so a lane's values in blocks 2s and 2s + 1
 // of a token column are eight consecutive vocabulary rows: one 16-byte store.
-template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED, int EXTRA>
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED, bool UNIT, int EXTRA>
 __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n0, TileCopy<true, true>& tc,
                                                const Lds& L, const int (&ycol)[8], float (&m)[8], float (&d)[8],
                                                float (&sz)[8], float (&zy)[8], __amdgpu_buffer_rsrc_t re,
@@ -1227,7 +1227,7 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
   const bool ragged = RAGGED && vleft < kTile;   // the vocabulary's last tile (wave-uniform)
   const float sc = a.logit_scale;
   auto logit = [&](float v, float bv, int row) -> float {
-    const float z = fmaf(v, sc, bv);
+    const float z = UNIT ? v : fmaf(v, sc, bv);   // UNIT: no bias, scale 1 (bit-identical)
     return (!ragged || row < vleft) ? z : -INFINITY;
   };
   // Pass 1: m_h of each token column.
@@ -1304,12 +1304,21 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
         }
       }
       // Target logit by selects: a branch here (as in the other epilogues)
-      // makes the compiler keep this pass's values live across it and spill.
+      // made the shared instance keep this pass's values live across it and
+      // spill.  The whole-tile instance takes the branch, rarely entered.
       const int t0 = ycol[j] - (v0 + r0), t1 = ycol[j] - (v0 + r1);
+      if (RAGGED) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        zy[j] = t0 == r ? z[r] : zy[j];
-        zy[j] = t1 == r ? z[4 + r] : zy[j];
+        for (int r = 0; r < 4; ++r) {
+          zy[j] = t0 == r ? z[r] : zy[j];
+          zy[j] = t1 == r ? z[4 + r] : zy[j];
+        }
+      } else if (__ballot((unsigned)t0 < 4u || (unsigned)t1 < 4u)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (t0 == r) zy[j] = z[r];
+          if (t1 == r) zy[j] = z[4 + r];
+        }
       }
       if constexpr (sizeof(T) == 2) {
         const uint32_t off = !RAGGED || n0 + nl < a.N ? (uint32_t)(((int64_t)nl * a.lde + v0 + r0) * 2) : kOOB;
@@ -1342,8 +1351,9 @@ __device__ __forceinline__ void fused_fwd_tile(const FwdLaunch& a, int vt, int n
 // Chunk forward: the forward kernel's schedule (persistent over token tile and
 // vocabulary phase, one workgroup per CU) with fused_fwd_tile's epilogue;
 // writes the same per-phase partials, which fwd_combine_kernel merges.
-// RAGGED as for fwd_lse_kernel.
-template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED>
+// RAGGED as for fwd_lse_kernel.  UNIT (whole-tile launches without a bias and
+// with a logit scale of 1): the logits are the accumulators themselves.
+template <class T, bool BIAS, bool SMOOTH, bool XFIRST, bool RAGGED, bool UNIT>
 __global__ void __launch_bounds__(kThreads, 1) fused_fwd_kernel(FwdLaunch a) {
   FLCE_LDS(L, T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -1383,11 +1393,12 @@ __global__ void __launch_bounds__(kThreads, 1) fused_fwd_kernel(FwdLaunch a) {
   // The first tile is peeled: later tiles start with the previous tile's
   // kept-value stores still in flight (counted in the mainloop's first wait).
   if (vt < a.VT) {
-    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, BIAS ? 1 : 0>(a, vt, n0, tc, L, ycol, m, d, sz, zy, re, rm, tid);
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, UNIT, BIAS ? 1 : 0>(a, vt, n0, tc, L, ycol, m, d, sz, zy, re, rm,
+                                                                        tid);
     vt += a.P;
   }
   for (; vt < a.VT; vt += a.P)
-    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, (BIAS ? 1 : 0) + kFusedStoresVm>(a, vt, n0, tc, L, ycol, m, d, sz, zy,
+    fused_fwd_tile<T, BIAS, SMOOTH, XFIRST, RAGGED, UNIT, (BIAS ? 1 : 0) + kFusedStoresVm>(a, vt, n0, tc, L, ycol, m, d, sz, zy,
                                                                              re, rm, tid);
   // Merge the four lanes of a token, then the two waves, as the forward does.
 #pragma unroll
@@ -1562,10 +1573,14 @@ template <class T, bool XFIRST, bool RAGGED>
 static void launch_fused_fwd_inst(const FwdLaunch& a, hipStream_t st) {
   const int G = a.NT * a.P;
   const bool bias = a.b != nullptr, smooth = a.eps > 0.f;
-  if (bias && smooth) FLCE_LAUNCH((fused_fwd_kernel<T, true, true, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (bias) FLCE_LAUNCH((fused_fwd_kernel<T, true, false, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
-  else if (smooth) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
-  else FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST, RAGGED>), dim3(G), dim3(kThreads), 0, st, a);
+  const bool unit = !RAGGED && !bias && a.logit_scale == 1.f;
+  constexpr bool kU = !RAGGED;   // UNIT of the unit instances (whole tiles only)
+  if (bias && smooth) FLCE_LAUNCH((fused_fwd_kernel<T, true, true, XFIRST, RAGGED, false>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (bias) FLCE_LAUNCH((fused_fwd_kernel<T, true, false, XFIRST, RAGGED, false>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth && unit) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST, RAGGED, kU>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (smooth) FLCE_LAUNCH((fused_fwd_kernel<T, false, true, XFIRST, RAGGED, false>), dim3(G), dim3(kThreads), 0, st, a);
+  else if (unit) FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST, RAGGED, kU>), dim3(G), dim3(kThreads), 0, st, a);
+  else FLCE_LAUNCH((fused_fwd_kernel<T, false, false, XFIRST, RAGGED, false>), dim3(G), dim3(kThreads), 0, st, a);
 }
 
 // Whole tiles only (V and N multiples of 256, 16-bit inputs): the instance
