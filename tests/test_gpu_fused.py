@@ -61,7 +61,7 @@ def check_fused(w, got, f, bw, need=(True, True, True)):
 
 
 NAMES = ["tiny_f32", "c2_small", "c3_small", "c4_small", "c5_small", "sum_bias", "f32_none", "bf16_v_lt_tile",
-         "f32_v1030"]
+         "f32_v1030", "c3_whole", "c5_whole_unit", "c2_whole"]
 
 
 @pytest.mark.parametrize("chunk", [0, 256])

@@ -82,6 +82,18 @@ def test_keep_forced_small_slabs(monkeypatch, cols):
         check_keep(CASES[name], got, f, bw)
 
 
+@pytest.mark.parametrize("name", ["c3_whole", "c5_whole_unit", "c2_whole"])
+def test_keep_whole_tiles_several_slabs(monkeypatch, name):
+    # N and V multiples of 256 with 512-column slabs: the kept-value forward on
+    # the first 512 rows, the forward on the rest and the recompute all run
+    # their whole-tile instances.
+    monkeypatch.setenv("FLCE_DEBUG_SLAB_COLS", "512")
+    print(f"[gpu] keep, whole tiles, slabs of 512: {name}", flush=True)
+    got = run_keep(inputs(name))
+    f, bw = oracle(name)
+    check_keep(CASES[name], got, f, bw)
+
+
 def test_slab_cols_knob(monkeypatch):
     # The documented FLCE_SLAB_COLS narrows the slabs for both calls and the
     # workspace queries the binding makes: 256 columns give c3_small nine slabs,

@@ -37,6 +37,12 @@ CASES = {
     "c4_small": _case("n32768_h2048_v128000", "c4_small", N=1024, H=264, V=4000),
     "c5_small": _case("n16384_h1024_v256000", "c5_small", N=777, H=128, V=5003),
     "c5_whole": _case("n16384_h1024_v256000", "c5_whole", N=512, H=128, V=5003),
+    # whole tiles in every dimension (N and V multiples of 256): the forward's, the kept-value forward's and the
+    # recompute's instances without partial-tile code; with a bias (c3), and without one at a logit scale of 1
+    # (c5, c2: the kept-value forward reads the logits straight from its accumulators)
+    "c3_whole": _case("n8192_h4096_v128256", "c3_whole", N=512, H=256, V=2048, n_ignored=20),
+    "c5_whole_unit": _case("n16384_h1024_v256000", "c5_whole_unit", N=512, H=128, V=2048),
+    "c2_whole": _case("n4096_h2048_v32000", "c2_whole", N=256, H=256, V=1024),
     "sum_bias": _case("n8192_h4096_v128256", "sum_bias", N=300, H=200, V=1500, n_ignored=7,
                       reduction="sum", grad="scalar_normal", seed=7),
     "f32_none": _case("tiny_f32", "f32_none", N=300, H=136, V=1100, n_ignored=11, label_smoothing=0.1,
