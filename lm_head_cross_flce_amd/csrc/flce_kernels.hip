@@ -74,6 +74,8 @@ __device__ __forceinline__ void merge_md(float& m, float& d, float m2, float d2)
 // Logits are scale * acc + bias, the bias already multiplied by scale.
 // rb: tile row index of the lane's row 0 (v0 + wave row offset + 4 g); t: the
 // token's target minus rb (negative if ignored or elsewhere).
+// RAGGED here: this tile is the vocabulary's partial last one (rows at or
+// past V are masked), not the kernels' launch-wide flag of the same name.
 // UNIT: no bias and a logit scale of 1, so the logits are the accumulators
 // themselves (skips one fma per logit; bit-identical).
 template <bool SMOOTH, bool RAGGED, bool UNIT = false>
